@@ -1,0 +1,92 @@
+// Expert sort for the MoE block.
+//
+// Operation: "DeepSeek V4 950 低精度优化全复盘", section 3.2: sort the (token, slot)
+// pairs by expert id before the gather, so each expert's rows are contiguous; the
+// per-expert row counts become the group_list of the grouped GEMM ("DeepSeek-V4 W8A8
+// 性能分析", section 五).
+//
+// One workgroup of 16 waves does a stable counting sort.  Wave w owns a contiguous chunk
+// of the pairs.  Pass 1: per-wave histograms in LDS.  Pass 2: an exclusive scan over
+// (expert, wave) in expert-major order gives each wave the first output slot of each
+// expert.  Pass 3: each wave walks its chunk 64 pairs at a time in order; lanes holding
+// the same id find each other with one ballot per id bit, so a lane's rank among equal
+// ids is the popcount of the lower matching lanes - the pair order is kept.
+#include "wq_device.h"
+#include "wq_kernels.h"
+
+namespace wq {
+
+constexpr int kSortWaves = 16;
+constexpr int kSortMaxE = 1024;
+
+__global__ __launch_bounds__(1024) void k_moe_sort(const int32_t* __restrict__ ids, int n, int topk, int E,
+                                                   int32_t* __restrict__ perm, int32_t* __restrict__ row_token,
+                                                   int64_t* __restrict__ offsets) {
+  __shared__ int cnt[kSortMaxE * kSortWaves];  // [e][w]
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  for (int i = t; i < E * kSortWaves; i += 1024) cnt[i] = 0;
+  __syncthreads();
+  const int chunk = (n + kSortWaves - 1) / kSortWaves;
+  const int lo = w * chunk, hi = min(n, lo + chunk);
+  for (int i = lo + lane; i < hi; i += 64) {
+    const int id = ids[i];
+    if (id >= 0 && id < E) atomicAdd(&cnt[id * kSortWaves + w], 1);
+  }
+  __syncthreads();
+  // exclusive scan over cnt in (e, w) order, single wave
+  if (w == 0) {
+    const int total = E * kSortWaves;
+    int carry = 0;
+    for (int base = 0; base < total; base += 64) {
+      const int i = base + lane;
+      const int v = (i < total) ? cnt[i] : 0;
+      int incl = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+      }
+      if (i < total) cnt[i] = carry + incl - v;
+      carry += __shfl(incl, 63, 64);
+    }
+  }
+  __syncthreads();
+  for (int e = t; e <= E; e += 1024) offsets[e] = (e < E) ? (int64_t)cnt[e * kSortWaves] : (int64_t)n;
+  __syncthreads();
+  // stable scatter
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + lane;
+    int id = i < hi ? ids[i] : -1;
+    const bool valid = id >= 0 && id < E;  // out-of-range ids are dropped
+    if (!valid) id = 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t ones = __ballot(valid && ((id >> b) & 1));
+      peers &= ((id >> b) & 1) ? ones : ~ones;
+    }
+    if (valid) {
+      const uint64_t lower = peers & ((1ull << lane) - 1ull);
+      const int rank = __popcll(lower);
+      const int pos = cnt[id * kSortWaves + w] + rank;
+      perm[pos] = i;
+      row_token[pos] = i / topk;
+    }
+    // the lowest lane of each peer group advances that expert's slot; only this wave
+    // touches column w of cnt, and its LDS accesses complete in program order
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (peers & ((1ull << lane) - 1ull)) == 0) cnt[id * kSortWaves + w] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+hipError_t launch_moe_sort(const int32_t* ids, int64_t T, int topk, int E, int32_t* perm, int32_t* row_token,
+                           int64_t* offsets, hipStream_t st) {
+  if (E > kSortMaxE) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_moe_sort, dim3(1), dim3(1024), 0, st, ids, (int)(T * topk), topk, E, perm, row_token,
+                     offsets);
+  return hipGetLastError();
+}
+
+}  // namespace wq

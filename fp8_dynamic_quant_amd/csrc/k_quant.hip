@@ -1,0 +1,226 @@
+// Per-token dynamic INT8 quantisation, with an optional RMSNorm prologue and row gather.
+//
+// Operation: "DeepSeek-V4 W8A8 性能分析", section 一 (BF16 X -> INT8 X + per-token scale)
+// and section 二 (row-parallel work limited by the row count; long rows split along K).
+// RMSNorm fusion and the expert-sorted gather: "DeepSeek V4 950 低精度优化全复盘",
+// sections 2.3 and 3.2.
+//
+// Mapping: one wave64 per (row, K-split).  A wave reads the whole source row into
+// registers (16-byte loads, lane l takes chunks l, l+64, ...), reduces the absmax with
+// cross-lane shuffles, and quantises only the chunks of its own K slice.  With S > 1
+// splits the S waves of a row sit in different workgroups and so spread the quantise and
+// store work of a short batch over more CUs; each still reads the full row for the
+// absmax (served from L2 after the first), which keeps every wave independent: no
+// cross-workgroup barrier, nothing to wait on.
+#include "wq_device.h"
+#include "wq_kernels.h"
+
+namespace wq {
+
+template <typename T>
+struct In;
+template <>
+struct In<uint16_t> {  // bf16
+  static constexpr int EPC = 8;  // elements per 16-byte chunk
+  __device__ static void load(const uint16_t* p, float* v) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <>
+struct In<float> {
+  static constexpr int EPC = 4;
+  __device__ static void load(const float* p, float* v) {
+    float4 u = *reinterpret_cast<const float4*>(p);
+    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+  }
+};
+
+template <int EPC>
+__device__ __forceinline__ void load_gamma(const uint16_t* g, float* v) {
+  if constexpr (EPC == 8) {
+    uint4 u = *reinterpret_cast<const uint4*>(g);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    uint2 u = *reinterpret_cast<const uint2*>(g);
+    v[0] = __uint_as_float(u.x << 16);
+    v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(u.y << 16);
+    v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+  }
+}
+
+template <int EPC>
+__device__ __forceinline__ void store_codes(int8_t* dst, const float* v, float s) {
+  if constexpr (EPC == 8) {
+    uint2 o;
+    o.x = pack4_i8(quant_i8(v[0], s), quant_i8(v[1], s), quant_i8(v[2], s), quant_i8(v[3], s));
+    o.y = pack4_i8(quant_i8(v[4], s), quant_i8(v[5], s), quant_i8(v[6], s), quant_i8(v[7], s));
+    *reinterpret_cast<uint2*>(dst) = o;
+  } else {
+    *reinterpret_cast<uint32_t*>(dst) =
+        pack4_i8(quant_i8(v[0], s), quant_i8(v[1], s), quant_i8(v[2], s), quant_i8(v[3], s));
+  }
+}
+
+// RMSNorm scale 1 / sqrt(f32(ss / K) + eps), every step correctly rounded.
+__device__ __forceinline__ float rms_inv(double ss, int K, float eps) {
+  float ms = (float)(ss / (double)K);
+  float d = __fadd_rn(ms, eps);
+  return __fdiv_rn(1.0f, __fsqrt_rn(d));
+}
+
+// CH > 0: the row is cached in registers (CH chunks per lane).  CH == 0: rows longer than
+// the register cache are streamed in three passes (sum of squares, absmax, quantise).
+template <typename TIn, int CH, bool RMS>
+__global__ __launch_bounds__(256) void k_dynamic_quant(const TIn* __restrict__ x, int64_t M, int K,
+                                                       int64_t ldx, const uint16_t* __restrict__ gamma,
+                                                       float eps, const int32_t* __restrict__ row_index,
+                                                       int8_t* __restrict__ xq, float* __restrict__ xs,
+                                                       int S) {
+  constexpr int EPC = In<TIn>::EPC;
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t row = gw / S;
+  const int j = (int)(gw - row * S);
+  if (row >= M) return;
+  const int64_t src = row_index ? (int64_t)row_index[row] : row;
+  const TIn* xr = x + src * ldx;
+  const int C = K / EPC;
+  const int c0 = (int)((int64_t)C * j / S), c1 = (int)((int64_t)C * (j + 1) / S);
+  int8_t* qr = xq + row * (int64_t)K;
+
+  if constexpr (CH > 0) {
+    float v[CH][EPC];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < C) {
+        In<TIn>::load(xr + (int64_t)c * EPC, v[i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) v[i][e] = 0.0f;
+      }
+    }
+    if constexpr (RMS) {
+      double ss = 0.0;
+#pragma unroll
+      for (int i = 0; i < CH; ++i)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) ss += (double)v[i][e] * (double)v[i][e];
+      ss = wave_sum_f64(ss);
+      const float inv = rms_inv(ss, K, eps);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int c = lane + 64 * i;
+        if (c < C) {
+          float g[EPC];
+          load_gamma<EPC>(gamma + (int64_t)c * EPC, g);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) v[i][e] = __fmul_rn(__fmul_rn(v[i][e], inv), g[e]);
+        }
+      }
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) a = fmaxf(a, fabsf(v[i][e]));
+    a = wave_max(a);
+    const float s = __fdiv_rn(a, 127.0f);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = lane + 64 * i;
+      if (c >= c0 && c < c1) store_codes<EPC>(qr + (int64_t)c * EPC, v[i], s);
+    }
+    if (j == 0 && lane == 0) xs[row] = s;
+  } else {
+    float inv = 1.0f;
+    if constexpr (RMS) {
+      double ss = 0.0;
+      for (int c = lane; c < C; c += 64) {
+        float v[EPC];
+        In<TIn>::load(xr + (int64_t)c * EPC, v);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) ss += (double)v[e] * (double)v[e];
+      }
+      ss = wave_sum_f64(ss);
+      inv = rms_inv(ss, K, eps);
+    }
+    float a = 0.0f;
+    for (int c = lane; c < C; c += 64) {
+      float v[EPC];
+      In<TIn>::load(xr + (int64_t)c * EPC, v);
+      if constexpr (RMS) {
+        float g[EPC];
+        load_gamma<EPC>(gamma + (int64_t)c * EPC, g);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) v[e] = __fmul_rn(__fmul_rn(v[e], inv), g[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) a = fmaxf(a, fabsf(v[e]));
+    }
+    a = wave_max(a);
+    const float s = __fdiv_rn(a, 127.0f);
+    for (int c = c0 + lane; c < c1; c += 64) {
+      float v[EPC];
+      In<TIn>::load(xr + (int64_t)c * EPC, v);
+      if constexpr (RMS) {
+        float g[EPC];
+        load_gamma<EPC>(gamma + (int64_t)c * EPC, g);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) v[e] = __fmul_rn(__fmul_rn(v[e], inv), g[e]);
+      }
+      store_codes<EPC>(qr + (int64_t)c * EPC, v, s);
+    }
+    if (j == 0 && lane == 0) xs[row] = s;
+  }
+}
+
+template <typename TIn, bool RMS>
+static hipError_t launch_t(const TIn* x, int64_t M, int K, int64_t ldx, const uint16_t* gamma, float eps,
+                           const int32_t* row_index, int8_t* xq, float* xs, int S, hipStream_t st,
+                           int* ch_used) {
+  constexpr int EPC = In<TIn>::EPC;
+  const int C = K / EPC;
+  const int need = (C + 63) / 64;
+  const int64_t waves = M * S;
+  dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+#define WQ_QL(CHV)                                                                                     \
+  do {                                                                                                 \
+    *ch_used = CHV;                                                                                    \
+    hipLaunchKernelGGL((k_dynamic_quant<TIn, CHV, RMS>), grid, block, 0, st, x, M, K, ldx, gamma, eps, \
+                       row_index, xq, xs, S);                                                          \
+    return hipGetLastError();                                                                          \
+  } while (0)
+  if (need <= 1) WQ_QL(1);
+  if (need <= 2) WQ_QL(2);
+  if (need <= 4) WQ_QL(4);
+  if (need <= 8) WQ_QL(8);
+  if (need <= 16) WQ_QL(16);
+  WQ_QL(0);
+#undef WQ_QL
+}
+
+hipError_t launch_dynamic_quant(const void* x, bool x_f32, int64_t M, int K, int64_t ldx,
+                                const uint16_t* gamma, float eps, const int32_t* row_index, int8_t* xq,
+                                float* xs, int S, hipStream_t st, int* ch_used) {
+  if (x_f32) {
+    return gamma ? launch_t<float, true>((const float*)x, M, K, ldx, gamma, eps, row_index, xq, xs, S, st, ch_used)
+                 : launch_t<float, false>((const float*)x, M, K, ldx, gamma, eps, row_index, xq, xs, S, st, ch_used);
+  }
+  return gamma ? launch_t<uint16_t, true>((const uint16_t*)x, M, K, ldx, gamma, eps, row_index, xq, xs, S, st, ch_used)
+               : launch_t<uint16_t, false>((const uint16_t*)x, M, K, ldx, gamma, eps, row_index, xq, xs, S, st, ch_used);
+}
+
+}  // namespace wq

@@ -1,0 +1,79 @@
+// Host-side launchers for the wq kernels (internal to libwq).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+// Per-token INT8 quant (k_quant.hip).  S = K-split factor.  *ch_used reports the
+// register-cache depth chosen (0 = streamed rows).
+hipError_t launch_dynamic_quant(const void* x, bool x_f32, int64_t M, int K, int64_t ldx,
+                                const uint16_t* gamma, float eps, const int32_t* row_index, int8_t* xq,
+                                float* xs, int S, hipStream_t st, int* ch_used);
+
+// Split-K INT8 GEMM for small M (k_gemm_i8.hip).  When x_bf16 is non-null the kernel
+// quantises the bf16 rows itself (fused path) and a/a_scale are ignored.
+struct SplitKArgs {
+  const int8_t* a;        // int8 [M, lda]
+  int64_t lda;
+  const float* a_scale;   // f32 [M]
+  const uint16_t* x;      // bf16 [M, ldx] (fused) or null
+  int64_t ldx;
+  const int8_t* w;        // int8 [N, K]
+  const float* w_scale;   // f32 [N]
+  int M, N, K;
+  uint16_t* y;            // bf16 [M, ldy]
+  int64_t ldy;
+  int32_t* acc_out;       // optional [M, N]
+  int8_t* xq_out;         // optional (fused)
+  float* xs_out;          // optional (fused)
+  int32_t* ws_acc;        // zeroed workspace [M, N] int32
+  uint32_t* ws_cnt;       // zeroed counters [ceil(N/64)]
+  int ksteps;             // K slice per workgroup = 64 * ksteps
+  int S;                  // number of K slices = ceil(K / (64 * ksteps))
+};
+hipError_t launch_gemm_i8_splitk(const SplitKArgs& a, hipStream_t st);
+
+// Tiled INT8 GEMM for large M (k_gemm_i8.hip), optionally over expert segments.
+struct TileArgs {
+  const int8_t* a;        // int8 rows, row stride lda
+  int64_t lda;
+  const float* a_scale;   // f32 per row
+  const int8_t* w;        // int8 [batch][N][K]
+  int64_t w_batch_stride;
+  const float* w_scale;   // f32 [batch][N]
+  int M, N, K;
+  int epilogue;           // 1 = bf16, 2 = swiglu f32
+  void* y;
+  int64_t ldy;
+  int32_t* acc_out;       // optional [M, N] (dense only)
+  const int64_t* seg_offsets;  // device [batch+1] or null (dense)
+  int batch;
+};
+hipError_t launch_gemm_i8_tile(const TileArgs& a, hipStream_t st);
+
+// FP8 group quant with packed UE8M0 scales (k_fp8.hip).
+hipError_t launch_group_quant_fp8(const uint16_t* x, int64_t T, int G, int D, uint8_t* xq, int32_t* xs,
+                                  hipStream_t st);
+
+// Grouped FP8 contraction (k_fp8.hip).
+struct Fp8Args {
+  const uint8_t* a;       // e4m3 codes; row stride lda, group stride a_gs (bytes)
+  int64_t lda, a_gs;
+  const int32_t* a_s;     // packed storage [G, PH, TA]
+  int64_t TA;
+  const uint8_t* w;       // e4m3 [G][N][K]
+  int64_t w_gs;
+  const float* w_s;       // f32 pow2 [G][N/128][K/128]
+  int M, N, K, G;
+  uint16_t* y;            // bf16; row stride ldy, group stride y_gs
+  int64_t ldy, y_gs;
+};
+hipError_t launch_fp8_grouped(const Fp8Args& a, hipStream_t st);
+
+// Expert sort (k_moe.hip).
+hipError_t launch_moe_sort(const int32_t* ids, int64_t T, int topk, int E, int32_t* perm, int32_t* row_token,
+                           int64_t* offsets, hipStream_t st);
+
+}  // namespace wq

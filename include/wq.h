@@ -1,0 +1,187 @@
+/*
+ * wq.h - W8A8 dynamic-quant linear and FP8 per-token-group quant for MI355X (gfx950).
+ *
+ * The operation (from "DeepSeek-V4 W8A8 性能分析：小 M、NZ 布局与测量方法", section 一):
+ * a dense linear Y = X W with X [M, K], W [K, N], Y [M, N], run as BF16 X -> per-token
+ * dynamic quant -> INT8 X + per-token f32 scale -> INT8 x INT8 -> INT32 GEMM against
+ * per-output-channel-scaled INT8 weights -> BF16 Y.  The FP8 variant (SGLang PR #34277
+ * summary, 功能与动机 / 实现拆解) quantises each 128-wide hidden group of each token to
+ * E4M3FN with a power-of-two UE8M0 scale, and writes the scales packed 4 per int32 in the
+ * [G, ceil((D/128)/4), align4(T)] layout the grouped FP8 contraction reads directly.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *    allocates, frees or synchronises in these calls: it validates the arguments on the
+ *    host, enqueues kernels on `stream` (a hipStream_t passed as void*; NULL = the null
+ *    stream) and returns.  Device faults surface at the caller's next synchronisation.
+ *  - Weights are stored [N, K] with K contiguous (output-channel rows), the logical
+ *    W[K, N] transposed once at load time.
+ *  - Every base pointer and every leading dimension times the element size must be a
+ *    multiple of 16 bytes (the 16-byte scale-base rule of PR #34277, 实现拆解 item 1);
+ *    INT8 GEMMs need K % 16 == 0 and N % 16 == 0; FP8 needs D, K and N multiples of 128.
+ *  - On any failed check nothing is written and nothing is launched.
+ *  - An empty problem (M == 0 or T == 0) returns WQ_OK with no launch (the wrapper in
+ *    PR #34277 launches only when x has elements).
+ *  - Outputs are deterministic: the same inputs give the same bytes on every call.
+ *  - A context and its workspace serve one stream at a time: calls that overlap on two
+ *    streams must use two contexts.
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------------------ */
+enum {
+  WQ_OK = 0,
+  WQ_ERR_NULL = 1,        /* a required pointer is NULL                                  */
+  WQ_ERR_SHAPE = 2,       /* negative or inconsistent sizes, unsupported divisibility   */
+  WQ_ERR_ALIGN = 3,       /* a base pointer or leading dimension not 16-byte aligned    */
+  WQ_ERR_WORKSPACE = 4,   /* workspace missing or smaller than wq_workspace_bytes()     */
+  WQ_ERR_DEVICE = 5,      /* not a gfx950 device, or the launch failed                  */
+  WQ_ERR_UNSUPPORTED = 6  /* a valid but unimplemented combination of options           */
+};
+
+/* input element types */
+enum { WQ_IN_BF16 = 1, WQ_IN_F32 = 2 };
+/* GEMM payload types */
+enum { WQ_PAYLOAD_INT8 = 1, WQ_PAYLOAD_FP8_E4M3 = 2 };
+/* GEMM epilogues */
+enum { WQ_EPI_BF16 = 1, WQ_EPI_SWIGLU_F32 = 2 };
+
+/* Human-readable text for a status code (static storage). */
+const char* wq_status_str(int status);
+
+/* ABI revision of this header. */
+int wq_abi_version(void);
+
+/* ---- context ----------------------------------------------------------------------- */
+typedef struct wq_ctx wq_ctx;
+
+/* Bytes of device workspace a context needs (a fixed bound, independent of shapes). */
+size_t wq_workspace_bytes(void);
+
+/* Create a context for `device`.  `workspace` is caller-owned device memory of at least
+ * wq_workspace_bytes() bytes, 256-byte aligned and ZEROED ONCE by the caller before the
+ * first call; every kernel that uses it leaves it zeroed again when it completes, so no
+ * per-call clearing is needed.  Fails with WQ_ERR_DEVICE if the device is not gfx950.
+ * Reads the environment once: WQ_LOG=1 prints one line per call describing the chosen
+ * launch (kernel, tiles, split, grid); WQ_FORCE_SPLIT=n forces the K-split factor of the
+ * quant kernel and of the split-K GEMM (tests use it to check every split gives the same
+ * bytes). */
+int wq_ctx_create(int device, void* workspace, size_t workspace_bytes, wq_ctx** out);
+void wq_ctx_destroy(wq_ctx* ctx);
+
+/* Force the K-split factor of later calls on this context (the same knob as
+ * WQ_FORCE_SPLIT); n = 0 restores the automatic choice.  Results are bit-identical for
+ * every split; tests use this to show it.  Returns WQ_ERR_SHAPE for n < 0. */
+int wq_ctx_set_split(wq_ctx* ctx, int n);
+
+/* ---- per-token dynamic INT8 quantisation --------------------------------------------
+ * Follows section 一 of the W8A8 article (npu_dynamic_quant: BF16 X -> INT8 X plus a
+ * per-token scale) and section 二 (row-parallel work whose parallelism is capped by the
+ * row count; long rows may additionally be split along K over several workgroups).
+ * Optionally fuses an RMSNorm in front and a row gather, following "DeepSeek V4 950 低精度
+ * 优化全复盘" section 2.3 (RMSNorm fused with quantisation in registers) and section 3.2
+ * (rows gathered in expert-sorted order).
+ *
+ * For output row r (0 <= r < M), with src = row_index ? row_index[r] : r:
+ *   v[k]  = x[src, k]                                  (no RMSNorm)
+ *   v[k]  = (x[src, k] * inv) * gamma[k],  inv = 1 / sqrt(f32(sum_k x^2 / K) + rms_eps)
+ *                                                      (rms_gamma != NULL; sum in f64)
+ *   a     = max_k |v[k]|,   x_scale[r] = RN_f32(a / 127)
+ *   x_q[r, k] = clamp(rint(RN_f32(v[k] / x_scale[r])), -127, 127)   (0 when a == 0)
+ * x: x_dtype WQ_IN_BF16 or WQ_IN_F32, row stride ldx elements (ldx >= K).
+ * rms_gamma: NULL or bf16 [K].  row_index: NULL or int32 [M] (values are not checked).
+ * x_q: int8 [M, K] contiguous.  x_scale: f32 [M].  K % 16 == 0, K <= 131072. */
+int wq_dynamic_quant(wq_ctx* ctx, const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                     const void* rms_gamma, float rms_eps, const int32_t* row_index,
+                     int8_t* x_q, float* x_scale, void* stream);
+
+/* ---- per-token-group FP8 quantisation with packed UE8M0 scales -----------------------
+ * Follows the SGLang PR #34277 summary (实现拆解 items 1-2 and the kernel write-logic and
+ * wrapper snippets).  x: bf16 [T, G, D] contiguous, D % 128 == 0.  HG = D / 128,
+ * PH = ceil(HG / 4), TA = 4 * ceil(T / 4).  For each (t, g, h):
+ *   a = max |x[t, g, 128h .. 128h+127]|,  e = max(-127, smallest e with 2^e >= a / 448)
+ *   x_q[t, g, 128h + i] = E4M3FN(x * 2^-e), nearest-even       (uint8 [T, G, D])
+ *   byte e + 127 goes to byte (h % 4) of int32 word (g * PH + h / 4) * TA + t of x_s
+ * x_s: int32 storage [G, PH, TA] (16-byte aligned).  Every byte of x_s not written this
+ * way - the tail of the last pack and the token-padding words t in [T, TA) - is written
+ * as zero.  The logical [T, G, PH] view has element strides (1, PH * TA, TA). */
+int wq_group_quant_fp8_ue8m0(wq_ctx* ctx, const void* x, int64_t T, int64_t G, int64_t D,
+                             uint8_t* x_q, int32_t* x_s, void* stream);
+
+/* ---- quantised matmul ---------------------------------------------------------------
+ * INT8 (section 一 of the W8A8 article; npu_quant_matmul, and the tuple-reuse path where
+ * an upstream producer already gave (x_q, x_scale)):
+ *   acc[m, n] = sum_k a[m, k] * b[n, k]                    (exact int32)
+ *   y[m, n]   = bf16_RN((f32(acc) * a_scale[m]) * b_scale[n])            (WQ_EPI_BF16)
+ * WQ_EPI_SWIGLU_F32 (MoE gate/up, "DeepSeek V4 950" section 2.3): with N = 2I,
+ *   g = (f32(acc[m, n]) * a_scale[m]) * b_scale[n],  u likewise for column n + I,
+ *   y[m, n] = f32( g / (1 + exp(-g)) * u )  for n < I   (f32 [M, I]; exp is the fixed
+ *   f32 sequence: n = rint(x*log2e), Cody-Waite r, degree-7 Taylor Horner, ldexp).
+ * Segments (MoE, section 五 of the W8A8 article: group_list = tokens per expert):
+ *   batch = E experts and seg_offsets = device int64 [E + 1], non-decreasing, with
+ *   seg_offsets[E] == M; rows [seg_offsets[e], seg_offsets[e+1]) use b + e*b_batch_stride
+ *   and b_scale + e*N.
+ * FP8 (SGLang PR #34277: the grouped contraction that reads the packed scales):
+ *   payload WQ_PAYLOAD_FP8_E4M3, batch = G groups, a = E4M3 codes with row stride lda
+ *   bytes and group stride a_batch_stride bytes; a_scale = the int32 packed storage
+ *   [G, PH, TA] written by wq_group_quant_fp8_ue8m0 with TA = a_scale_tokens; b = E4M3
+ *   [G][N][K]; b_scale = f32 powers of two [G][N/128][K/128];
+ *   y[m, g, n] = bf16_RN( sum_kb 2^(e_a(m,g,kb)) * b_scale[g, n/128, kb]
+ *                         * sum_{k in block kb} a[m, g, k] * b[g, n, k] )   (f32 accumulate)
+ * acc_out (INT8 dense only, may be NULL): the raw int32 accumulators [M, N], row stride N. */
+typedef struct {
+  int32_t payload;         /* WQ_PAYLOAD_INT8 or WQ_PAYLOAD_FP8_E4M3                      */
+  int32_t epilogue;        /* WQ_EPI_BF16 or WQ_EPI_SWIGLU_F32                            */
+  int64_t M, N, K;         /* rows (per batch for strided batches), columns, depth        */
+  int64_t batch;           /* 1 = dense; G for FP8 groups; E for segments                 */
+  const int64_t* seg_offsets; /* device int64 [batch + 1] for segments, else NULL         */
+  const void* a;           /* payload rows                                                */
+  int64_t lda;             /* row stride of a in elements (bytes: 1-byte payloads)        */
+  int64_t a_batch_stride;  /* elements between batches of a (strided batches)             */
+  const void* a_scale;     /* INT8: f32 [M]; FP8: int32 packed storage [batch, PH, TA]    */
+  int64_t a_scale_tokens;  /* FP8: TA, the token stride of the packed storage             */
+  const void* b;           /* weights [batch][N][K]                                       */
+  int64_t b_batch_stride;  /* elements between batches of b                               */
+  const float* b_scale;    /* INT8: [batch][N]; FP8: [batch][N/128][K/128]                */
+  void* y;                 /* output                                                      */
+  int64_t ldy;             /* row stride of y in elements                                 */
+  int64_t y_batch_stride;  /* elements between batches of y (strided batches)             */
+  int32_t* acc_out;        /* optional raw INT8 accumulators [M, N]                       */
+} wq_matmul_desc;
+
+int wq_quant_matmul(wq_ctx* ctx, const wq_matmul_desc* desc, void* stream);
+
+/* ---- fused quant + INT8 GEMM (one launch) -------------------------------------------
+ * The whole chain of section 一 of the W8A8 article in one kernel: per-token quant of the
+ * bf16 x [M, K] (row stride ldx), the INT8 GEMM against w [N, K] and the bf16 epilogue,
+ * with no HBM round trip of the INT8 payload.  Outputs are bit-identical to
+ * wq_dynamic_quant followed by wq_quant_matmul.  y: bf16 [M, N] row stride ldy.  The
+ * optional outputs export the (x_q, x_scale) tuple and the int32 accumulators so that a
+ * downstream Linear can reuse them (the tuple-reuse path of section 一). */
+int wq_fused_quant_matmul(wq_ctx* ctx, const void* x, int64_t M, int64_t K, int64_t ldx,
+                          const int8_t* w, const float* w_scale, int64_t N, void* y, int64_t ldy,
+                          int8_t* x_q_out, float* x_scale_out, int32_t* acc_out, void* stream);
+
+/* ---- expert sort (MoE) ---------------------------------------------------------------
+ * "DeepSeek V4 950" section 3.2: sort the (token, slot) pairs by expert id before the
+ * gather so each expert's rows are contiguous.  topk_ids: int32 [T, topk], values in
+ * [0, E).  Outputs: perm int32 [T*topk] (flattened pair index t*topk + slot of each sorted
+ * row; stable: ties keep pair order), row_token int32 [T*topk] (= perm / topk),
+ * offsets int64 [E + 1] (exclusive prefix sum of rows per expert; the group_list of
+ * section 五 of the W8A8 article).  Out-of-range ids give undefined output, not a fault. */
+int wq_moe_sort(wq_ctx* ctx, const int32_t* topk_ids, int64_t T, int64_t topk, int64_t E,
+                int32_t* perm, int32_t* row_token, int64_t* offsets, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

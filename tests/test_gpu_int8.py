@@ -1,0 +1,164 @@
+"""GPU parity of the INT8 path (quant, split-K and tiled GEMM, fused) against the oracle.
+
+Bit-exact: INT8 payloads, f32 scales, int32 accumulators.  BF16 outputs: within 1 bf16
+ulp of the oracle's correctly rounded value (relative error <= 2^-8).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic as syn
+from gpu_util import DEV, bf16_dev, dev, host, host_bf16_bits, poison
+from oracle import int8_linear as il
+from oracle import numerics as nm
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import fp8_dynamic_quant_amd as wq
+
+
+def _y_within_one_ulp(y_gpu_bits, y_ref_bits):
+    d = nm.bf16_ulp_distance(y_gpu_bits, y_ref_bits)
+    assert d.max() <= 1, f"max bf16 ulp distance {d.max()}"
+
+
+def _check_linear(x, w, sw, *, fused, split=0):
+    ref = il.linear_w8a8(x, w, sw)
+    M, K = x.shape
+    N = w.shape[0]
+    wq.set_split(DEV, split)
+    try:
+        xd, wd, swd = bf16_dev(x), dev(w), dev(sw)
+        acc = poison((M, N), torch.int32)
+        if fused:
+            xq = poison((M, K), torch.int8)
+            xs = poison((M,), torch.float32)
+            y = wq.wq_fused_quant_matmul(xd, wd, swd, x_q_out=xq, x_scale_out=xs, acc_out=acc)
+        else:
+            xq, xs = wq.wq_dynamic_quant(xd)
+            y = wq.wq_quant_matmul(xq, xs, wd, swd, acc_out=acc)
+        torch.cuda.synchronize()
+    finally:
+        wq.set_split(DEV, 0)
+    assert np.array_equal(host(xq), ref["q"])
+    assert np.array_equal(host(xs).view(np.uint32), ref["s"].view(np.uint32))
+    assert np.array_equal(host(acc), ref["acc"])
+    _y_within_one_ulp(host_bf16_bits(y), ref["y"])
+    return y
+
+
+def test_tiny_linear():
+    x, w, sw = syn.tiny_linear()
+    _check_linear(x, w, sw, fused=False)
+    _check_linear(x, w, sw, fused=True)
+
+
+@pytest.mark.parametrize("M", syn.WQ_A["M_sweep"])
+def test_wq_a_decode_standalone_and_fused(M):
+    x, w, sw = syn.wq_a_linear(M)
+    y1 = _check_linear(x, w, sw, fused=False)
+    y2 = _check_linear(x, w, sw, fused=True)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("split", [1, 2, 4, 8, 16, 64])
+def test_every_split_gives_identical_bytes(split):
+    x, w, sw = syn.wq_a_linear(7)
+    _check_linear(x, w, sw, fused=False, split=split)
+    _check_linear(x, w, sw, fused=True, split=split)
+
+
+@pytest.mark.parametrize("M", [1, 8, 64, 512])
+def test_wq_b_wide(M):
+    x = syn.wq_b_x(M)
+    w, sw = syn.wq_b_w()
+    _check_linear(x, w, sw, fused=False)
+
+
+def test_wq_b_prefill_8192_sampled_rows():
+    M = 8192
+    x = syn.wq_b_x(M)
+    w, sw = syn.wq_b_w()
+    xd, wd, swd = bf16_dev(x), dev(w), dev(sw)
+    xq, xs = wq.wq_dynamic_quant(xd)
+    acc = torch.empty((M, w.shape[0]), dtype=torch.int32, device=DEV)
+    y = wq.wq_quant_matmul(xq, xs, wd, swd, acc_out=acc)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(0).choice(M, 48, replace=False)
+    rows = np.concatenate([rows, [0, 127, 128, M - 1]])
+    q, s = il.quant_int8_per_token(x[rows])
+    assert np.array_equal(host(xq[torch.from_numpy(rows).to(DEV)]), q)
+    accr = il.gemm_int8_int32(q, w)
+    assert np.array_equal(host(acc[torch.from_numpy(rows).to(DEV)]), accr)
+    _y_within_one_ulp(host_bf16_bits(y[torch.from_numpy(rows).to(DEV)]), il.epilogue_bf16(accr, s, sw))
+
+
+@pytest.mark.parametrize("M,K,N", [(3, 272, 48), (65, 272, 48), (130, 1040, 208), (64, 64, 16), (17, 4096, 1040)])
+def test_ragged_shapes(M, K, N):
+    x = syn.activations((90, M, K), M, K, outlier_frac=0.01, outlier_mul=20.0)
+    w, sw = syn.int8_weights((91, N, K), N, K)
+    _check_linear(x, w, sw, fused=False)
+    if M <= 64:
+        _check_linear(x, w, sw, fused=True)
+
+
+def test_zero_rows_and_extremes():
+    M, K, N = 5, 512, 64
+    x = syn.activations((92,), M, K)
+    x[1] = 0  # all-zero row: s = 0, q = 0, y = 0
+    x[3, :] = syn.to_bf16_bits(np.full(K, -1.0e30, np.float32))[:]  # large magnitudes (the f32 epilogue stays finite)
+    w, sw = syn.int8_weights((93,), N, K)
+    _check_linear(x, w, sw, fused=False)
+    _check_linear(x, w, sw, fused=True)
+
+
+def test_quant_strided_rows_and_splits():
+    M, K = 6, 4096
+    big = syn.activations((94,), M, K + 64, outlier_frac=0.01, outlier_mul=30.0)
+    xd = bf16_dev(big)[:, :K]
+    q_ref, s_ref = il.quant_int8_per_token(big[:, :K])
+    for split in (0, 1, 2, 4, 8):
+        wq.set_split(DEV, split)
+        try:
+            q, s = wq.wq_dynamic_quant(xd)
+            torch.cuda.synchronize()
+        finally:
+            wq.set_split(DEV, 0)
+        assert np.array_equal(host(q), q_ref) and np.array_equal(host(s), s_ref)
+
+
+def test_quant_long_rows_streamed():
+    M, K = 3, 32768  # beyond the register cache: three streamed passes
+    x = syn.activations((95,), M, K, outlier_frac=0.001, outlier_mul=100.0)
+    q, s = wq.wq_dynamic_quant(bf16_dev(x))
+    torch.cuda.synchronize()
+    q_ref, s_ref = il.quant_int8_per_token(x)
+    assert np.array_equal(host(q), q_ref) and np.array_equal(host(s), s_ref)
+
+
+def test_empty_and_errors():
+    w, sw = syn.int8_weights((96,), 64, 256)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    q, s = wq.wq_dynamic_quant(x)
+    assert q.shape == (0, 256)
+    y = wq.wq_fused_quant_matmul(x, dev(w), dev(sw))
+    assert y.shape == (0, 64)
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_dynamic_quant(torch.zeros((2, 24), dtype=torch.bfloat16, device=DEV))  # K % 16 != 0
+    assert e.value.status == 2
+    xb = torch.zeros((2, 256 + 4), dtype=torch.bfloat16, device=DEV)[:, 4:]  # base 8 bytes off
+    with pytest.raises(wq.WqError) as e:
+        wq.wq_dynamic_quant(xb)
+    assert e.value.status == 3
+
+
+def test_deterministic_bytes():
+    x, w, sw = syn.wq_a_linear(16)
+    xd, wd, swd = bf16_dev(x), dev(w), dev(sw)
+    ys = [wq.wq_fused_quant_matmul(xd, wd, swd).view(torch.int16).clone() for _ in range(3)]
+    ys += [wq.wq_quant_matmul(*wq.wq_dynamic_quant(xd), wd, swd).view(torch.int16).clone() for _ in range(2)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(ys[0], y)
