@@ -47,7 +47,7 @@ def standalone_bytes(M, K=K_A, N=N_A):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("k_gemm_i8.hip", "wq_device.h", "wq_api.hip"):
+    for f in ("k_decode.hip", "k_quant.hip", "wq_device.h", "wq_api.hip"):
         with open(os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -138,19 +138,27 @@ def main():
 
     stream = torch.cuda.Stream()
 
-    def capture(fn, copies):
-        """One graph per rotation slot; each graph runs fn(r) (all M of the sweep)."""
-        graphs = []
+    def graph_len(steps):
+        """Steps per captured graph: the largest divisor of `steps` not above R, so the
+        timed region is a whole number of replays and each step uses its own copy."""
+        for g in range(min(steps, R), 0, -1):
+            if steps % g == 0:
+                return g
+        return 1
+
+    def capture(fn, n):
+        """One graph running fn(r) for r = 0..n-1 back to back (one rotation slot each), so
+        the GPU runs the kernels without host gaps between them."""
+        g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
-            for r in range(copies):
-                g = torch.cuda.CUDAGraph()
-                fn(r)  # eager warm call on the side stream
-                torch.cuda.synchronize()
-                with torch.cuda.graph(g, stream=stream):
+            for r in range(min(n, 2)):
+                fn(r)  # eager warm calls on the side stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for r in range(n):
                     fn(r)
-                graphs.append(g)
         torch.cuda.synchronize()
-        return graphs
+        return g
 
     def fused_step(r, Ms=SWEEP):
         for M in Ms:
@@ -161,36 +169,40 @@ def main():
             wq.wq_dynamic_quant(xs[M][r], x_q=xq[M][r], x_scale=xsc[M][r])
             wq.wq_quant_matmul(xq[M][r], xsc[M][r], ws[r], sws[r], y=ys[M][r])
 
-    def time_graphs(graphs, steps, warmup):
+    def time_graph(g, n_per_graph, steps, warmup):
+        """Replay g (n_per_graph steps each) to cover `warmup`, then exactly `steps` steps
+        between two events on the replay stream; returns us per step."""
+        reps = max(1, steps // n_per_graph)
         with torch.cuda.stream(stream):
-            for i in range(warmup):
-                graphs[i % len(graphs)].replay()
+            for _ in range(max(1, -(-warmup // n_per_graph))):
+                g.replay()
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            for i in range(steps):
-                graphs[i % len(graphs)].replay()
+            for _ in range(reps):
+                g.replay()
             b.record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / steps * 1e3  # us per replay
+        return a.elapsed_time(b) * 1e3 / (reps * n_per_graph)
 
     # ---- headline: fused decode linear over the sweep -------------------------------------
-    g_all = capture(lambda r: fused_step(r), R)
+    G = graph_len(args.steps)
+    g_all = capture(lambda r: fused_step(r), G)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    us_step = time_graphs(g_all, args.steps, args.warmup)
+    us_step = time_graph(g_all, G, args.steps, args.warmup)
     wall = time.perf_counter() - t0
     us_per_call = us_step / len(SWEEP)
+    del g_all
 
     # ---- per-M: fused and standalone ------------------------------------------------------
     sweep = []
-    per_steps = max(20, args.steps // 2)
     for M in ([] if args.no_sweep else SWEEP):
         gf = capture(lambda r, M=M: fused_step(r, (M,)), R)
-        us_f = time_graphs(gf, per_steps * 4, args.warmup)
+        us_f = time_graph(gf, R, 4 * R, R)
         del gf
         gs = capture(lambda r, M=M: standalone_step(r, (M,)), R)
-        us_s = time_graphs(gs, per_steps * 4, args.warmup)
+        us_s = time_graph(gs, R, 4 * R, R)
         del gs
         bf, bs = fused_bytes(M), standalone_bytes(M)
         sweep.append({
@@ -219,10 +231,10 @@ def main():
 
     launch_floor = copy_us = float("nan")
     if not args.no_sweep:
-        g_floor = capture(floor_step, 4)
-        launch_floor = time_graphs(g_floor, args.steps, args.warmup) / len(SWEEP)
+        g_floor = capture(floor_step, R)
+        launch_floor = time_graph(g_floor, R, 4 * R, R) / len(SWEEP)
         g_copy = capture(copy_step, R)
-        copy_us = time_graphs(g_copy, args.steps, args.warmup)
+        copy_us = time_graph(g_copy, R, 4 * R, R)
         del g_floor, g_copy
 
     # ---- prefill point: wq_b-shaped M=8192, K=1024, N=32768 -----------------------------
@@ -281,7 +293,7 @@ def main():
                    "K": K_A, "N": N_A, "M_sweep": list(SWEEP), "rotating_copies": R},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "k_gemm_i8_splitk<MT,KSTEPS,FUSED=true>",
+                     "kernel": "k_decode<MT,NT,FUSED,A_LDS> (wq_fused_quant_matmul; M > 8 adds k_dynamic_quant)",
                      "bytes_per_step": total_bytes, "us_per_step_events": round(us_step, 3)},
         "sweep": sweep,
         "prefill_m8192": prefill,

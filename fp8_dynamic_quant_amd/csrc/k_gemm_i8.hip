@@ -5,18 +5,9 @@
 // derived from the real M, N, K; for small M and N the K dimension is split across
 // cores, the SmallMN / StreamK idea).
 //
-// Two kernels:
-//  * k_gemm_i8_splitk - decode-sized M (<= 64).  Weight streaming bounds it, so the grid
-//    is sized to put every CU on a distinct slice of W: a workgroup owns 64 output
-//    columns and one K slice; its four waves issue all their weight loads (16 bytes per
-//    lane per 64-deep step) before touching the activations, then run
-//    v_mfma_i32_16x16x64_i8 with A staged in LDS.  Partial int32 sums from the K slices
-//    meet in a workspace via integer atomics (exact, order-free); the last workgroup of
-//    a column block applies the epilogue and leaves the workspace zeroed.  The fused
-//    variant quantises the bf16 rows itself (same arithmetic as k_quant), so the INT8
-//    payload never goes through HBM.
-//  * k_gemm_i8_tile - large M.  128x128 workgroup tiles, LDS double buffering, and
-//    v_mfma_i32_16x16x64_i8; optionally over expert segments (MoE group_list).
+// k_gemm_i8_tile - large M.  128x128 workgroup tiles, LDS double buffering, and
+// v_mfma_i32_16x16x64_i8; optionally over expert segments (MoE group_list).  Decode-sized
+// M runs in k_decode.hip instead.
 #include "wq_device.h"
 #include "wq_kernels.h"
 
@@ -27,170 +18,6 @@ namespace wq {
 // ------------------------------------------------------------------------------------
 __device__ __forceinline__ uint16_t epi_bf16(int acc, float s, float sw) {
   return (uint16_t)f32_to_bf16_rn(__fmul_rn(__fmul_rn((float)acc, s), sw));
-}
-
-// ------------------------------------------------------------------------------------
-// split-K kernel for small M
-// ------------------------------------------------------------------------------------
-constexpr int kNB = 64;  // output columns per workgroup (4 waves x 16)
-
-template <int MT, int KSTEPS, bool FUSED>
-__global__ __launch_bounds__(256) void k_gemm_i8_splitk(SplitKArgs p) {
-  constexpr int KS = KSTEPS * 64;
-  constexpr int LDS_STRIDE = KS + 16;
-  __shared__ __attribute__((aligned(16))) int8_t a_lds[MT * 16 * LDS_STRIDE];
-  __shared__ float s_lds[MT * 16];
-  __shared__ int last_flag;
-
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int NBLK = (p.N + kNB - 1) / kNB;
-  const int nb = blockIdx.x % NBLK;
-  const int ks = blockIdx.x / NBLK;
-  const int n0 = nb * kNB;
-  const int k0 = ks * KS;
-  const int M = p.M, N = p.N, K = p.K;
-  const int col = n0 + wv * 16 + (lane & 15);
-  const int kg = lane >> 4;
-
-  // 1. weight loads for the whole K slice, issued first so HBM latency overlaps the rest
-  v4i b[KSTEPS];
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    const int kk = k0 + 64 * s + 16 * kg;
-    if (col < N && kk < K)
-      b[s] = *reinterpret_cast<const v4i*>(p.w + (int64_t)col * K + kk);
-    else
-      b[s] = v4i{0, 0, 0, 0};
-  }
-
-  // 2. activations -> LDS as INT8
-  if constexpr (FUSED) {
-    // per-row scale from the whole row, one wave per row
-    for (int m = wv; m < M; m += 4) {
-      const uint16_t* xr = p.x + (int64_t)m * p.ldx;
-      float a = 0.0f;
-      for (int c = lane; c < K / 8; c += 64) {
-        uint4 u = *reinterpret_cast<const uint4*>(xr + (int64_t)c * 8);
-        uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a = fmaxf(a, fabsf(__uint_as_float(w4[i] << 16)));
-          a = fmaxf(a, fabsf(__uint_as_float(w4[i] & 0xFFFF0000u)));
-        }
-      }
-      a = wave_max(a);
-      if (lane == 0) s_lds[m] = __fdiv_rn(a, 127.0f);
-    }
-    __syncthreads();
-    const bool export_q = p.xq_out != nullptr && nb == 0;
-    for (int c = t; c < MT * 16 * (KS / 8); c += 256) {
-      const int m = c / (KS / 8), kc = c % (KS / 8);
-      const int kk = k0 + kc * 8;
-      uint2 o = {0u, 0u};
-      if (m < M && kk < K) {
-        const float s = s_lds[m];
-        uint4 u = *reinterpret_cast<const uint4*>(p.x + (int64_t)m * p.ldx + kk);
-        o.x = pack4_i8(quant_i8(__uint_as_float(u.x << 16), s), quant_i8(__uint_as_float(u.x & 0xFFFF0000u), s),
-                       quant_i8(__uint_as_float(u.y << 16), s), quant_i8(__uint_as_float(u.y & 0xFFFF0000u), s));
-        o.y = pack4_i8(quant_i8(__uint_as_float(u.z << 16), s), quant_i8(__uint_as_float(u.z & 0xFFFF0000u), s),
-                       quant_i8(__uint_as_float(u.w << 16), s), quant_i8(__uint_as_float(u.w & 0xFFFF0000u), s));
-        if (export_q) *reinterpret_cast<uint2*>(p.xq_out + (int64_t)m * K + kk) = o;
-      }
-      *reinterpret_cast<uint2*>(&a_lds[m * LDS_STRIDE + kc * 8]) = o;
-    }
-    if (p.xs_out != nullptr && nb == 0 && ks == 0 && t < M) p.xs_out[t] = s_lds[t];
-  } else {
-    for (int c = t; c < MT * 16 * (KS / 16); c += 256) {
-      const int m = c / (KS / 16), kc = c % (KS / 16);
-      const int kk = k0 + kc * 16;
-      v4i v = {0, 0, 0, 0};
-      if (m < M && kk < K) v = *reinterpret_cast<const v4i*>(p.a + (int64_t)m * p.lda + kk);
-      *reinterpret_cast<v4i*>(&a_lds[m * LDS_STRIDE + kc * 16]) = v;
-    }
-    if (t < MT * 16) s_lds[t] = (t < M) ? p.a_scale[t] : 0.0f;
-  }
-  __syncthreads();
-
-  // 3. MFMA over the K slice
-  v4i acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = v4i{0, 0, 0, 0};
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const v4i af = *reinterpret_cast<const v4i*>(&a_lds[(mt * 16 + (lane & 15)) * LDS_STRIDE + 64 * s + 16 * kg]);
-      acc[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, b[s], acc[mt], 0, 0, 0);
-    }
-  }
-
-  // 4. epilogue: lane holds column `col`, rows mt*16 + 4*kg + i
-  if (p.S == 1) {
-    if (col < N) {
-      const float sw = p.w_scale[col];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = mt * 16 + 4 * kg + i;
-          if (m < M) {
-            p.y[(int64_t)m * p.ldy + col] = epi_bf16(acc[mt][i], s_lds[m], sw);
-            if (p.acc_out) p.acc_out[(int64_t)m * N + col] = acc[mt][i];
-          }
-        }
-    }
-    return;
-  }
-  if (col < N) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mt * 16 + 4 * kg + i;
-        if (m < M) atomicAdd(&p.ws_acc[(int64_t)m * N + col], acc[mt][i]);
-      }
-  }
-  __threadfence();
-  __syncthreads();
-  if (t == 0) last_flag = (atomicAdd(&p.ws_cnt[nb], 1u) == (unsigned)(p.S - 1));
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  for (int idx = t; idx < M * kNB; idx += 256) {
-    const int m = idx / kNB, n = n0 + idx % kNB;
-    if (n < N) {
-      const int v = atomicExch(&p.ws_acc[(int64_t)m * N + n], 0);
-      p.y[(int64_t)m * p.ldy + n] = epi_bf16(v, s_lds[m], p.w_scale[n]);
-      if (p.acc_out) p.acc_out[(int64_t)m * N + n] = v;
-    }
-  }
-  if (t == 0) atomicExch(&p.ws_cnt[nb], 0u);
-}
-
-template <int MT, bool FUSED>
-static hipError_t splitk_mt(const SplitKArgs& a, hipStream_t st) {
-  const int NBLK = (a.N + kNB - 1) / kNB;
-  dim3 grid((unsigned)(NBLK * a.S)), block(256);
-  switch (a.ksteps) {
-#define WQ_KS(V) \
-  case V: hipLaunchKernelGGL((k_gemm_i8_splitk<MT, V, FUSED>), grid, block, 0, st, a); break;
-    WQ_KS(1) WQ_KS(2) WQ_KS(4) WQ_KS(8) WQ_KS(16)
-#undef WQ_KS
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_i8_splitk(const SplitKArgs& a, hipStream_t st) {
-  const int MT = (a.M + 15) / 16;
-  const bool fused = a.x != nullptr;
-  switch (MT) {
-    case 1: return fused ? splitk_mt<1, true>(a, st) : splitk_mt<1, false>(a, st);
-    case 2: return fused ? splitk_mt<2, true>(a, st) : splitk_mt<2, false>(a, st);
-    case 3: return fused ? splitk_mt<3, true>(a, st) : splitk_mt<3, false>(a, st);
-    case 4: return fused ? splitk_mt<4, true>(a, st) : splitk_mt<4, false>(a, st);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 // ------------------------------------------------------------------------------------

@@ -61,15 +61,17 @@ __device__ __forceinline__ void load_gamma(const uint16_t* g, float* v) {
 }
 
 template <int EPC>
-__device__ __forceinline__ void store_codes(int8_t* dst, const float* v, float s) {
+__device__ __forceinline__ void store_codes(int8_t* dst, const float* v, float s, float inv) {
   if constexpr (EPC == 8) {
     uint2 o;
-    o.x = pack4_i8(quant_i8(v[0], s), quant_i8(v[1], s), quant_i8(v[2], s), quant_i8(v[3], s));
-    o.y = pack4_i8(quant_i8(v[4], s), quant_i8(v[5], s), quant_i8(v[6], s), quant_i8(v[7], s));
+    o.x = pack4_i8(quant_i8_fast(v[0], s, inv), quant_i8_fast(v[1], s, inv), quant_i8_fast(v[2], s, inv),
+                   quant_i8_fast(v[3], s, inv));
+    o.y = pack4_i8(quant_i8_fast(v[4], s, inv), quant_i8_fast(v[5], s, inv), quant_i8_fast(v[6], s, inv),
+                   quant_i8_fast(v[7], s, inv));
     *reinterpret_cast<uint2*>(dst) = o;
   } else {
-    *reinterpret_cast<uint32_t*>(dst) =
-        pack4_i8(quant_i8(v[0], s), quant_i8(v[1], s), quant_i8(v[2], s), quant_i8(v[3], s));
+    *reinterpret_cast<uint32_t*>(dst) = pack4_i8(quant_i8_fast(v[0], s, inv), quant_i8_fast(v[1], s, inv),
+                                                 quant_i8_fast(v[2], s, inv), quant_i8_fast(v[3], s, inv));
   }
 }
 
@@ -138,10 +140,11 @@ __global__ __launch_bounds__(256) void k_dynamic_quant(const TIn* __restrict__ x
       for (int e = 0; e < EPC; ++e) a = fmaxf(a, fabsf(v[i][e]));
     a = wave_max(a);
     const float s = __fdiv_rn(a, 127.0f);
+    const float inv = __fdiv_rn(1.0f, s);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = lane + 64 * i;
-      if (c >= c0 && c < c1) store_codes<EPC>(qr + (int64_t)c * EPC, v[i], s);
+      if (c >= c0 && c < c1) store_codes<EPC>(qr + (int64_t)c * EPC, v[i], s, inv);
     }
     if (j == 0 && lane == 0) xs[row] = s;
   } else {
@@ -172,6 +175,7 @@ __global__ __launch_bounds__(256) void k_dynamic_quant(const TIn* __restrict__ x
     }
     a = wave_max(a);
     const float s = __fdiv_rn(a, 127.0f);
+    const float qinv = __fdiv_rn(1.0f, s);
     for (int c = c0 + lane; c < c1; c += 64) {
       float v[EPC];
       In<TIn>::load(xr + (int64_t)c * EPC, v);
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(256) void k_dynamic_quant(const TIn* __restrict__ x
 #pragma unroll
         for (int e = 0; e < EPC; ++e) v[e] = __fmul_rn(__fmul_rn(v[e], inv), g[e]);
       }
-      store_codes<EPC>(qr + (int64_t)c * EPC, v, s);
+      store_codes<EPC>(qr + (int64_t)c * EPC, v, s, qinv);
     }
     if (j == 0 && lane == 0) xs[row] = s;
   }

@@ -26,13 +26,19 @@ struct wq_ctx {
   size_t ws_bytes;
   int log;
   int force_split;
+  int decode_nt;  // 0 = automatic; else 4, 8 or 16 (WQ_DECODE_NT)
+  // Largest M quantised inside the GEMM launch.  Every workgroup then quantises all M
+  // rows itself (no workgroup may wait for another), so the prologue grows with M while
+  // the second launch it saves costs a fixed ~2 us; above this M the call runs the quant
+  // kernel and then the GEMM.  WQ_FUSED_MAX_M overrides (<= 64).
+  int fused_max_m;
 };
 
 namespace {
 
-constexpr size_t kWsAccBytes = 16u << 20;  // int32 split-K accumulators
-constexpr size_t kWsCntBytes = 64u << 10;  // per-column-block arrival counters
-constexpr size_t kWsBytes = kWsAccBytes + kWsCntBytes;
+constexpr size_t kWsQBytes = 64u << 20;      // INT8 payload staged between two launches
+constexpr size_t kWsScaleBytes = 1u << 20;   // its f32 per-row scales
+constexpr size_t kWsBytes = kWsQBytes + kWsScaleBytes;
 constexpr int kAbiVersion = 1;
 
 inline bool al16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -50,8 +56,18 @@ struct DeviceGuard {
 
 int status_of(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_DEVICE; }
 
-int32_t* ws_acc(wq_ctx* c) { return reinterpret_cast<int32_t*>(c->ws); }
-uint32_t* ws_cnt(wq_ctx* c) { return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(c->ws) + kWsAccBytes); }
+int8_t* ws_q(wq_ctx* c) { return reinterpret_cast<int8_t*>(c->ws); }
+float* ws_scale(wq_ctx* c) { return reinterpret_cast<float*>(reinterpret_cast<char*>(c->ws) + kWsQBytes); }
+
+// Columns per decode workgroup: the narrowest tile (4, 8 or 16) that still gives at
+// most two workgroups per CU, so that every CU streams a distinct slice of W.
+int decode_nt(const wq_ctx* c, int64_t N) {
+  if (c->decode_nt > 0) return c->decode_nt;
+  for (int nt : {4, 8}) {
+    if ((N + nt - 1) / nt <= 2 * (int64_t)c->num_cu) return nt;
+  }
+  return 16;
+}
 
 int quant_split(const wq_ctx* c, int64_t M, int64_t K) {
   if (c->force_split > 0) return c->force_split;
@@ -100,6 +116,12 @@ int wq_ctx_create(int device, void* workspace, size_t workspace_bytes, wq_ctx** 
   c->log = lg && lg[0] == '1';
   const char* fs = std::getenv("WQ_FORCE_SPLIT");
   c->force_split = fs ? std::atoi(fs) : 0;
+  const char* dn = std::getenv("WQ_DECODE_NT");
+  c->decode_nt = dn ? std::atoi(dn) : 0;
+  if (c->decode_nt != 0 && c->decode_nt != 4 && c->decode_nt != 8 && c->decode_nt != 16) c->decode_nt = 0;
+  const char* fm = std::getenv("WQ_FUSED_MAX_M");
+  c->fused_max_m = fm ? std::atoi(fm) : 4;
+  if (c->fused_max_m < 0 || c->fused_max_m > 64) c->fused_max_m = 4;
   *out = c;
   return WQ_OK;
 }
@@ -168,7 +190,7 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   if (d->seg_offsets == nullptr && d->batch != 1) return WQ_ERR_UNSUPPORTED;
   if (d->seg_offsets != nullptr || d->epilogue != WQ_EPI_BF16) return WQ_ERR_UNSUPPORTED;  // see below
   if (M <= 64) {
-    wq::SplitKArgs a{};
+    wq::DecodeArgs a{};
     a.a = static_cast<const int8_t*>(d->a);
     a.lda = d->lda;
     a.a_scale = static_cast<const float*>(d->a_scale);
@@ -178,25 +200,20 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
     a.y = static_cast<uint16_t*>(d->y);
     a.ldy = d->ldy;
     a.acc_out = d->acc_out;
-    a.ws_acc = ws_acc(c);
-    a.ws_cnt = ws_cnt(c);
-    const int64_t nblk = (N + 63) / 64;
-    int ksteps = 16;
-    if (c->force_split > 0) {
-      const int64_t per = (K + c->force_split - 1) / c->force_split;
-      ksteps = 1;
-      while (ksteps * 64 < per && ksteps < 16) ksteps *= 2;
-    } else {
-      while (ksteps > 4 && nblk * ((K + 64 * ksteps - 1) / (64 * ksteps)) < c->num_cu) ksteps /= 2;
+    // M <= 4: dense dot4 rows beat the MFMA layout (measured on MI355X; at M = 8 the
+    // MFMA decode kernel is already faster)
+    if (M <= 4 && wq::gemv_fits((int)M, (int)K, false) && c->decode_nt == 0) {
+      hipError_t e = wq::launch_gemv(a, st);
+      if (c->log)
+        std::fprintf(stderr, "[wq] quant_matmul int8 gemv M=%lld N=%lld K=%lld rows/wg=4 grid=%lld\n", (long long)M,
+                     (long long)N, (long long)K, (long long)((N + 3) / 4));
+      return status_of(e);
     }
-    a.ksteps = ksteps;
-    a.S = (int)((K + 64 * ksteps - 1) / (64 * ksteps));
-    if ((size_t)M * N * 4 > kWsAccBytes && a.S > 1) return WQ_ERR_WORKSPACE;
-    if (nblk > (int64_t)(kWsCntBytes / 4)) return WQ_ERR_SHAPE;
-    hipError_t e = wq::launch_gemm_i8_splitk(a, st);
+    const int nt = decode_nt(c, N);
+    hipError_t e = wq::launch_decode(a, nt, st);
     if (c->log)
-      std::fprintf(stderr, "[wq] quant_matmul int8 splitk M=%lld N=%lld K=%lld kslice=%d S=%d grid=%lld cus=%d\n",
-                   (long long)M, (long long)N, (long long)K, 64 * ksteps, a.S, (long long)(nblk * a.S), c->num_cu);
+      std::fprintf(stderr, "[wq] quant_matmul int8 decode M=%lld N=%lld K=%lld cols/wg=%d grid=%lld cus=%d\n",
+                   (long long)M, (long long)N, (long long)K, nt, (long long)((N + nt - 1) / nt), c->num_cu);
     return status_of(e);
   }
   wq::TileArgs t{};
@@ -246,9 +263,15 @@ int wq_fused_quant_matmul(wq_ctx* c, const void* x, int64_t M, int64_t K, int64_
     return WQ_ERR_ALIGN;
   DeviceGuard g(c->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (M > 64) {
-    // prefill sizes: the GEMM dominates; run quant then the tiled GEMM (two launches)
-    if (!x_q_out || !x_scale_out) return WQ_ERR_UNSUPPORTED;
+  const bool one_launch_gemv = M <= c->fused_max_m && wq::gemv_fits((int)M, (int)K, true) && c->decode_nt == 0;
+  const bool one_launch_mfma = M <= c->fused_max_m && !one_launch_gemv && wq::decode_fused_fits((int)M, (int)K);
+  if (!one_launch_gemv && !one_launch_mfma) {
+    // quantise, then the GEMM (two launches); the INT8 payload goes through the
+    // caller's buffers when given, else through the context workspace
+    if (!x_q_out && (size_t)M * K > kWsQBytes) return WQ_ERR_WORKSPACE;
+    if (!x_scale_out && (size_t)M * 4 > kWsScaleBytes) return WQ_ERR_WORKSPACE;
+    if (!x_q_out) x_q_out = ws_q(c);
+    if (!x_scale_out) x_scale_out = ws_scale(c);
     int r = wq_dynamic_quant(c, x, WQ_IN_BF16, M, K, ldx, nullptr, 0.0f, nullptr, x_q_out, x_scale_out, stream);
     if (r != WQ_OK) return r;
     wq_matmul_desc d{};
@@ -258,7 +281,7 @@ int wq_fused_quant_matmul(wq_ctx* c, const void* x, int64_t M, int64_t K, int64_
     d.y = y; d.ldy = ldy; d.acc_out = acc_out;
     return wq_quant_matmul(c, &d, stream);
   }
-  wq::SplitKArgs a{};
+  wq::DecodeArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.ldx = ldx;
   a.w = w;
@@ -269,25 +292,18 @@ int wq_fused_quant_matmul(wq_ctx* c, const void* x, int64_t M, int64_t K, int64_
   a.acc_out = acc_out;
   a.xq_out = x_q_out;
   a.xs_out = x_scale_out;
-  a.ws_acc = ws_acc(c);
-  a.ws_cnt = ws_cnt(c);
-  const int64_t nblk = (N + 63) / 64;
-  int ksteps = 16;
-  if (c->force_split > 0) {
-    const int64_t per = (K + c->force_split - 1) / c->force_split;
-    ksteps = 1;
-    while (ksteps * 64 < per && ksteps < 16) ksteps *= 2;
-  } else {
-    while (ksteps > 4 && nblk * ((K + 64 * ksteps - 1) / (64 * ksteps)) < c->num_cu) ksteps /= 2;
+  if (one_launch_gemv) {
+    hipError_t e = wq::launch_gemv(a, st);
+    if (c->log)
+      std::fprintf(stderr, "[wq] fused_quant_matmul gemv M=%lld N=%lld K=%lld rows/wg=4 grid=%lld\n", (long long)M,
+                   (long long)N, (long long)K, (long long)((N + 3) / 4));
+    return status_of(e);
   }
-  a.ksteps = ksteps;
-  a.S = (int)((K + 64 * ksteps - 1) / (64 * ksteps));
-  if ((size_t)M * N * 4 > kWsAccBytes && a.S > 1) return WQ_ERR_WORKSPACE;
-  if (nblk > (int64_t)(kWsCntBytes / 4)) return WQ_ERR_SHAPE;
-  hipError_t e = wq::launch_gemm_i8_splitk(a, st);
+  const int nt = decode_nt(c, N);
+  hipError_t e = wq::launch_decode(a, nt, st);
   if (c->log)
-    std::fprintf(stderr, "[wq] fused_quant_matmul M=%lld N=%lld K=%lld kslice=%d S=%d grid=%lld cus=%d\n",
-                 (long long)M, (long long)N, (long long)K, 64 * ksteps, a.S, (long long)(nblk * a.S), c->num_cu);
+    std::fprintf(stderr, "[wq] fused_quant_matmul M=%lld N=%lld K=%lld cols/wg=%d grid=%lld cus=%d\n",
+                 (long long)M, (long long)N, (long long)K, nt, (long long)((N + nt - 1) / nt), c->num_cu);
   return status_of(e);
 }
 

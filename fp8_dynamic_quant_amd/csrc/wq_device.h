@@ -44,9 +44,49 @@ __device__ __forceinline__ int quant_i8(float v, float s) {
   return (int)r;
 }
 
+// The same code as quant_i8, usually without the division.  With inv = RN(1/s),
+// t = RN(v * inv) lies within |v/s| * 1.5 * 2^-23 of RN(v/s) (three roundings of 2^-24
+// each).  When t is farther than that from every half-integer, RN(v/s) and t share the
+// integer they round to, so rint(t) is the answer; otherwise (ties and near-ties, or a
+// non-finite t when s is subnormal) the correctly rounded division decides.
+__device__ __forceinline__ int quant_i8_fast(float v, float s, float inv) {
+  if (s == 0.0f) return 0;
+  const float tq = __fmul_rn(v, inv);
+  float r = rintf(tq);
+  const float d = fabsf(__fsub_rn(tq, r));
+  const float margin = __fmul_rn(fmaxf(fabsf(tq), 1.0f), 4.8e-7f);
+  if (!(__fsub_rn(0.5f, d) > margin)) r = rintf(__fdiv_rn(v, s));
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
          ((uint32_t)(d & 0xFF) << 24);
+}
+
+// max |x| over 8 bf16 values packed in 16 bytes
+__device__ __forceinline__ float bf16x8_absmax(const uint4 u) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a = fmaxf(a, fabsf(__uint_as_float(w[i] << 16)));
+    a = fmaxf(a, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+  }
+  return a;
+}
+
+// INT8 codes of 8 bf16 values (16 bytes) -> 8 bytes
+__device__ __forceinline__ uint2 quant8_bf16(const uint4 u, float s, float inv) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  int q[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    q[2 * i] = quant_i8_fast(__uint_as_float(w[i] << 16), s, inv);
+    q[2 * i + 1] = quant_i8_fast(__uint_as_float(w[i] & 0xFFFF0000u), s, inv);
+  }
+  return uint2{pack4_i8(q[0], q[1], q[2], q[3]), pack4_i8(q[4], q[5], q[6], q[7])};
 }
 
 // Fixed-sequence f32 exp: n = rint(x*log2e); r = (x - n*ln2_hi) - n*ln2_lo;

@@ -12,9 +12,9 @@ hipError_t launch_dynamic_quant(const void* x, bool x_f32, int64_t M, int K, int
                                 const uint16_t* gamma, float eps, const int32_t* row_index, int8_t* xq,
                                 float* xs, int S, hipStream_t st, int* ch_used);
 
-// Split-K INT8 GEMM for small M (k_gemm_i8.hip).  When x_bf16 is non-null the kernel
-// quantises the bf16 rows itself (fused path) and a/a_scale are ignored.
-struct SplitKArgs {
+// Decode-sized INT8 GEMM, M <= 64 (k_decode.hip).  When x is non-null the kernel
+// quantises the bf16 rows itself (fused path) and a / a_scale are ignored.
+struct DecodeArgs {
   const int8_t* a;        // int8 [M, lda]
   int64_t lda;
   const float* a_scale;   // f32 [M]
@@ -28,12 +28,16 @@ struct SplitKArgs {
   int32_t* acc_out;       // optional [M, N]
   int8_t* xq_out;         // optional (fused)
   float* xs_out;          // optional (fused)
-  int32_t* ws_acc;        // zeroed workspace [M, N] int32
-  uint32_t* ws_cnt;       // zeroed counters [ceil(N/64)]
-  int ksteps;             // K slice per workgroup = 64 * ksteps
-  int S;                  // number of K slices = ceil(K / (64 * ksteps))
 };
-hipError_t launch_gemm_i8_splitk(const SplitKArgs& a, hipStream_t st);
+// nt: output columns per workgroup (4, 8 or 16).
+hipError_t launch_decode(const DecodeArgs& a, int nt, hipStream_t st);
+// dynamic LDS bytes the decode kernel needs
+size_t decode_lds_bytes(int M, int K, bool fused);
+// whether the fused (quantise-inside) decode kernel can hold M rows of length K
+bool decode_fused_fits(int M, int K);
+// GEMV-style kernel for M <= 8 (k_decode.hip); fused needs M <= 4 and K <= 8192
+hipError_t launch_gemv(const DecodeArgs& a, hipStream_t st);
+bool gemv_fits(int M, int K, bool fused);
 
 // Tiled INT8 GEMM for large M (k_gemm_i8.hip), optionally over expert segments.
 struct TileArgs {

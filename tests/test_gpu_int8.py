@@ -61,6 +61,10 @@ def test_wq_a_decode_standalone_and_fused(M):
     y1 = _check_linear(x, w, sw, fused=False)
     y2 = _check_linear(x, w, sw, fused=True)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    # without the optional outputs (the payload stays on chip, or in the workspace)
+    y3 = wq.wq_fused_quant_matmul(bf16_dev(x), dev(w), dev(sw))
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
 
 
 @pytest.mark.parametrize("split", [1, 2, 4, 8, 16, 64])
@@ -95,7 +99,9 @@ def test_wq_b_prefill_8192_sampled_rows():
     _y_within_one_ulp(host_bf16_bits(y[torch.from_numpy(rows).to(DEV)]), il.epilogue_bf16(accr, s, sw))
 
 
-@pytest.mark.parametrize("M,K,N", [(3, 272, 48), (65, 272, 48), (130, 1040, 208), (64, 64, 16), (17, 4096, 1040)])
+@pytest.mark.parametrize("M,K,N", [(3, 272, 48), (65, 272, 48), (130, 1040, 208), (64, 64, 16), (17, 4096, 1040),
+                                   (5, 512, 4096), (33, 528, 2064), (2, 8192, 528), (40, 1024, 96),
+                                   (3, 16384, 64), (8, 12288, 80), (1, 16, 16)])
 def test_ragged_shapes(M, K, N):
     x = syn.activations((90, M, K), M, K, outlier_frac=0.01, outlier_mul=20.0)
     w, sw = syn.int8_weights((91, N, K), N, K)
