@@ -99,6 +99,4 @@ hipError_t launch_group_quant_fp8(const uint16_t* x, int64_t T, int G, int D, ui
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_grouped(const Fp8Args&, hipStream_t) { return hipErrorNotSupported; }
-
 }  // namespace wq

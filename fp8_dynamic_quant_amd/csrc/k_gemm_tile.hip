@@ -1,0 +1,338 @@
+// Tiled MFMA GEMM for prefill-sized M: INT8 (per-token x per-channel scales) and FP8 E4M3
+// with power-of-two block scales, over strided groups or expert segments.
+//
+// Operation: "DeepSeek-V4 W8A8 性能分析", section 一 (quant matmul with the scale
+// epilogue to BF16) and section 五 (grouped matmul over the expert segments given by
+// group_list); "DeepSeek V4 950 低精度优化全复盘" section 2.3 (SwiGLU fused behind the
+// gate/up matmul); the SGLang PR #34277 summary (the FP8 contraction that reads the
+// packed UE8M0 activation scales as written, with 128x128 power-of-two weight block
+// scales).
+//
+// Tile: 128 x 128 outputs per workgroup, 128-byte K slices, four waves in a 2 x 2 grid of
+// 64 x 64 wave tiles (2 x 2 MFMA tiles of 32 x 32).  Operand slices move global -> LDS with
+// global_load_lds_dwordx4 (no VGPR staging) into two LDS stages, so the next slice is in
+// flight while the current one feeds the MFMAs.  Rows of a slice are 128 bytes = 8
+// chunks of 16 bytes, stored XOR-swizzled by (row & 7) to spread the MFMA operand reads
+// over the LDS banks.
+//  * INT8: v_mfma_i32_32x32x32_i8, 4 per slice per tile; exact int32 accumulation; the
+//    epilogue computes bf16((f32(acc) * s_m) * sw_n).
+//  * FP8: v_mfma_scale_f32_32x32x64_f8f6f4, 2 per slice per tile.  A 128-byte K slice is
+//    exactly one scale block, so the block scales ride in the MFMA's E8M0 scale operands:
+//    the activation byte is the packed UE8M0 byte itself, the weight byte is the exponent
+//    field of its f32 power-of-two scale.  f32 accumulation.
+//  * Segments (MoE): the grid is persistent; each workgroup builds the list of non-empty
+//    (expert, 128-row tile) pairs from the segment offsets once, then walks the
+//    (pair, column tile) work items with a grid stride, so empty experts cost nothing.
+//  * SwiGLU: the workgroup computes the gate tile (columns n) and the up tile (columns
+//    n + I) of the same rows together and writes f32 silu(g) * u.
+// Rows or columns past the edge read a clamped valid row (they only feed outputs that
+// are not stored); K must be a multiple of 128 here (the host routes other K elsewhere).
+#include <type_traits>
+
+#include "wq_device.h"
+#include "wq_kernels.h"
+
+namespace wq {
+
+constexpr int kBM = 128, kBN = 128, kBK = 128;
+constexpr int kSlice = kBM * kBK;  // bytes of one operand slice in LDS
+constexpr int kGroupM = 8;         // tile rows per group in the L2-friendly tile order
+constexpr int kMaxSegTiles = 4096; // (expert, row tile) pairs a persistent workgroup can list
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ int tswz(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 4); }
+
+// DMA one 128-row x 128-byte slice: rows [r0, r0+128) of `src` (row stride ld bytes,
+// clamped to < rows), bytes [k0, k0+128); lands swizzled at `dst`
+__device__ __forceinline__ void dma_slice(const int8_t* src, int64_t ld, int r0, int rows, int k0, int8_t* dst,
+                                          int wv, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pos = (wv * 4 + i) * 64 + lane;  // 16-byte position in the slice, 0..1023
+    const int r = pos >> 3, pc = pos & 7;
+    const int c = pc ^ (r & 7);
+    int gr = r0 + r;
+    gr = gr < rows ? gr : rows - 1;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + (int64_t)gr * ld + k0 + c * 16),
+                                     (lds_ptr_t)(dst + (wv * 4 + i) * 1024), 16, 0, 0);
+  }
+}
+
+template <bool FP8>
+using acc_t = typename std::conditional<FP8, v16f, v16i>::type;
+
+// One 128 x 128 tile (two B tiles when DUAL): acc[i][j] (and acc2) over all K.
+// a: rows [m0, row_hi) clamped; b: columns [n0, ..) of w (row stride K), b2 at n0 + dual_off.
+template <bool FP8, bool DUAL>
+__device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, const int8_t* A, int m0, int row_hi,
+                                              const int8_t* B, int n0, int dual_off, int g, acc_t<FP8> (&acc)[2][2],
+                                              acc_t<FP8> (&acc2)[2][2]) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int K = p.K, N = p.N;
+  const int KT = K / kBK;
+  constexpr int kStage = (DUAL ? 3 : 2) * kSlice;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        acc[i][j][e] = 0;
+        acc2[i][j][e] = 0;
+      }
+  int srow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = m0 + wm * 64 + i * 32 + (lane & 31);
+    srow[i] = r < row_hi ? r : row_hi - 1;
+  }
+  const int PH = (KT + 3) >> 2;
+  const int32_t* xs_g = FP8 ? p.a_scale_packed + (int64_t)g * PH * p.a_scale_tokens : nullptr;
+
+  __syncthreads();  // the previous tile's LDS reads are done before the new DMA lands
+  dma_slice(A, p.lda, m0, row_hi, 0, smem, wv, lane);
+  dma_slice(B, K, n0, N, 0, smem + kSlice, wv, lane);
+  if constexpr (DUAL) dma_slice(B, K, n0 + dual_off, N, 0, smem + 2 * kSlice, wv, lane);
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    int8_t* sa = smem + cur * kStage;
+    int8_t* sb = sa + kSlice;
+    int8_t* sb2 = sa + 2 * kSlice;
+    int sca[2] = {127, 127}, scb = 127;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int32_t w = xs_g[(int64_t)(kt >> 2) * p.a_scale_tokens + srow[i]];
+        sca[i] = (w >> (8 * (kt & 3))) & 0xFF;
+      }
+      const float wsf = p.w_scale[((int64_t)g * (N / 128) + (n0 >> 7)) * KT + kt];
+      scb = (__float_as_uint(wsf) >> 23) & 0xFF;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // slice kt is in LDS for everyone; the other stage is free
+    if (kt + 1 < KT) {
+      int8_t* na = smem + (cur ^ 1) * kStage;
+      dma_slice(A, p.lda, m0, row_hi, (kt + 1) * kBK, na, wv, lane);
+      dma_slice(B, K, n0, N, (kt + 1) * kBK, na + kSlice, wv, lane);
+      if constexpr (DUAL) dma_slice(B, K, n0 + dual_off, N, (kt + 1) * kBK, na + 2 * kSlice, wv, lane);
+    }
+    const int ar = wm * 64 + (lane & 31), br = wn * 64 + (lane & 31);
+    const int kh = lane >> 5;  // which half of the K step this lane carries
+    if constexpr (FP8) {
+      // two K=64 MFMAs per slice; a lane carries 32 bytes = chunks 4*ks + 2*kh, +1
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        v8i af[2], bf[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const v4i lo = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 32, 4 * ks + 2 * kh));
+          const v4i hi = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 32, 4 * ks + 2 * kh + 1));
+          af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const v4i blo = *reinterpret_cast<const v4i*>(sb + tswz(br + i * 32, 4 * ks + 2 * kh));
+          const v4i bhi = *reinterpret_cast<const v4i*>(sb + tswz(br + i * 32, 4 * ks + 2 * kh + 1));
+          bf[i] = v8i{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, sca[i], 0,
+                                                                         scb);
+      }
+    } else {
+      // four K=32 MFMAs per slice; a lane carries 16 bytes = chunk 2*ks + kh
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        v4i af[2], bf[2], bf2[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          af[i] = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 32, 2 * ks + kh));
+          bf[i] = *reinterpret_cast<const v4i*>(sb + tswz(br + i * 32, 2 * ks + kh));
+          if constexpr (DUAL) bf2[i] = *reinterpret_cast<const v4i*>(sb2 + tswz(br + i * 32, 2 * ks + kh));
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+            if constexpr (DUAL) acc2[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf2[j], acc2[i][j], 0, 0, 0);
+          }
+      }
+    }
+  }
+}
+
+// Epilogue.  The lane holds column (lane & 31) and rows 8*(e/4) + 4*(lane>>5) + e%4 of each
+// 32 x 32 MFMA tile.
+template <bool FP8, int EPI>
+__device__ __forceinline__ void tile_epilogue(const TileArgs& p, int m0, int row_hi, int n0, int g,
+                                              const float* wsc, acc_t<FP8> (&acc)[2][2], acc_t<FP8> (&acc2)[2][2]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int N = p.N;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+    if constexpr (EPI == 2) {
+      const int I = N / 2;
+      if (n >= I) continue;
+      const float swg = wsc[n], swu = wsc[n + I];
+      float* H = reinterpret_cast<float*>(p.y);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          if (m < row_hi) {
+            const float s = p.a_scale[m];
+            const float gv = __fmul_rn(__fmul_rn((float)acc[i][j][e], s), swg);
+            const float uv = __fmul_rn(__fmul_rn((float)acc2[i][j][e], s), swu);
+            const float sg = __fdiv_rn(gv, __fadd_rn(1.0f, exp_fixed(-gv)));
+            H[(int64_t)m * p.ldy + n] = __fmul_rn(sg, uv);
+          }
+        }
+    } else {
+      if (n >= N) continue;
+      const float sw = FP8 ? 1.0f : wsc[n];
+      uint16_t* Y = reinterpret_cast<uint16_t*>(p.y) + (p.seg_offsets ? 0 : (int64_t)g * p.y_batch_stride);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          if (m < row_hi) {
+            uint16_t out;
+            if constexpr (FP8) {
+              out = (uint16_t)f32_to_bf16_rn(acc[i][j][e]);
+            } else {
+              out = (uint16_t)f32_to_bf16_rn(__fmul_rn(__fmul_rn((float)acc[i][j][e], p.a_scale[m]), sw));
+              if (p.acc_out) p.acc_out[(int64_t)m * N + n] = acc[i][j][e];
+            }
+            Y[(int64_t)m * p.ldy + n] = out;
+          }
+        }
+    }
+  }
+}
+
+// Dense or strided groups: one tile per workgroup (groups on blockIdx.y).
+template <bool FP8>
+__global__ __launch_bounds__(256) void k_gemm_tile(TileArgs p, int tiles_m, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) int8_t smem[];
+  const int g = blockIdx.y;
+  const int8_t* A = p.a + (int64_t)g * p.a_batch_stride;
+  const int8_t* B = p.w + (int64_t)g * p.w_batch_stride;
+  // XCD-aware order: consecutive workgroups land on different XCDs (round robin), so each
+  // XCD gets a contiguous run of tile indices; within a run, tiles go in groups of
+  // kGroupM tile rows sweeping the tile columns, so the A rows and B columns a CU group
+  // works on at once stay in that XCD's L2
+  const int nt = tiles_m * tiles_n;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int per_xcd = (nt + 7) >> 3;
+  const int lin = xcd * per_xcd + slot;
+  if (lin >= nt) return;
+  const int group = lin / (kGroupM * tiles_n);
+  const int gm0 = group * kGroupM;
+  const int gsz = min(kGroupM, tiles_m - gm0);
+  const int in = lin - group * kGroupM * tiles_n;
+  const int tm = gm0 + in % gsz, tn = in / gsz;
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  acc_t<FP8> acc[2][2], acc2[2][2];
+  tile_mainloop<FP8, false>(p, smem, A, m0, p.M, B, n0, 0, g, acc, acc2);
+  tile_epilogue<FP8, 1>(p, m0, p.M, n0, g, FP8 ? nullptr : p.w_scale + (int64_t)g * p.N, acc, acc2);
+}
+
+// Expert segments (INT8), persistent.  EPI 1: bf16 [rows, N]; EPI 2: f32 silu(gate)*up [rows, N/2].
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) int8_t smem[];
+  __shared__ int pair_e[kMaxSegTiles];
+  __shared__ int pair_m[kMaxSegTiles];
+  __shared__ int npairs;
+  const int t = threadIdx.x;
+  // list the non-empty (expert, row tile) pairs, in expert order (one wave, scan by shuffles)
+  if (t < 64) {
+    int base = 0;
+    for (int e0 = 0; e0 < p.batch; e0 += 64) {
+      const int e = e0 + t;
+      int cnt = 0;
+      int64_t lo = 0;
+      if (e < p.batch) {
+        lo = p.seg_offsets[e];
+        cnt = (int)((p.seg_offsets[e + 1] - lo + kBM - 1) / kBM);
+      }
+      int incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (t >= o) incl += u;
+      }
+      const int start = base + incl - cnt;
+      for (int j = 0; j < cnt; ++j) {
+        if (start + j < kMaxSegTiles) {
+          pair_e[start + j] = e;
+          pair_m[start + j] = (int)lo + j * kBM;
+        }
+      }
+      base += __shfl(incl, 63, 64);
+    }
+    if (t == 0) npairs = base < kMaxSegTiles ? base : kMaxSegTiles;
+  }
+  __syncthreads();
+  const int npair = npairs;
+  const int nn = (EPI == 2) ? (p.N / 2 + kBN - 1) / kBN : tiles_n;
+  const int total = npair * nn;
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const int pi = item / nn, tn = item - pi * nn;
+    const int e = pair_e[pi];
+    const int m0 = pair_m[pi];
+    const int row_hi = (int)p.seg_offsets[e + 1];
+    const int8_t* B = p.w + (int64_t)e * p.w_batch_stride;
+    const float* wsc = p.w_scale + (int64_t)e * p.N;
+    acc_t<false> acc[2][2], acc2[2][2];
+    const int n0 = tn * kBN;
+    tile_mainloop<false, EPI == 2>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, 0, acc, acc2);
+    tile_epilogue<false, EPI>(p, m0, row_hi, n0, 0, wsc, acc, acc2);
+  }
+}
+
+bool tile_fits(int K) { return K % kBK == 0; }
+
+hipError_t launch_gemm_tile(const TileArgs& a, bool fp8, hipStream_t st) {
+  if (!tile_fits(a.K)) return hipErrorInvalidValue;
+  const int tiles_n = (a.N + kBN - 1) / kBN;
+  if (a.seg_offsets) {
+    if (fp8) return hipErrorInvalidValue;
+    if (a.epilogue == 2 && (a.N % 256) != 0) return hipErrorInvalidValue;
+    const int dual = a.epilogue == 2;
+    const size_t lds = (size_t)2 * (dual ? 3 : 2) * kSlice;
+    auto kfn = dual ? k_gemm_seg<2> : k_gemm_seg<1>;
+    static bool attr[2] = {false, false};
+    if (!attr[dual]) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      attr[dual] = true;
+    }
+    int dev = 0, cus = 256;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    hipLaunchKernelGGL(kfn, dim3((unsigned)(2 * cus)), dim3(256), lds, st, a, tiles_n);
+    return hipGetLastError();
+  }
+  const int tiles_m = (a.M + kBM - 1) / kBM;
+  const int nt = tiles_m * tiles_n;
+  dim3 grid((unsigned)(((nt + 7) / 8) * 8), (unsigned)a.batch), block(256);
+  const size_t lds = 2 * (size_t)2 * kSlice;
+  if (fp8)
+    hipLaunchKernelGGL((k_gemm_tile<true>), grid, block, lds, st, a, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((k_gemm_tile<false>), grid, block, lds, st, a, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace wq

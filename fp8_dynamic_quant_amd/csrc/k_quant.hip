@@ -75,11 +75,14 @@ __device__ __forceinline__ void store_codes(int8_t* dst, const float* v, float s
   }
 }
 
-// RMSNorm scale 1 / sqrt(f32(ss / K) + eps), every step correctly rounded.
+// RMSNorm scale 1 / sqrt(f32(ss / K) + eps), every step correctly rounded.  sqrtf is
+// the correctly rounded square root under -fhip-fp32-correctly-rounded-divide-sqrt (the
+// library's build flag); __fsqrt_rn is not correctly rounded on gfx950 (measured: about
+// 15% of inputs land one ulp off), so it is not used.
 __device__ __forceinline__ float rms_inv(double ss, int K, float eps) {
   float ms = (float)(ss / (double)K);
   float d = __fadd_rn(ms, eps);
-  return __fdiv_rn(1.0f, __fsqrt_rn(d));
+  return __fdiv_rn(1.0f, sqrtf(d));
 }
 
 // CH > 0: the row is cached in registers (CH chunks per lane).  CH == 0: rows longer than

@@ -188,7 +188,33 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   if (!al16(d->a) || !al16(d->b) || !al16(d->y) || !al16(d->acc_out) || d->lda % 16 != 0 || (d->ldy * ysz) % 16 != 0)
     return WQ_ERR_ALIGN;
   if (d->seg_offsets == nullptr && d->batch != 1) return WQ_ERR_UNSUPPORTED;
-  if (d->seg_offsets != nullptr || d->epilogue != WQ_EPI_BF16) return WQ_ERR_UNSUPPORTED;  // see below
+  if (d->seg_offsets != nullptr) {
+    // expert segments: persistent 128x128 tiles over the non-empty (expert, row tile) pairs
+    if (!wq::tile_fits((int)K) || d->acc_out) return WQ_ERR_UNSUPPORTED;
+    if (d->epilogue == WQ_EPI_SWIGLU_F32 && N % 256 != 0) return WQ_ERR_SHAPE;
+    if (d->b_batch_stride < N * K) return WQ_ERR_SHAPE;
+    if (d->batch > 4096) return WQ_ERR_SHAPE;
+    wq::TileArgs t{};
+    t.a = static_cast<const int8_t*>(d->a);
+    t.lda = d->lda;
+    t.a_scale = static_cast<const float*>(d->a_scale);
+    t.w = static_cast<const int8_t*>(d->b);
+    t.w_batch_stride = d->b_batch_stride;
+    t.w_scale = d->b_scale;
+    t.M = (int)M; t.N = (int)N; t.K = (int)K;
+    t.epilogue = d->epilogue;
+    t.y = d->y;
+    t.ldy = d->ldy;
+    t.seg_offsets = d->seg_offsets;
+    t.batch = (int)d->batch;
+    hipError_t e = wq::launch_gemm_tile(t, false, st);
+    if (c->log)
+      std::fprintf(stderr, "[wq] quant_matmul int8 segments E=%lld rows=%lld N=%lld K=%lld epilogue=%s persistent grid=%d\n",
+                   (long long)d->batch, (long long)M, (long long)N, (long long)K,
+                   d->epilogue == WQ_EPI_SWIGLU_F32 ? "swiglu-f32" : "bf16", 2 * c->num_cu);
+    return status_of(e);
+  }
+  if (d->epilogue != WQ_EPI_BF16) return WQ_ERR_UNSUPPORTED;
   if (M <= 64) {
     wq::DecodeArgs a{};
     a.a = static_cast<const int8_t*>(d->a);
@@ -230,10 +256,46 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   t.acc_out = d->acc_out;
   t.seg_offsets = d->seg_offsets;
   t.batch = (int)d->batch;
-  hipError_t e = wq::launch_gemm_i8_tile(t, st);
+  const bool dma_tiles = wq::tile_fits((int)K);
+  hipError_t e = dma_tiles ? wq::launch_gemm_tile(t, false, st) : wq::launch_gemm_i8_tile(t, st);
   if (c->log)
-    std::fprintf(stderr, "[wq] quant_matmul int8 tile128 M=%lld N=%lld K=%lld grid=%lld\n", (long long)M,
-                 (long long)N, (long long)K, (long long)(((M + 127) / 128) * ((N + 127) / 128)));
+    std::fprintf(stderr, "[wq] quant_matmul int8 %s M=%lld N=%lld K=%lld grid=%lld\n",
+                 dma_tiles ? "tile128-lds-dma" : "tile128", (long long)M, (long long)N, (long long)K,
+                 (long long)(((M + 127) / 128) * ((N + 127) / 128)));
+  return status_of(e);
+}
+
+static int fp8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
+  const int64_t M = d->M, N = d->N, K = d->K, G = d->batch;
+  if (N % 128 != 0 || K % 128 != 0 || d->seg_offsets != nullptr || d->epilogue != WQ_EPI_BF16) return WQ_ERR_SHAPE;
+  if (d->lda < K || d->ldy < N || d->a_batch_stride < 0 || d->y_batch_stride < 0) return WQ_ERR_SHAPE;
+  const int64_t TA = (M + 3) / 4 * 4;
+  if (d->a_scale_tokens < TA) return WQ_ERR_SHAPE;
+  if (!d->a || !d->a_scale || !d->b || !d->b_scale || !d->y) return WQ_ERR_NULL;
+  if (!al16(d->a) || !al16(d->b) || !al16(d->y) || !al16(d->a_scale) || d->lda % 16 != 0 ||
+      d->a_batch_stride % 16 != 0 || (d->ldy * 2) % 16 != 0 || (d->y_batch_stride * 2) % 16 != 0 ||
+      d->b_batch_stride % 16 != 0)
+    return WQ_ERR_ALIGN;
+  wq::TileArgs t{};
+  t.a = static_cast<const int8_t*>(d->a);
+  t.lda = d->lda;
+  t.a_batch_stride = d->a_batch_stride;
+  t.a_scale_packed = static_cast<const int32_t*>(d->a_scale);
+  t.a_scale_tokens = d->a_scale_tokens;
+  t.w = static_cast<const int8_t*>(d->b);
+  t.w_batch_stride = d->b_batch_stride;
+  t.w_scale = d->b_scale;
+  t.M = (int)M; t.N = (int)N; t.K = (int)K;
+  t.epilogue = WQ_EPI_BF16;
+  t.y = d->y;
+  t.ldy = d->ldy;
+  t.y_batch_stride = d->y_batch_stride;
+  t.batch = (int)G;
+  hipError_t e = wq::launch_gemm_tile(t, true, st);
+  if (c->log)
+    std::fprintf(stderr, "[wq] quant_matmul fp8 tile128-lds-dma M=%lld N=%lld K=%lld groups=%lld grid=%lld\n",
+                 (long long)M, (long long)N, (long long)K, (long long)G,
+                 (long long)(((M + 127) / 128) * (N / 128) * G));
   return status_of(e);
 }
 
@@ -246,7 +308,7 @@ int wq_quant_matmul(wq_ctx* c, const wq_matmul_desc* d, void* stream) {
   DeviceGuard g(c->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (d->payload == WQ_PAYLOAD_INT8) return int8_matmul(c, d, st);
-  if (d->payload == WQ_PAYLOAD_FP8_E4M3) return WQ_ERR_UNSUPPORTED;
+  if (d->payload == WQ_PAYLOAD_FP8_E4M3) return fp8_matmul(c, d, st);
   return WQ_ERR_SHAPE;
 }
 

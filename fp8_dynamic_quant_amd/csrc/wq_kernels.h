@@ -54,27 +54,19 @@ struct TileArgs {
   int32_t* acc_out;       // optional [M, N] (dense only)
   const int64_t* seg_offsets;  // device [batch+1] or null (dense)
   int batch;
+  int64_t a_batch_stride;      // strided groups: bytes between groups of a
+  const int32_t* a_scale_packed;  // FP8: packed UE8M0 storage [batch, PH, TA]
+  int64_t a_scale_tokens;      // FP8: TA
+  int64_t y_batch_stride;      // strided groups: elements between groups of y
 };
 hipError_t launch_gemm_i8_tile(const TileArgs& a, hipStream_t st);
+// 128x128 tiles with DMA-fed LDS (k_gemm_tile.hip); K % 128 == 0
+hipError_t launch_gemm_tile(const TileArgs& a, bool fp8, hipStream_t st);
+bool tile_fits(int K);
 
 // FP8 group quant with packed UE8M0 scales (k_fp8.hip).
 hipError_t launch_group_quant_fp8(const uint16_t* x, int64_t T, int G, int D, uint8_t* xq, int32_t* xs,
                                   hipStream_t st);
-
-// Grouped FP8 contraction (k_fp8.hip).
-struct Fp8Args {
-  const uint8_t* a;       // e4m3 codes; row stride lda, group stride a_gs (bytes)
-  int64_t lda, a_gs;
-  const int32_t* a_s;     // packed storage [G, PH, TA]
-  int64_t TA;
-  const uint8_t* w;       // e4m3 [G][N][K]
-  int64_t w_gs;
-  const float* w_s;       // f32 pow2 [G][N/128][K/128]
-  int M, N, K, G;
-  uint16_t* y;            // bf16; row stride ldy, group stride y_gs
-  int64_t ldy, y_gs;
-};
-hipError_t launch_fp8_grouped(const Fp8Args& a, hipStream_t st);
 
 // Expert sort (k_moe.hip).
 hipError_t launch_moe_sort(const int32_t* ids, int64_t T, int topk, int E, int32_t* perm, int32_t* row_token,

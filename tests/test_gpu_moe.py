@@ -1,0 +1,116 @@
+"""GPU parity of the MoE W8A8 expert block: expert sort, fused RMSNorm+quant with the
+expert-sorted gather, segmented gate/up GEMM with the SwiGLU epilogue, INT8 requant of
+the f32 activation, segmented down GEMM.
+
+Bit-exact: sort outputs, INT8 payloads and scales, the f32 SwiGLU activations (same
+fixed operation sequence on both sides).  BF16 outputs within 1 bf16 ulp.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic as syn
+from gpu_util import DEV, assert_same, bf16_dev, dev, host, host_bf16_bits
+from oracle import int8_linear as il
+from oracle import moe
+from oracle import numerics as nm
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import fp8_dynamic_quant_amd as wq
+
+
+@pytest.mark.parametrize("T,E,topk,seed", [(256, 256, 8, 51), (37, 16, 3, 1), (1, 4, 4, 2), (0, 8, 2, 3)])
+def test_expert_sort(T, E, topk, seed):
+    ids = syn.zipf_topk_ids((9, seed), T, E, topk) if T > 0 else np.zeros((0, topk), np.int32)
+    perm, row_token, offsets = wq.wq_moe_sort(dev(ids), E)
+    torch.cuda.synchronize()
+    p_ref, off_ref = moe.expert_sort(ids, E)
+    assert np.array_equal(host(perm), p_ref)
+    assert np.array_equal(host(row_token), p_ref // topk)
+    assert np.array_equal(host(offsets), off_ref)
+
+
+@pytest.mark.parametrize("T,H", [(16, 512), (8, 4096), (5, 2064)])
+def test_rmsnorm_quant_gather(T, H):
+    h = syn.activations((60, T, H), T, H)
+    gamma = syn.to_bf16_bits(np.random.default_rng(T).uniform(0.5, 1.5, H).astype(np.float32))
+    ids = syn.zipf_topk_ids((61, T), T, 8, 4)
+    p_ref, _ = moe.expert_sort(ids, 8)
+    tok = p_ref // 4
+    q, s = wq.wq_dynamic_quant(bf16_dev(h), rms_gamma=bf16_dev(gamma), row_index=dev(tok.astype(np.int32)))
+    torch.cuda.synchronize()
+    v = moe.rmsnorm_f32(h, gamma)
+    q_ref, s_ref = il.quant_int8_per_token(v[tok], is_bf16_bits=False)
+    assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host(q), q_ref)
+
+
+def _run_block_gpu(d, E):
+    ids_d = dev(d["ids"])
+    perm, row_token, offsets = wq.wq_moe_sort(ids_d, E)
+    q1, s1 = wq.wq_dynamic_quant(bf16_dev(d["h"]), rms_gamma=bf16_dev(d["gamma"]), row_index=row_token)
+    w13, sw13, w2, sw2 = d["w13_d"], d["sw13_d"], d["w2_d"], d["sw2_d"]
+    hmid = wq.wq_quant_matmul(q1, s1, w13, sw13, seg_offsets=offsets, epilogue=wq.WQ_EPI_SWIGLU_F32)
+    q2, s2 = wq.wq_dynamic_quant(hmid)
+    y = wq.wq_quant_matmul(q2, s2, w2, sw2, seg_offsets=offsets)
+    torch.cuda.synchronize()
+    return dict(perm=perm, offsets=offsets, q1=q1, s1=s1, h=hmid, q2=q2, s2=s2, y=y)
+
+
+@pytest.mark.parametrize("T,H,I,E,topk", [(32, 256, 128, 8, 2), (64, 1024, 512, 32, 8), (300, 512, 256, 4, 2)])
+def test_moe_block_against_oracle(T, H, I, E, topk):
+    d = syn.moe_inputs(seed=T, T=T, H=H, I=I, E=E, TOPK=topk)
+    d.update(w13_d=dev(d["w13"]), sw13_d=dev(d["sw13"]), w2_d=dev(d["w2"]), sw2_d=dev(d["sw2"]))
+    g = _run_block_gpu(d, E)
+    r = moe.moe_block(d["h"], d["gamma"], d["ids"], d["w13"], d["sw13"], d["w2"], d["sw2"], keep=True)
+    assert_same("perm", host(g["perm"]), r["perm"])
+    assert_same("offsets", host(g["offsets"]), r["offsets"])
+    assert_same("s1", host(g["s1"]), r["s1"])
+    assert_same("q1", host(g["q1"]), r["q1"])
+    assert_same("h", host(g["h"]), r["h"])
+    assert_same("s2", host(g["s2"]), r["s2"])
+    assert_same("q2", host(g["q2"]), r["q2"])
+    assert nm.bf16_ulp_distance(host_bf16_bits(g["y"]), r["y"]).max() <= 1
+
+
+def test_moe_block_full_size_sampled_experts():
+    """DeepSeek-V4 shape (256 tokens, hidden 4096, 256 experts of 2x2048, top-8 Zipf(1.1)):
+    weights generated on the GPU from a seeded generator, then the rows of three experts
+    (the busiest, a median one and a one-row one) checked against the oracle."""
+    T, H, I, E, topk = 256, 4096, 2048, 256, 8
+    d = syn.moe_inputs(seed=51, T=T, H=H, I=I, E=E, TOPK=topk, weights=False)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5151)
+    w13 = torch.randint(-127, 128, (E, 2 * I, H), generator=gen, device=DEV, dtype=torch.int8)
+    w2 = torch.randint(-127, 128, (E, H, I), generator=gen, device=DEV, dtype=torch.int8)
+    sw13 = torch.rand((E, 2 * I), generator=gen, device=DEV) * 9e-3 + 1e-3
+    sw2 = torch.rand((E, H), generator=gen, device=DEV) * 9e-3 + 1e-3
+    d.update(w13_d=w13, sw13_d=sw13, w2_d=w2, sw2_d=sw2)
+    g = _run_block_gpu(d, E)
+    offsets = host(g["offsets"])
+    counts = np.diff(offsets)
+    perm_ref, off_ref = moe.expert_sort(d["ids"], E)
+    assert np.array_equal(offsets, off_ref) and np.array_equal(host(g["perm"]), perm_ref)
+    assert counts.sum() == T * topk
+    order = np.argsort(counts)
+    busiest = int(order[-1])
+    one_row = int(np.flatnonzero(counts == 1)[0]) if (counts == 1).any() else int(order[0])
+    median = int(order[np.searchsorted(counts[order], np.median(counts[counts > 0]))])
+    v = moe.rmsnorm_f32(d["h"], d["gamma"])
+    for e in {busiest, one_row, median}:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if lo == hi:
+            continue
+        tok = perm_ref[lo:hi] // topk
+        q1, s1 = il.quant_int8_per_token(v[tok], is_bf16_bits=False)
+        assert_same(f"q1[e={e}]", host(g["q1"][lo:hi]), q1)
+        acc13 = il.gemm_int8_int32(q1, host(w13[e]))
+        hmid = moe.silu_mul_f32(acc13, s1, np.broadcast_to(host(sw13[e]), (hi - lo, 2 * I)))
+        assert_same(f"h[e={e}, rows {lo}:{hi}]", host(g["h"][lo:hi]), hmid)
+        q2, s2 = il.quant_int8_per_token(hmid, is_bf16_bits=False)
+        assert_same(f"q2[e={e}]", host(g["q2"][lo:hi]), q2)
+        y = il.epilogue_bf16(il.gemm_int8_int32(q2, host(w2[e])), s2, host(sw2[e]))
+        assert nm.bf16_ulp_distance(host_bf16_bits(g["y"][lo:hi]), y).max() <= 1
