@@ -63,6 +63,9 @@ hipError_t launch_gemm_i8_tile(const TileArgs& a, hipStream_t st);
 // 128x128 tiles with DMA-fed LDS (k_gemm_tile.hip); K % 128 == 0
 hipError_t launch_gemm_tile(const TileArgs& a, bool fp8, hipStream_t st);
 bool tile_fits(int K);
+// persistent 256x256 INT8 tiles for large M (k_gemm_big.hip)
+hipError_t launch_gemm_i8_big(const TileArgs& a, int num_cu, hipStream_t st);
+bool big_fits(int M, int N, int K, int64_t lda, int64_t ldy);
 
 // FP8 group quant with packed UE8M0 scales (k_fp8.hip).
 hipError_t launch_group_quant_fp8(const uint16_t* x, int64_t T, int G, int D, uint8_t* xq, int32_t* xs,

@@ -101,7 +101,8 @@ def test_wq_b_prefill_8192_sampled_rows():
 
 @pytest.mark.parametrize("M,K,N", [(3, 272, 48), (65, 272, 48), (130, 1040, 208), (64, 64, 16), (17, 4096, 1040),
                                    (5, 512, 4096), (33, 528, 2064), (2, 8192, 528), (40, 1024, 96),
-                                   (3, 16384, 64), (8, 12288, 80), (1, 16, 16)])
+                                   (3, 16384, 64), (8, 12288, 80), (1, 16, 16),
+                                   (300, 1024, 528), (257, 128, 256), (1000, 2048, 1536)])
 def test_ragged_shapes(M, K, N):
     x = syn.activations((90, M, K), M, K, outlier_frac=0.01, outlier_mul=20.0)
     w, sw = syn.int8_weights((91, N, K), N, K)
