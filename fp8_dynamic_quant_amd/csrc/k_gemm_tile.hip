@@ -37,7 +37,7 @@ namespace wq {
 constexpr int kBM = 128, kBN = 128, kBK = 128;
 constexpr int kSlice = kBM * kBK;  // bytes of one operand slice in LDS
 constexpr int kGroupM = 8;         // tile rows per group in the L2-friendly tile order
-constexpr int kMaxSegTiles = 4096; // (expert, row tile) pairs a persistent workgroup can list
+constexpr int kMaxSegTiles = kSegMaxPairs;  // (expert, row tile) pairs a persistent workgroup lists
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 

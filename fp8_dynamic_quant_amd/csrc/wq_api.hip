@@ -194,6 +194,9 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
     if (d->epilogue == WQ_EPI_SWIGLU_F32 && N % 256 != 0) return WQ_ERR_SHAPE;
     if (d->b_batch_stride < N * K) return WQ_ERR_SHAPE;
     if (d->batch > 4096) return WQ_ERR_SHAPE;
+    // every expert adds at most one partial row tile: E + ceil(M/128) bounds the
+    // (expert, row tile) pairs the persistent kernel lists in LDS
+    if (d->batch + (M + 127) / 128 > wq::kSegMaxPairs) return WQ_ERR_UNSUPPORTED;
     wq::TileArgs t{};
     t.a = static_cast<const int8_t*>(d->a);
     t.lda = d->lda;

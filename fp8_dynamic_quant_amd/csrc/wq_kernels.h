@@ -63,6 +63,8 @@ hipError_t launch_gemm_i8_tile(const TileArgs& a, hipStream_t st);
 // 128x128 tiles with DMA-fed LDS (k_gemm_tile.hip); K % 128 == 0
 hipError_t launch_gemm_tile(const TileArgs& a, bool fp8, hipStream_t st);
 bool tile_fits(int K);
+// (expert, 128-row tile) pairs the segmented kernel can hold
+constexpr int kSegMaxPairs = 4096;
 // persistent 256x256 INT8 tiles for large M (k_gemm_big.hip)
 hipError_t launch_gemm_i8_big(const TileArgs& a, int num_cu, hipStream_t st);
 bool big_fits(int M, int N, int K, int64_t lda, int64_t ldy);

@@ -67,19 +67,23 @@ typedef struct wq_ctx wq_ctx;
 size_t wq_workspace_bytes(void);
 
 /* Create a context for `device`.  `workspace` is caller-owned device memory of at least
- * wq_workspace_bytes() bytes, 256-byte aligned and ZEROED ONCE by the caller before the
- * first call; every kernel that uses it leaves it zeroed again when it completes, so no
- * per-call clearing is needed.  Fails with WQ_ERR_DEVICE if the device is not gfx950.
- * Reads the environment once: WQ_LOG=1 prints one line per call describing the chosen
- * launch (kernel, tiles, split, grid); WQ_FORCE_SPLIT=n forces the K-split factor of the
- * quant kernel and of the split-K GEMM (tests use it to check every split gives the same
- * bytes). */
+ * wq_workspace_bytes() bytes, 256-byte aligned; its contents need no initialisation.  The
+ * library uses it only to stage the INT8 payload and scales between the two launches of
+ * wq_fused_quant_matmul when M is above the one-launch limit and the caller passed no
+ * x_q_out / x_scale_out.  Fails with WQ_ERR_DEVICE if the device is not gfx950.
+ * Reads the environment once:
+ *   WQ_LOG=1          one line per call describing the chosen launch;
+ *   WQ_FORCE_SPLIT=n  the K-split factor of the quant kernel (tests use it to show every
+ *                     split gives the same bytes);
+ *   WQ_DECODE_NT=n    columns per workgroup of the decode GEMM (4, 8 or 16; 0 = auto);
+ *   WQ_FUSED_MAX_M=m  the largest M wq_fused_quant_matmul runs as one launch (default 4). */
 int wq_ctx_create(int device, void* workspace, size_t workspace_bytes, wq_ctx** out);
 void wq_ctx_destroy(wq_ctx* ctx);
 
-/* Force the K-split factor of later calls on this context (the same knob as
+/* Force the K-split factor of later quant calls on this context (the same knob as
  * WQ_FORCE_SPLIT); n = 0 restores the automatic choice.  Results are bit-identical for
- * every split; tests use this to show it.  Returns WQ_ERR_SHAPE for n < 0. */
+ * every split; tests use this to show it.  Returns WQ_ERR_SHAPE for n < 0; a split larger
+ * than K / 512 makes later quant calls return WQ_ERR_SHAPE. */
 int wq_ctx_set_split(wq_ctx* ctx, int n);
 
 /* ---- per-token dynamic INT8 quantisation --------------------------------------------
@@ -128,7 +132,9 @@ int wq_group_quant_fp8_ue8m0(wq_ctx* ctx, const void* x, int64_t T, int64_t G, i
  * Segments (MoE, section 五 of the W8A8 article: group_list = tokens per expert):
  *   batch = E experts and seg_offsets = device int64 [E + 1], non-decreasing, with
  *   seg_offsets[E] == M; rows [seg_offsets[e], seg_offsets[e+1]) use b + e*b_batch_stride
- *   and b_scale + e*N.
+ *   and b_scale + e*N.  Segments need K % 128 == 0, E + ceil(M / 128) <= 4096 and no
+ *   acc_out (else WQ_ERR_UNSUPPORTED); WQ_EPI_SWIGLU_F32 is available with segments only
+ *   and needs N % 256 == 0 (WQ_ERR_SHAPE otherwise).
  * FP8 (SGLang PR #34277: the grouped contraction that reads the packed scales):
  *   payload WQ_PAYLOAD_FP8_E4M3, batch = G groups, a = E4M3 codes with row stride lda
  *   bytes and group stride a_batch_stride bytes; a_scale = the int32 packed storage
@@ -159,12 +165,15 @@ typedef struct {
 
 int wq_quant_matmul(wq_ctx* ctx, const wq_matmul_desc* desc, void* stream);
 
-/* ---- fused quant + INT8 GEMM (one launch) -------------------------------------------
- * The whole chain of section 一 of the W8A8 article in one kernel: per-token quant of the
- * bf16 x [M, K] (row stride ldx), the INT8 GEMM against w [N, K] and the bf16 epilogue,
- * with no HBM round trip of the INT8 payload.  Outputs are bit-identical to
- * wq_dynamic_quant followed by wq_quant_matmul.  y: bf16 [M, N] row stride ldy.  The
- * optional outputs export the (x_q, x_scale) tuple and the int32 accumulators so that a
+/* ---- fused quant + INT8 GEMM -------------------------------------------------------
+ * The whole chain of section 一 of the W8A8 article: per-token quant of the bf16 x [M, K]
+ * (row stride ldx), the INT8 GEMM against w [N, K] and the bf16 epilogue.  Outputs are
+ * bit-identical to wq_dynamic_quant followed by wq_quant_matmul.  y: bf16 [M, N] row
+ * stride ldy.  For M up to the one-launch limit (WQ_FUSED_MAX_M, default 4) one kernel
+ * quantises in registers and never writes the INT8 payload to HBM; above it the call runs
+ * the quant and the GEMM as two launches, staging the payload in x_q_out / x_scale_out
+ * when given, else in the context workspace (WQ_ERR_WORKSPACE if M*K bytes exceed it).
+ * The optional outputs export the (x_q, x_scale) tuple and the int32 accumulators so a
  * downstream Linear can reuse them (the tuple-reuse path of section 一). */
 int wq_fused_quant_matmul(wq_ctx* ctx, const void* x, int64_t M, int64_t K, int64_t ldx,
                           const int8_t* w, const float* w_scale, int64_t N, void* y, int64_t ldy,
