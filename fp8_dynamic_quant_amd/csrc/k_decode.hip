@@ -15,20 +15,19 @@
 //    each wave fetching the rows of its own K quarter, in rounds when M rows do not fit;
 //    the 16-byte chunks of a row are XOR-swizzled by the row index so the MFMA A reads
 //    (16 rows, same chunk) hit 16 different bank groups;
-//  * the fused variant instead loads the bf16 rows into registers, takes the per-row
-//    absmax with an LDS max, and quantises with the same arithmetic as k_quant into the
-//    same swizzled LDS tile;
 //  * v_mfma_i32_16x16x64_i8 accumulates; the four waves' int32 tiles are summed in LDS
 //    (exact) and the scale epilogue writes bf16.
 // NT < 16 leaves MFMA column slots empty (their lanes load nothing): compute is cheap here
 // and the narrower tile puts N/NT workgroups on the chip, e.g. 256 for N = 1024.
+// Above 16 rows the grid's second dimension splits the rows into tiles of 16*MT: every
+// workgroup reads all its rows' activations from L2, so at M = 64 a workgroup per 16 rows
+// with 16 columns moves 128 KiB per CU instead of 272 KiB for all 64 rows and 4 columns.
 #include "wq_device.h"
 #include "wq_kernels.h"
 
 namespace wq {
 
 constexpr int kDecodeChunk = 16;      // 64-deep k-steps of weights held in registers per wave
-constexpr int kDecodeFusedJ = 16;     // 16-byte bf16 chunks per thread held by the fused prologue
 constexpr int kDecodeRoundBytes = 128 * 1024;  // LDS for one round of staged activations
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -59,11 +58,18 @@ __host__ __device__ inline int decode_round_steps(int M, int per) {
   return rs;
 }
 
-template <int MT, int NT, bool FUSED>
+template <int MT, int NT>
 __global__ __launch_bounds__(256) void k_decode(DecodeArgs p) {
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int M = p.M, N = p.N, K = p.K;
+  const int N = p.N, K = p.K;
+  // this workgroup's rows: [row0, row0 + M)
+  const int row0 = blockIdx.y * 16 * MT;
+  const int M = min(p.M - row0, 16 * MT);
+  p.a += (int64_t)row0 * p.lda;
+  p.a_scale += row0;
+  p.y += (int64_t)row0 * p.ldy;
+  if (p.acc_out) p.acc_out += (int64_t)row0 * N;
   const int n0 = blockIdx.x * NT;
   const int cl = lane & 15, kg = lane >> 4;
   const int col = n0 + cl;
@@ -73,14 +79,11 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs p) {
   const int ks0 = min(KST, wv * per), ks1 = min(KST, ks0 + per);
   const int nsteps = ks1 - ks0;
 
-  // LDS layout: [A tile][s_lds 64][inv_lds 64][wsc_lds 16][amax 64][red]
-  const int a_bytes = FUSED ? M * KST * 64 : kDecodeRoundBytes;
+  // LDS layout: [A staging rounds][s_lds 64][wsc_lds 16][red]
   int8_t* a_s = smem;
-  float* s_lds = reinterpret_cast<float*>(smem + a_bytes);
-  float* inv_lds = s_lds + 64;
-  float* wsc_lds = inv_lds + 64;
-  unsigned* amax = reinterpret_cast<unsigned*>(wsc_lds + 16);
-  int* red = reinterpret_cast<int*>(amax + 64);
+  float* s_lds = reinterpret_cast<float*>(smem + kDecodeRoundBytes);
+  float* wsc_lds = s_lds + 64;
+  int* red = reinterpret_cast<int*>(wsc_lds + 16);
 
   // ---- 1. every global load first --------------------------------------------------------
   v4i b[kDecodeChunk];
@@ -93,10 +96,10 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs p) {
   }
   float wsc = 0.0f, asc = 0.0f;
   if (t < NT && n0 + t < N) wsc = p.w_scale[n0 + t];
-  if (!FUSED && t < M) asc = p.a_scale[t];
+  if (t < M) asc = p.a_scale[t];
 
   // ---- 2. activations --------------------------------------------------------------------
-  const int rs = FUSED ? 0 : decode_round_steps(M, per);  // non-fused: steps per round
+  const int rs = decode_round_steps(M, per);               // steps per staging round
   int8_t* my_a = a_s + wv * (kDecodeRoundBytes / 4);      // this wave's staging region
   auto stage_round = [&](int r0) {
     // rows [0, M) x steps [r0, r0 + rs) of this wave's quarter -> my_a, swizzled rows of rs*64 B
@@ -117,74 +120,9 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs p) {
                                        (lds_ptr_t)(my_a + off), 16, 0, 0);
     }
   };
-  if constexpr (!FUSED) {
-    if (nsteps > 0) stage_round(0);
-  }
-
-  if constexpr (FUSED) {
-    // 2a. the bf16 rows into registers (all chunks of all M rows, spread over 256 threads)
-    const int C = K >> 3;  // 8-element chunks per row
-    const int tot = M * C;
-    uint4 xr[kDecodeFusedJ];
-#pragma unroll
-    for (int j = 0; j < kDecodeFusedJ; ++j) {
-      const int e = t + 256 * j;
-      if (e < tot) {
-        const int m = e / C, c = e - m * C;
-        xr[j] = *reinterpret_cast<const uint4*>(p.x + (int64_t)m * p.ldx + (int64_t)c * 8);
-      } else {
-        xr[j] = uint4{0u, 0u, 0u, 0u};
-      }
-    }
-    if (t < 64) amax[t] = 0u;
-    if (t < NT) wsc_lds[t] = wsc;
-    __syncthreads();
-    // 2b. per-row absmax: a wave's 64 chunks share a row when C % 64 == 0
-    const bool wave_rows = (C & 63) == 0;
-#pragma unroll
-    for (int j = 0; j < kDecodeFusedJ; ++j) {
-      const int e = t + 256 * j;
-      if (256 * j < tot) {  // uniform
-        float a = (e < tot) ? bf16x8_absmax(xr[j]) : 0.0f;
-        if (wave_rows) {
-          a = wave_max(a);
-          if (lane == 0 && e < tot) atomicMax(&amax[e / C], __float_as_uint(a));
-        } else if (e < tot) {
-          atomicMax(&amax[e / C], __float_as_uint(a));
-        }
-      }
-    }
-    __syncthreads();
-    if (t < M) {
-      const float s = __fdiv_rn(__uint_as_float(amax[t]), 127.0f);
-      s_lds[t] = s;
-      inv_lds[t] = __fdiv_rn(1.0f, s);
-    }
-    __syncthreads();
-    // 2c. quantise into the swizzled LDS tile; 8-byte halves of 16-byte chunks
-    const int rowb = KST * 64;
-#pragma unroll
-    for (int j = 0; j < kDecodeFusedJ; ++j) {
-      const int e = t + 256 * j;
-      if (e < tot) {
-        const int m = e / C, c = e - m * C;
-        const uint2 o = quant8_bf16(xr[j], s_lds[m], inv_lds[m]);
-        *reinterpret_cast<uint2*>(a_s + swz(m, c >> 1, rowb) + (c & 1) * 8) = o;
-        if (p.xq_out && blockIdx.x == 0) *reinterpret_cast<uint2*>(p.xq_out + (int64_t)m * K + c * 8) = o;
-      }
-    }
-    // K tail to the 64 multiple: zero (its B is zero too, but keep the bytes defined)
-    for (int e = t; e < M * (rowb / 8 - C); e += 256) {
-      const int tail = rowb / 8 - C;
-      const int m = e / tail, c = C + (e - m * tail);
-      *reinterpret_cast<uint2*>(a_s + swz(m, c >> 1, rowb) + (c & 1) * 8) = uint2{0u, 0u};
-    }
-    if (p.xs_out && blockIdx.x == 0 && t < M) p.xs_out[t] = s_lds[t];
-    __syncthreads();
-  } else {
-    if (t < M) s_lds[t] = asc;
-    if (t < NT) wsc_lds[t] = wsc;
-  }
+  if (nsteps > 0) stage_round(0);
+  if (t < M) s_lds[t] = asc;
+  if (t < NT) wsc_lds[t] = wsc;
 
   // ---- 3. MFMA over this wave's K quarter -------------------------------------------------
   v4i acc[MT];
@@ -227,20 +165,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs p) {
     }
   };
 
-  if constexpr (FUSED) {
-    // the tile holds whole rows; this wave's steps start at ks0
-    for (int kb = 0; kb < nsteps; kb += kDecodeChunk) {
-      if (kb != 0) {
-#pragma unroll
-        for (int j = 0; j < kDecodeChunk; ++j) {
-          const int ks = ks0 + kb + j;
-          b[j] = (bvalid && ks < ks1 && ks * 64 + 16 * kg < K) ? *reinterpret_cast<const v4i*>(wcol + ks * 64)
-                                                               : v4i{0, 0, 0, 0};
-        }
-      }
-      mfma_steps(a_s, KST * 64, kb, 0, min(kDecodeChunk, nsteps - kb), -ks0);
-    }
-  } else {
+  {
     // rounds of rs steps staged in this wave's region and weight chunks of 16 steps nest:
     // walk in pieces of min(rs, 16) steps
     const int piece = min(rs, kDecodeChunk);
@@ -453,21 +378,12 @@ hipError_t launch_gemv(const DecodeArgs& a, hipStream_t st) {
   return gemv_mr<8>(a, false, st);
 }
 
-size_t decode_lds_bytes(int M, int K, bool fused) {
-  const int MT = (M + 15) / 16;
-  const int KST = (K + 63) / 64;
-  const size_t a = fused ? (size_t)M * KST * 64 : (size_t)kDecodeRoundBytes;
-  return a + (64 + 64 + 16 + 64) * 4 + (size_t)4 * MT * 4 * 64 * 4;
-}
+size_t decode_lds_bytes(int mt) { return (size_t)kDecodeRoundBytes + (64 + 16) * 4 + (size_t)4 * mt * 4 * 64 * 4; }
 
-bool decode_fused_fits(int M, int K) {
-  return (int64_t)M * (K / 8) <= 256 * kDecodeFusedJ && decode_lds_bytes(M, K, true) <= 144 * 1024;
-}
-
-template <int MT, int NT, bool FUSED>
+template <int MT, int NT>
 static hipError_t decode_launch(const DecodeArgs& a, hipStream_t st) {
-  const size_t lds = decode_lds_bytes(a.M, a.K, FUSED);
-  auto kfn = k_decode<MT, NT, FUSED>;
+  const size_t lds = decode_lds_bytes(MT);
+  auto kfn = k_decode<MT, NT>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
@@ -475,34 +391,27 @@ static hipError_t decode_launch(const DecodeArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  dim3 grid((unsigned)((a.N + NT - 1) / NT)), block(256);
+  dim3 grid((unsigned)((a.N + NT - 1) / NT), (unsigned)((a.M + 16 * MT - 1) / (16 * MT))), block(256);
   hipLaunchKernelGGL(kfn, grid, block, lds, st, a);
   return hipGetLastError();
 }
 
-template <int MT, int NT>
-static hipError_t decode_mt_nt(const DecodeArgs& a, bool fused, hipStream_t st) {
-  return fused ? decode_launch<MT, NT, true>(a, st) : decode_launch<MT, NT, false>(a, st);
-}
-
 template <int MT>
-static hipError_t decode_mt(const DecodeArgs& a, int nt, bool fused, hipStream_t st) {
+static hipError_t decode_mt(const DecodeArgs& a, int nt, hipStream_t st) {
   switch (nt) {
-    case 4: return decode_mt_nt<MT, 4>(a, fused, st);
-    case 8: return decode_mt_nt<MT, 8>(a, fused, st);
-    case 16: return decode_mt_nt<MT, 16>(a, fused, st);
+    case 4: return decode_launch<MT, 4>(a, st);
+    case 8: return decode_launch<MT, 8>(a, st);
+    case 16: return decode_launch<MT, 16>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int nt, hipStream_t st) {
-  const bool fused = a.x != nullptr;
-  if (fused && !decode_fused_fits(a.M, a.K)) return hipErrorInvalidValue;
-  switch ((a.M + 15) / 16) {
-    case 1: return decode_mt<1>(a, nt, fused, st);
-    case 2: return decode_mt<2>(a, nt, fused, st);
-    case 3: return decode_mt<3>(a, nt, fused, st);
-    case 4: return decode_mt<4>(a, nt, fused, st);
+hipError_t launch_decode(const DecodeArgs& a, int nt, int mt, hipStream_t st) {
+  if (a.x != nullptr || a.M < 1 || a.M > 64) return hipErrorInvalidValue;
+  switch (mt) {
+    case 1: return decode_mt<1>(a, nt, st);
+    case 2: return decode_mt<2>(a, nt, st);
+    case 4: return decode_mt<4>(a, nt, st);
     default: return hipErrorInvalidValue;
   }
 }

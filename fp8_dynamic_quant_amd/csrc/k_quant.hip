@@ -63,15 +63,9 @@ __device__ __forceinline__ void load_gamma(const uint16_t* g, float* v) {
 template <int EPC>
 __device__ __forceinline__ void store_codes(int8_t* dst, const float* v, float s, float inv) {
   if constexpr (EPC == 8) {
-    uint2 o;
-    o.x = pack4_i8(quant_i8_fast(v[0], s, inv), quant_i8_fast(v[1], s, inv), quant_i8_fast(v[2], s, inv),
-                   quant_i8_fast(v[3], s, inv));
-    o.y = pack4_i8(quant_i8_fast(v[4], s, inv), quant_i8_fast(v[5], s, inv), quant_i8_fast(v[6], s, inv),
-                   quant_i8_fast(v[7], s, inv));
-    *reinterpret_cast<uint2*>(dst) = o;
+    *reinterpret_cast<uint2*>(dst) = quant8(v, s, inv);
   } else {
-    *reinterpret_cast<uint32_t*>(dst) = pack4_i8(quant_i8_fast(v[0], s, inv), quant_i8_fast(v[1], s, inv),
-                                                 quant_i8_fast(v[2], s, inv), quant_i8_fast(v[3], s, inv));
+    *reinterpret_cast<uint32_t*>(dst) = quant4(v, s, inv);
   }
 }
 

@@ -27,11 +27,14 @@ struct wq_ctx {
   int log;
   int force_split;
   int decode_nt;  // 0 = automatic; else 4, 8 or 16 (WQ_DECODE_NT)
-  // Largest M quantised inside the GEMM launch.  Every workgroup then quantises all M
-  // rows itself (no workgroup may wait for another), so the prologue grows with M while
-  // the second launch it saves costs a fixed ~2 us; above this M the call runs the quant
-  // kernel and then the GEMM.  WQ_FUSED_MAX_M overrides (<= 64).
-  int fused_max_m;
+  int decode_mt;  // 0 = automatic; else 1, 2 or 4 16-row tiles per workgroup (WQ_DECODE_MT)
+  // The fused call quantises inside the GEMM launch up to these M (measured on MI355X at
+  // K = 4096, N = 1024): the dot4 GEMV up to 2 rows, the 8-wave MFMA kernel up to 16.
+  // Every workgroup then quantises all M rows itself (no workgroup may wait for another),
+  // ~0.3 us per row, while a second launch costs a fixed ~6 us; above the limit the call
+  // runs the quant kernel and then the GEMM.
+  int fused_max_m;       // largest M the one-launch fused kernel takes (WQ_FUSED_MAX_M)
+  int fused_gemv_max_m;  // largest M the fused GEMV takes instead (WQ_FUSED_GEMV_MAX_M)
 };
 
 namespace {
@@ -67,6 +70,35 @@ int decode_nt(const wq_ctx* c, int64_t N) {
     if ((N + nt - 1) / nt <= 2 * (int64_t)c->num_cu) return nt;
   }
   return 16;
+}
+
+// Decode tile shape for M rows: up to 16 rows, one 16-row tile of decode_nt columns.
+// Above 16 rows every workgroup would read all M activation rows from L2 for a handful
+// of columns, so the rows are split into 16-row tiles (grid y) and the column tile nt is
+// the one that moves the fewest bytes per CU: rounds of workgroups per CU times the bytes
+// one workgroup reads (16 K activation bytes per row tile + nt K weight bytes); ties go to
+// the shape with more workgroups.
+void decode_shape(const wq_ctx* c, int64_t M, int64_t N, int* nt, int* mt) {
+  *mt = c->decode_mt > 0 ? c->decode_mt : 1;
+  if (M <= 16 && c->decode_mt == 0) {
+    *nt = decode_nt(c, N);
+    return;
+  }
+  if (c->decode_nt > 0) {
+    *nt = c->decode_nt;
+    return;
+  }
+  const int64_t rt = (M + 16 * *mt - 1) / (16 * *mt);
+  int64_t best = -1;
+  for (int w : {16, 8, 4}) {
+    const int64_t wgs = (N + w - 1) / w * rt;
+    const int64_t rounds = (wgs + c->num_cu - 1) / c->num_cu;
+    const int64_t cost = rounds * (16 * *mt + w);
+    if (best < 0 || cost <= best) {
+      best = cost;
+      *nt = w;
+    }
+  }
 }
 
 int quant_split(const wq_ctx* c, int64_t M, int64_t K) {
@@ -119,9 +151,15 @@ int wq_ctx_create(int device, void* workspace, size_t workspace_bytes, wq_ctx** 
   const char* dn = std::getenv("WQ_DECODE_NT");
   c->decode_nt = dn ? std::atoi(dn) : 0;
   if (c->decode_nt != 0 && c->decode_nt != 4 && c->decode_nt != 8 && c->decode_nt != 16) c->decode_nt = 0;
+  const char* dm = std::getenv("WQ_DECODE_MT");
+  c->decode_mt = dm ? std::atoi(dm) : 0;
+  if (c->decode_mt != 0 && c->decode_mt != 1 && c->decode_mt != 2 && c->decode_mt != 4) c->decode_mt = 0;
   const char* fm = std::getenv("WQ_FUSED_MAX_M");
-  c->fused_max_m = fm ? std::atoi(fm) : 4;
-  if (c->fused_max_m < 0 || c->fused_max_m > 64) c->fused_max_m = 4;
+  c->fused_max_m = fm ? std::atoi(fm) : 16;
+  if (c->fused_max_m < 0 || c->fused_max_m > 64) c->fused_max_m = 16;
+  const char* gm = std::getenv("WQ_FUSED_GEMV_MAX_M");
+  c->fused_gemv_max_m = gm ? std::atoi(gm) : 2;
+  if (c->fused_gemv_max_m < 0 || c->fused_gemv_max_m > 4) c->fused_gemv_max_m = 2;
   *out = c;
   return WQ_OK;
 }
@@ -238,11 +276,13 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
                      (long long)N, (long long)K, (long long)((N + 3) / 4));
       return status_of(e);
     }
-    const int nt = decode_nt(c, N);
-    hipError_t e = wq::launch_decode(a, nt, st);
+    int nt, mt;
+    decode_shape(c, M, N, &nt, &mt);
+    hipError_t e = wq::launch_decode(a, nt, mt, st);
     if (c->log)
-      std::fprintf(stderr, "[wq] quant_matmul int8 decode M=%lld N=%lld K=%lld cols/wg=%d grid=%lld cus=%d\n",
-                   (long long)M, (long long)N, (long long)K, nt, (long long)((N + nt - 1) / nt), c->num_cu);
+      std::fprintf(stderr, "[wq] quant_matmul int8 decode M=%lld N=%lld K=%lld cols/wg=%d rows/wg=%d grid=%lldx%lld cus=%d\n",
+                   (long long)M, (long long)N, (long long)K, nt, 16 * mt, (long long)((N + nt - 1) / nt),
+                   (long long)((M + 16 * mt - 1) / (16 * mt)), c->num_cu);
     return status_of(e);
   }
   wq::TileArgs t{};
@@ -336,8 +376,8 @@ int wq_fused_quant_matmul(wq_ctx* c, const void* x, int64_t M, int64_t K, int64_
     return WQ_ERR_ALIGN;
   DeviceGuard g(c->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool one_launch_gemv = M <= c->fused_max_m && wq::gemv_fits((int)M, (int)K, true) && c->decode_nt == 0;
-  const bool one_launch_mfma = M <= c->fused_max_m && !one_launch_gemv && wq::decode_fused_fits((int)M, (int)K);
+  const bool one_launch_gemv = M <= c->fused_gemv_max_m && wq::gemv_fits((int)M, (int)K, true) && c->decode_nt == 0;
+  const bool one_launch_mfma = M <= c->fused_max_m && !one_launch_gemv && wq::fused_decode_fits((int)M, (int)K);
   if (!one_launch_gemv && !one_launch_mfma) {
     // quantise, then the GEMM (two launches); the INT8 payload goes through the
     // caller's buffers when given, else through the context workspace
@@ -373,9 +413,9 @@ int wq_fused_quant_matmul(wq_ctx* c, const void* x, int64_t M, int64_t K, int64_
     return status_of(e);
   }
   const int nt = decode_nt(c, N);
-  hipError_t e = wq::launch_decode(a, nt, st);
+  hipError_t e = wq::launch_fused_decode(a, nt, st);
   if (c->log)
-    std::fprintf(stderr, "[wq] fused_quant_matmul M=%lld N=%lld K=%lld cols/wg=%d grid=%lld cus=%d\n",
+    std::fprintf(stderr, "[wq] fused_quant_matmul one launch M=%lld N=%lld K=%lld cols/wg=%d grid=%lld cus=%d\n",
                  (long long)M, (long long)N, (long long)K, nt, (long long)((N + nt - 1) / nt), c->num_cu);
   return status_of(e);
 }

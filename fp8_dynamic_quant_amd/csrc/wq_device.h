@@ -44,25 +44,68 @@ __device__ __forceinline__ int quant_i8(float v, float s) {
   return (int)r;
 }
 
-// The same code as quant_i8, usually without the division.  With inv = RN(1/s),
-// t = RN(v * inv) lies within |v/s| * 1.5 * 2^-23 of RN(v/s) (three roundings of 2^-24
-// each).  When t is farther than that from every half-integer, RN(v/s) and t share the
-// integer they round to, so rint(t) is the answer; otherwise (ties and near-ties, or a
-// non-finite t when s is subnormal) the correctly rounded division decides.
-__device__ __forceinline__ int quant_i8_fast(float v, float s, float inv) {
-  if (s == 0.0f) return 0;
-  const float tq = __fmul_rn(v, inv);
-  float r = rintf(tq);
-  const float d = fabsf(__fsub_rn(tq, r));
-  const float margin = __fmul_rn(fmaxf(fabsf(tq), 1.0f), 4.8e-7f);
-  if (!(__fsub_rn(0.5f, d) > margin)) r = rintf(__fdiv_rn(v, s));
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (int)r;
-}
-
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
   return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
          ((uint32_t)(d & 0xFF) << 24);
+}
+
+// Four f32 values that hold integers in [-127, 127] -> their INT8 codes packed little
+// endian.  Adding 1.5 * 2^23 (exact for such integers) leaves the integer, in two's
+// complement, in the low mantissa bits; v_perm_b32 gathers the four low bytes.
+__device__ __forceinline__ uint32_t pack4_rounded(float r0, float r1, float r2, float r3) {
+  const float kPlace = 12582912.0f;  // 1.5 * 2^23
+  const uint32_t b0 = __float_as_uint(__fadd_rn(r0, kPlace));
+  const uint32_t b1 = __float_as_uint(__fadd_rn(r1, kPlace));
+  const uint32_t b2 = __float_as_uint(__fadd_rn(r2, kPlace));
+  const uint32_t b3 = __float_as_uint(__fadd_rn(r3, kPlace));
+  // selector byte k picks output byte k: 0..3 = bytes of the second operand, 4..7 = bytes
+  // of the first, 0x0c = zero
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);  // b0.byte0, b1.byte0, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x04000c0cu);  // 0, 0, b2.byte0, b3.byte0
+  return lo | hi;
+}
+
+// Fast path of quant_i8 for N values at once, without the division, for a normal finite
+// scale s (s = RN(absmax/127), so |v/s| <= 127 (1 + 2^-23) for every value of the row).
+// With inv = RN(1/s), t = RN(v * inv) lies within 3 * 2^-24 * |v/s| < 2.3e-5 of RN(v/s).
+// When every t is at least 2^-14 from the nearest half-integer, RN(v/s) rounds to the same
+// integer as t, which is within [-127, 127], so rint(t) is the code and the clamp is moot.
+// Returns false for a near-tie (the caller then takes the exact path for these N values;
+// a wave branches once per N values, not per value).  Only the largest |t - rint(t)| is
+// compared: one compare per N values.
+template <int N>
+__device__ __forceinline__ bool quant_fast(const float* v, float inv, float* r) {
+  constexpr float kGuard = 0.49993896484375f;  // 0.5 - 2^-14
+  float dmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float t = __fmul_rn(v[i], inv);
+    r[i] = rintf(t);
+    dmax = fmaxf(dmax, fabsf(__fsub_rn(t, r[i])));
+  }
+  return dmax < kGuard;
+}
+
+// the fast path's precondition on the scale: normal and finite (a zero, subnormal or
+// infinite scale goes to the exact path, where the clamp and the s == 0 rule act)
+__device__ __forceinline__ bool quant_scale_normal(float s) {
+  return s >= 1.17549435e-38f && s <= 3.40282347e+38f;
+}
+
+// INT8 codes of 8 values (two packed words), bit-identical to quant_i8 on each value.
+__device__ __forceinline__ uint2 quant8(const float* v, float s, float inv) {
+  float r[8];
+  if (quant_scale_normal(s) && quant_fast<8>(v, inv, r))
+    return uint2{pack4_rounded(r[0], r[1], r[2], r[3]), pack4_rounded(r[4], r[5], r[6], r[7])};
+  return uint2{pack4_i8(quant_i8(v[0], s), quant_i8(v[1], s), quant_i8(v[2], s), quant_i8(v[3], s)),
+               pack4_i8(quant_i8(v[4], s), quant_i8(v[5], s), quant_i8(v[6], s), quant_i8(v[7], s))};
+}
+
+// INT8 codes of 4 values (one packed word), bit-identical to quant_i8 on each value.
+__device__ __forceinline__ uint32_t quant4(const float* v, float s, float inv) {
+  float r[4];
+  if (quant_scale_normal(s) && quant_fast<4>(v, inv, r)) return pack4_rounded(r[0], r[1], r[2], r[3]);
+  return pack4_i8(quant_i8(v[0], s), quant_i8(v[1], s), quant_i8(v[2], s), quant_i8(v[3], s));
 }
 
 // max |x| over 8 bf16 values packed in 16 bytes
@@ -80,13 +123,13 @@ __device__ __forceinline__ float bf16x8_absmax(const uint4 u) {
 // INT8 codes of 8 bf16 values (16 bytes) -> 8 bytes
 __device__ __forceinline__ uint2 quant8_bf16(const uint4 u, float s, float inv) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-  int q[8];
+  float v[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    q[2 * i] = quant_i8_fast(__uint_as_float(w[i] << 16), s, inv);
-    q[2 * i + 1] = quant_i8_fast(__uint_as_float(w[i] & 0xFFFF0000u), s, inv);
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
-  return uint2{pack4_i8(q[0], q[1], q[2], q[3]), pack4_i8(q[4], q[5], q[6], q[7])};
+  return quant8(v, s, inv);
 }
 
 // Fixed-sequence f32 exp: n = rint(x*log2e); r = (x - n*ln2_hi) - n*ln2_lo;

@@ -12,8 +12,8 @@ hipError_t launch_dynamic_quant(const void* x, bool x_f32, int64_t M, int K, int
                                 const uint16_t* gamma, float eps, const int32_t* row_index, int8_t* xq,
                                 float* xs, int S, hipStream_t st, int* ch_used);
 
-// Decode-sized INT8 GEMM, M <= 64 (k_decode.hip).  When x is non-null the kernel
-// quantises the bf16 rows itself (fused path) and a / a_scale are ignored.
+// Decode-sized INT8 GEMM, M <= 64 (k_decode.hip); also the argument block of the fused
+// decode kernels (x non-null: they quantise the bf16 rows themselves).
 struct DecodeArgs {
   const int8_t* a;        // int8 [M, lda]
   int64_t lda;
@@ -29,12 +29,13 @@ struct DecodeArgs {
   int8_t* xq_out;         // optional (fused)
   float* xs_out;          // optional (fused)
 };
-// nt: output columns per workgroup (4, 8 or 16).
-hipError_t launch_decode(const DecodeArgs& a, int nt, hipStream_t st);
-// dynamic LDS bytes the decode kernel needs
-size_t decode_lds_bytes(int M, int K, bool fused);
-// whether the fused (quantise-inside) decode kernel can hold M rows of length K
-bool decode_fused_fits(int M, int K);
+// nt: output columns per workgroup (4, 8 or 16); mt: 16-row MFMA tiles per workgroup
+// (1, 2 or 4), the grid's second dimension covering ceil(M / (16 mt)) row tiles.
+hipError_t launch_decode(const DecodeArgs& a, int nt, int mt, hipStream_t st);
+// One-launch fused quant + GEMM for M <= 64, K % 512 == 0, K <= 4096 (k_fused.hip);
+// nt output columns per workgroup (4, 8 or 16)
+hipError_t launch_fused_decode(const DecodeArgs& a, int nt, hipStream_t st);
+bool fused_decode_fits(int M, int K);
 // GEMV-style kernel for M <= 8 (k_decode.hip); fused needs M <= 4 and K <= 8192
 hipError_t launch_gemv(const DecodeArgs& a, hipStream_t st);
 bool gemv_fits(int M, int K, bool fused);

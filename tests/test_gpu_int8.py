@@ -67,6 +67,16 @@ def test_wq_a_decode_standalone_and_fused(M):
     assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
 
 
+@pytest.mark.parametrize("M,K,N", [(1, 512, 64), (15, 1024, 128), (16, 2048, 256), (17, 4096, 1040), (31, 4096, 48),
+                                   (48, 1024, 1040), (64, 4096, 1024), (2, 4096, 32768), (9, 512, 4096)])
+def test_fused_one_launch_shapes(M, K, N):
+    # the one-launch fused kernel takes K % 512 == 0, K <= 4096, M <= 64: one 16-row group
+    # and several, a partial last group, narrow and wide N, exported x_q / x_scale / acc
+    x = syn.activations((97, M, K), M, K, outlier_frac=0.005, outlier_mul=30.0)
+    w, sw = syn.int8_weights((98, N, K), N, K)
+    _check_linear(x, w, sw, fused=True)
+
+
 @pytest.mark.parametrize("split", [1, 2, 4, 8, 16, 64])
 def test_every_split_gives_identical_bytes(split):
     x, w, sw = syn.wq_a_linear(7)
