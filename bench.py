@@ -4,15 +4,20 @@
 Workload (the wq_a-shaped decode linear of "DeepSeek-V4 W8A8 性能分析", section 三):
 X bf16 [M, 4096] ~ N(0,1) with 0.5% outliers x30, M in {1,2,4,7,8,16,32,64}, against
 W int8 [4096 -> 1024] with f32 per-channel scales.  One step = the fused quant+GEMM
-linear (one launch) once at every M of the sweep.  Inputs are resident in HBM and rotate
-over enough distinct copies (>= 512 MiB) that neither L2 nor the 256 MB Infinity Cache
-holds the weights between calls.  Each step is captured in a HIP graph so the host launch
-rate does not bound the measurement.
+linear once at every M of the sweep.  Inputs are resident in HBM and rotate over enough
+distinct copies (>= 512 MiB) that neither L2 nor the 256 MB Infinity Cache holds the
+weights between calls.  Steps are captured in HIP graphs so the host launch rate does not
+bound the measurement.
 
 Printed: one JSON line with the metric (mean us per fused call over the sweep), the
 per-M sweep (fused and standalone quant+GEMM, GB/s, fraction of the 8 TB/s HBM peak),
-the M=8192 wide-linear prefill point (int8 TOPS against 5.0 POPS), the roofline object
-for the dominant kernel and the CPU oracle baseline.
+the roofline object of the dominant kernel, and one measurement per remaining step of the
+path: the M=8192 wide-linear prefill GEMM (int8 TOPS), the standalone quant, the FP8
+per-token-group quant with packed UE8M0 scales and the grouped FP8 contraction, and the
+expert-sorted MoE block; then the CPU oracle baseline.
+
+--traffic-probe runs only the roofline kernel's launches (plus a copy kernel of known
+size that calibrates the counters) for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs.
 """
 
 from __future__ import annotations
@@ -29,10 +34,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
+FP8_PEAK_TOPS = 5000.0
 SWEEP = (1, 2, 4, 7, 8, 16, 32, 64)
 K_A, N_A = 4096, 1024
 ROTATE_BYTES = 512 << 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_decode_wq_a.json")
+ROOFLINE_KERNEL = "k_fused_decode"  # the one-launch fused kernel (wq_fused_path == 2)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_fused_decode_wq_a.json")
+KERNEL_SOURCES = ("k_fused.hip", "wq_device.h", "wq_api.hip", "wq_kernels.h")
 
 
 def fused_bytes(M, K=K_A, N=N_A):
@@ -47,7 +55,7 @@ def standalone_bytes(M, K=K_A, N=N_A):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("k_decode.hip", "k_quant.hip", "wq_device.h", "wq_api.hip"):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -56,8 +64,6 @@ def kernel_source_hash():
 def cpu_baseline(budget_s=10.0):
     """Time the CPU oracle (as it stands) on the same workload: the full fused chain at
     every M of the sweep, repeated until about budget_s seconds have passed."""
-    import numpy as np
-
     import synthetic as syn
     from oracle import int8_linear as il
 
@@ -93,8 +99,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-sweep", action="store_true", help="skip the per-M breakdown and the floors")
+    ap.add_argument("--no-rows", action="store_true", help="skip the prefill / FP8 / MoE measurements")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the standalone sweep and the floors")
+    ap.add_argument("--traffic-probe", action="store_true", help="only the roofline kernel's launches, for counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the kernels run on one MI355X and the "
@@ -110,6 +117,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     wq.lib()
+    stream = torch.cuda.Stream()
 
     # ---- inputs: R rotating copies of W / w_scale / X / Y per M --------------------------
     R = max(2, ROTATE_BYTES // (K_A * N_A))
@@ -122,21 +130,8 @@ def main():
     xs = {M: [torch.from_numpy(x_host[M].view(np.int16)).to(dev).view(torch.bfloat16).clone() for _ in range(R)]
           for M in SWEEP}
     ys = {M: [torch.empty((M, N_A), dtype=torch.bfloat16, device=dev) for _ in range(R)] for M in SWEEP}
-    xq = {M: [torch.empty((M, K_A), dtype=torch.int8, device=dev) for _ in range(R)] for M in SWEEP}
-    xsc = {M: [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(R)] for M in SWEEP}
-
-    # one correctness check against the oracle before timing (the full parity suite is in tests/)
-    from oracle import int8_linear as il  # noqa: E402  (checker only; not on the timed path)
-
-    for M in (1, 64):
-        y = wq.wq_fused_quant_matmul(xs[M][0], ws[0], sws[0])
-        ref = il.linear_w8a8(x_host[M], w_host, sw_host)["y"]
-        got = y.view(torch.int16).cpu().numpy().view(np.uint16)
-        from oracle.numerics import bf16_ulp_distance
-
-        assert bf16_ulp_distance(got, ref).max() <= 1, "fused linear disagrees with the oracle"
-
-    stream = torch.cuda.Stream()
+    paths = {M: wq.wq_fused_path(M, K_A, N_A) for M in SWEEP}
+    roof_ms = [M for M in SWEEP if paths[M] == 2]
 
     def graph_len(steps):
         """Steps per captured graph: the largest divisor of `steps` not above R, so the
@@ -160,15 +155,6 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    def fused_step(r, Ms=SWEEP):
-        for M in Ms:
-            wq.wq_fused_quant_matmul(xs[M][r], ws[r], sws[r], y=ys[M][r])
-
-    def standalone_step(r, Ms=SWEEP):
-        for M in Ms:
-            wq.wq_dynamic_quant(xs[M][r], x_q=xq[M][r], x_scale=xsc[M][r])
-            wq.wq_quant_matmul(xq[M][r], xsc[M][r], ws[r], sws[r], y=ys[M][r])
-
     def time_graph(g, n_per_graph, steps, warmup):
         """Replay g (n_per_graph steps each) to cover `warmup`, then exactly `steps` steps
         between two events on the replay stream; returns us per step."""
@@ -185,61 +171,133 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / (reps * n_per_graph)
 
+    def fused_step(r, Ms=SWEEP):
+        for M in Ms:
+            wq.wq_fused_quant_matmul(xs[M][r], ws[r], sws[r], y=ys[M][r])
+
+    def time_in_graph(fn, n=64):
+        """Mean us per call of fn(r) over replays of a graph of n back-to-back calls
+        r = 0..n-1 (for calls of a few us, where eager launches would time the host)."""
+        g = capture(fn, n)
+        us = time_graph(g, n, 4 * n, n)
+        del g
+        return us
+
+    def time_events(fn, n, warm=3):
+        """Mean us per call of fn() over n eager calls on the side stream (launch-bound
+        work is not timed this way: every call here runs for tens of us or more)."""
+        with torch.cuda.stream(stream):
+            for _ in range(warm):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(n):
+                fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    if args.traffic_probe:
+        # eager launches of the roofline kernel, each on a cold weight copy, then one copy
+        # kernel of exactly 64 MiB read + 64 MiB written for the counter calibration
+        with torch.cuda.stream(stream):
+            for M in roof_ms:
+                for r in range(8):
+                    fused_step(r, (M,))
+            src = torch.ones(64 << 20, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": {"roofline_ms": roof_ms, "launches_per_m": 8, "calibration_copy_bytes": 64 << 20,
+                                            "kernel_source_hash": kernel_source_hash()}}))
+        return
+
+    # one correctness check against the oracle before timing (the full parity suite is in tests/)
+    from oracle import int8_linear as il  # noqa: E402  (checker only; not on the timed path)
+    from oracle.numerics import bf16_ulp_distance  # noqa: E402
+
+    for M in (1, 8, 64):
+        y = wq.wq_fused_quant_matmul(xs[M][0], ws[0], sws[0])
+        ref = il.linear_w8a8(x_host[M], w_host, sw_host)["y"]
+        got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert bf16_ulp_distance(got, ref).max() <= 1, "fused linear disagrees with the oracle"
+
     # ---- headline: fused decode linear over the sweep -------------------------------------
     G = graph_len(args.steps)
     g_all = capture(lambda r: fused_step(r), G)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     us_step = time_graph(g_all, G, args.steps, args.warmup)
     wall = time.perf_counter() - t0
     us_per_call = us_step / len(SWEEP)
     del g_all
 
-    # ---- per-M: fused and standalone ------------------------------------------------------
-    sweep = []
-    for M in ([] if args.no_sweep else SWEEP):
+    # ---- per-M: fused (always, for the roofline) and standalone -----------------------------
+    xq = {M: [torch.empty((M, K_A), dtype=torch.int8, device=dev) for _ in range(R)] for M in SWEEP}
+    xsc = {M: [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(R)] for M in SWEEP}
+
+    def standalone_step(r, Ms=SWEEP):
+        for M in Ms:
+            wq.wq_dynamic_quant(xs[M][r], x_q=xq[M][r], x_scale=xsc[M][r])
+            wq.wq_quant_matmul(xq[M][r], xsc[M][r], ws[r], sws[r], y=ys[M][r])
+
+    sweep, us_fused = [], {}
+    for M in SWEEP:
         gf = capture(lambda r, M=M: fused_step(r, (M,)), R)
-        us_f = time_graph(gf, R, 4 * R, R)
+        us_fused[M] = time_graph(gf, R, 4 * R, R)
         del gf
-        gs = capture(lambda r, M=M: standalone_step(r, (M,)), R)
-        us_s = time_graph(gs, R, 4 * R, R)
-        del gs
-        bf, bs = fused_bytes(M), standalone_bytes(M)
-        sweep.append({
-            "M": M,
-            "us_fused": round(us_f, 3),
-            "us_standalone_quant_plus_gemm": round(us_s, 3),
-            "fused_GBps": round(bf / us_f / 1e3, 1),
-            "fused_frac_hbm": round(bf / us_f / 1e3 / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes": bf,
-            "standalone_bytes": bs,
-            "TOPS": round(2 * M * K_A * N_A / us_f / 1e6, 3),
-        })
+        row = {"M": M, "path": wq.FUSED_PATHS[paths[M]], "us_fused": round(us_fused[M], 3)}
+        if not args.no_sweep:
+            gs = capture(lambda r, M=M: standalone_step(r, (M,)), R)
+            row["us_standalone_quant_plus_gemm"] = round(time_graph(gs, R, 4 * R, R), 3)
+            del gs
+        bf = fused_bytes(M)
+        row.update({"fused_GBps": round(bf / us_fused[M] / 1e3, 1),
+                    "fused_frac_hbm": round(bf / us_fused[M] / 1e3 / HBM_PEAK_GBS, 4),
+                    "algorithmic_bytes": bf, "standalone_bytes": standalone_bytes(M),
+                    "TOPS": round(2 * M * K_A * N_A / us_fused[M] / 1e6, 3)})
+        sweep.append(row)
         torch.cuda.synchronize()
 
-    # reference floors: an empty-ish launch and a plain same-size device copy
-    tiny = torch.zeros(1, device=dev)
-    src = torch.empty(K_A * N_A, dtype=torch.uint8, device=dev)
-    dst_bufs = [torch.empty_like(src) for _ in range(R)]
-
-    def floor_step(r):
-        for _ in SWEEP:
-            tiny.add_(1.0)
-
-    def copy_step(r):
-        dst_bufs[r].copy_(ws[r].view(-1))
-
-    launch_floor = copy_us = float("nan")
+    # reference floors: a tiny launch and a plain same-size device copy, in the same graphs
+    floors = None
     if not args.no_sweep:
-        g_floor = capture(floor_step, R)
-        launch_floor = time_graph(g_floor, R, 4 * R, R) / len(SWEEP)
-        g_copy = capture(copy_step, R)
+        tiny = torch.zeros(1, device=dev)
+        src = torch.empty(K_A * N_A, dtype=torch.uint8, device=dev)
+        dst_bufs = [torch.empty_like(src) for _ in range(R)]
+        g_floor = capture(lambda r: tiny.add_(1.0), R)
+        launch_floor = time_graph(g_floor, R, 4 * R, R)
+        g_copy = capture(lambda r: dst_bufs[r].copy_(ws[r].view(-1)), R)
         copy_us = time_graph(g_copy, R, 4 * R, R)
-        del g_floor, g_copy
+        del g_floor, g_copy, dst_bufs
+        floors = {"graph_launch_us_per_tiny_kernel": round(launch_floor, 3), "copy_4MiB_us": round(copy_us, 3),
+                  "copy_4MiB_GBps": round(2 * K_A * N_A / copy_us / 1e3, 1)}
 
-    # ---- prefill point: wq_b-shaped M=8192, K=1024, N=32768 -----------------------------
-    prefill = None
-    if not args.no_prefill:
+    # ---- roofline of the dominant kernel: the one-launch fused kernel ----------------------
+    roofline = None
+    if roof_ms:
+        b_sum = sum(fused_bytes(M) for M in roof_ms)
+        t_sum = sum(us_fused[M] for M in roof_ms)
+        achieved = b_sum / t_sum / 1e3
+        traffic = None
+        if os.path.exists(TRAFFIC_FILE):
+            try:
+                tr = json.load(open(TRAFFIC_FILE))
+                if tr.get("kernel_source_hash") == kernel_source_hash():
+                    traffic = tr.get("hbm_bytes_per_launch_mean")
+            except Exception:
+                traffic = None
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": ROOFLINE_KERNEL, "launches": f"one per fused call at M in {roof_ms} (K=4096, N=1024)",
+                    "bytes_per_launch_mean": round(b_sum / len(roof_ms)),
+                    "us_per_launch_mean": round(t_sum / len(roof_ms), 3),
+                    "us_per_launch": {str(M): round(us_fused[M], 3) for M in roof_ms}}
+
+    rows = {}
+    if not args.no_rows:
+        # ---- prefill GEMM: wq_b-shaped M=8192, K=1024, N=32768 -----------------------------
         Mp, Kp, Np = 8192, 1024, 32768
         xp = torch.from_numpy(syn.wq_b_x(Mp).view(np.int16)).to(dev).view(torch.bfloat16)
         wp_h, swp_h = syn.wq_b_w()
@@ -247,33 +305,82 @@ def main():
         swp = torch.from_numpy(swp_h).to(dev)
         xqp, xsp = wq.wq_dynamic_quant(xp)
         yp = torch.empty((Mp, Np), dtype=torch.bfloat16, device=dev)
-        for i in range(3):
-            wq.wq_quant_matmul(xqp, xsp, wp[i % 2], swp, y=yp)
-        torch.cuda.synchronize()
-        n_it = 10
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(n_it):
-            wq.wq_quant_matmul(xqp, xsp, wp[i % 2], swp, y=yp)
-        b.record()
-        torch.cuda.synchronize()
-        us_p = a.elapsed_time(b) / n_it * 1e3
+        it = iter(range(1 << 30))
+        us_p = time_events(lambda: wq.wq_quant_matmul(xqp, xsp, wp[next(it) % 2], swp, y=yp), 10)
         tops = 2 * Mp * Np * Kp / us_p / 1e6
-        prefill = {"workload": "wq_b wide linear GEMM (x_q given): M=8192, K=1024, N=32768, bf16 out",
-                   "us": round(us_p, 2), "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+        rows["prefill_gemm_m8192"] = {
+            "workload": "wq_b wide linear INT8 GEMM (x_q given): M=8192, K=1024, N=32768, bf16 out",
+            "kernel": "k_gemm_i8_big", "us": round(us_p, 2), "TOPS": round(tops, 1),
+            "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+        # ---- standalone per-token quant at the prefill shape (HBM bound) --------------------
+        us_q = time_in_graph(lambda r: wq.wq_dynamic_quant(xp, x_q=xqp, x_scale=xsp))
+        qb = 2 * Mp * Kp + Mp * Kp + 4 * Mp
+        rows["int8_quant_m8192"] = {"workload": "per-token INT8 quant X bf16 [8192, 1024] (one buffer, reused by every call)", "kernel": "k_dynamic_quant",
+                                    "us": round(us_q, 2), "GBps": round(qb / us_q / 1e3, 1),
+                                    "frac_hbm": round(qb / us_q / 1e3 / HBM_PEAK_GBS, 4)}
         del xp, wp, yp, xqp
 
-    # ---- roofline of the dominant kernel (the fused decode launch), over the sweep -------
-    total_bytes = sum(fused_bytes(M) for M in SWEEP)
-    achieved = total_bytes / us_step / 1e3  # GB/s
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            tr = json.load(open(TRAFFIC_FILE))
-            if tr.get("kernel_source_hash") == kernel_source_hash():
-                traffic = tr.get("bytes_per_step")
-        except Exception:
-            traffic = None
+        # ---- FP8 per-token-group quant (packed UE8M0) and the grouped contraction ----------
+        # 16 rotating copies of the 32 MiB weight and of the activations (>= 512 MiB in all
+        # at T = 512) keep each call's inputs out of L2 and the Infinity Cache
+        G8, D8, N8, R8 = 8, 4096, 1024, 16
+        wq8_h, ws8_h = syn.fp8_weights(42, G=G8, N=N8, D=D8)
+        wq8 = [torch.from_numpy(wq8_h).to(dev) for _ in range(R8)]
+        ws8 = torch.from_numpy(ws8_h).to(dev)
+        fp8 = {}
+        for T in (1, 64, 512):
+            x8h = torch.from_numpy(syn.fp8_group_x(T, G=G8, D=D8).view(np.int16)).to(dev).view(torch.bfloat16)
+            x8 = [x8h.clone() for _ in range(R8)]
+            _, PH, TA = wq.packed_scale_dims(T, D8)
+            q8 = [torch.empty((T, G8, D8), dtype=torch.uint8, device=dev) for _ in range(R8)]
+            st8 = [torch.empty((G8, PH, TA), dtype=torch.int32, device=dev) for _ in range(R8)]
+            us_gq = time_in_graph(lambda r: wq.wq_group_quant_fp8_ue8m0(x8[r], x_q=q8[r], storage=st8[r]), R8)
+            y8 = torch.empty((T, G8, N8), dtype=torch.bfloat16, device=dev)
+            us_c = time_in_graph(lambda r: wq.wq_quant_matmul(q8[r], st8[r], wq8[r], ws8, y=y8, fp8_groups=G8), R8)
+            del x8, q8, st8
+            gq_bytes = 2 * T * G8 * D8 + T * G8 * D8 + 4 * G8 * PH * TA
+            c_bytes = T * G8 * D8 + 4 * G8 * PH * TA + G8 * N8 * D8 + 4 * G8 * (N8 // 128) * (D8 // 128) + 2 * T * G8 * N8
+            c_ops = 2 * T * G8 * N8 * D8
+            fp8[str(T)] = {"group_quant_us": round(us_gq, 3), "group_quant_GBps": round(gq_bytes / us_gq / 1e3, 1),
+                           "contraction_us": round(us_c, 3), "contraction_GBps": round(c_bytes / us_c / 1e3, 1),
+                           "contraction_frac_hbm": round(c_bytes / us_c / 1e3 / HBM_PEAK_GBS, 4),
+                           "contraction_TOPS": round(c_ops / us_c / 1e6, 2)}
+        rows["fp8_wo_a"] = {"workload": "X bf16 [T, 8, 4096] -> E4M3 + packed UE8M0 [8, 8, align4(T)]; "
+                                        "out[T,g,:] = x_q[T,g,:] W_g^T, W_g E4M3 [1024, 4096], 128x128 pow2 scales",
+                            "kernels": "k_group_quant_fp8, k_gemm_tile<FP8>", "by_T": fp8}
+        del wq8
+
+        # ---- MoE block: T=256, hidden 4096, 256 experts of 2x2048, top-8 Zipf(1.1) ----------
+        T, H, I, E, topk = 256, 4096, 2048, 256, 8
+        d = syn.moe_inputs(seed=51, T=T, H=H, I=I, E=E, TOPK=topk, weights=False)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(5151)
+        w13 = torch.randint(-127, 128, (E, 2 * I, H), generator=gen, device=dev, dtype=torch.int8)
+        w2 = torch.randint(-127, 128, (E, H, I), generator=gen, device=dev, dtype=torch.int8)
+        sw13 = torch.rand((E, 2 * I), generator=gen, device=dev) * 9e-3 + 1e-3
+        sw2 = torch.rand((E, H), generator=gen, device=dev) * 9e-3 + 1e-3
+        ids = torch.from_numpy(d["ids"]).to(dev)
+        h = torch.from_numpy(d["h"].view(np.int16)).to(dev).view(torch.bfloat16)
+        gamma = torch.from_numpy(d["gamma"].view(np.int16)).to(dev).view(torch.bfloat16)
+
+        def moe_block():
+            perm, row_token, offsets = wq.wq_moe_sort(ids, E)
+            q1, s1 = wq.wq_dynamic_quant(h, rms_gamma=gamma, row_index=row_token)
+            hmid = wq.wq_quant_matmul(q1, s1, w13, sw13, seg_offsets=offsets, epilogue=wq.WQ_EPI_SWIGLU_F32)
+            q2, s2 = wq.wq_dynamic_quant(hmid)
+            return wq.wq_quant_matmul(q2, s2, w2, sw2, seg_offsets=offsets)
+
+        us_moe = time_events(moe_block, 5, warm=2)
+        counts = np.bincount(d["ids"].reshape(-1), minlength=E)
+        active = int((counts > 0).sum())
+        wbytes = active * (2 * I * H + I * H) + active * 4 * (2 * I + H)
+        rows["moe_block"] = {
+            "workload": "T=256, hidden 4096, E=256 experts (W13 4096->2x2048, W2 2048->4096 int8), top-8 Zipf(1.1): "
+                        "sort, RMSNorm+quant+gather, gate/up segmented GEMM + SwiGLU, requant, down segmented GEMM",
+            "kernels": "k_moe_sort, k_dynamic_quant x2, k_gemm_seg<2>, k_gemm_seg<1>", "active_experts": active,
+            "us": round(us_moe, 1), "weight_bytes": wbytes, "weight_GBps": round(wbytes / us_moe / 1e3, 1),
+            "frac_hbm": round(wbytes / us_moe / 1e3 / HBM_PEAK_GBS, 4)}
+        del w13, w2
 
     out = {
         "metric": "W8A8 linear us & % HBM roofline at M=1..64 (K4096,N1024); int8 TOPS at M=8192",
@@ -291,14 +398,10 @@ def main():
         "config": {"workload": "wq_a decode linear, fused quant+GEMM: X bf16 [M,4096] x W int8 [4096->1024], "
                                "M in 1,2,4,7,8,16,32,64",
                    "K": K_A, "N": N_A, "M_sweep": list(SWEEP), "rotating_copies": R},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "k_decode<MT,NT,FUSED,A_LDS> (wq_fused_quant_matmul; M > 8 adds k_dynamic_quant)",
-                     "bytes_per_step": total_bytes, "us_per_step_events": round(us_step, 3)},
+        "roofline": roofline,
         "sweep": sweep,
-        "prefill_m8192": prefill,
-        "floors": {"graph_launch_us_per_tiny_kernel": round(launch_floor, 3),
-                   "copy_4MiB_us": round(copy_us, 3), "copy_4MiB_GBps": round(2 * K_A * N_A / copy_us / 1e3, 1)},
+        "floors": floors,
+        "rows": rows,
         "timed_wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -68,6 +68,7 @@ EXPORTS = {
                                              _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "wq_moe_sort": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                    _c_void_p]),
+    "wq_fused_path": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64]),
 }
 
 _LIB = None
@@ -172,16 +173,22 @@ def packed_scale_dims(T: int, D: int):
     return HG, (HG + 3) // 4, (T + 3) // 4 * 4
 
 
-def wq_group_quant_fp8_ue8m0(x: torch.Tensor):
+def wq_group_quant_fp8_ue8m0(x: torch.Tensor, x_q: torch.Tensor | None = None, storage: torch.Tensor | None = None):
     """x bf16 [T, G, D] contiguous -> (x_q uint8 [T, G, D] E4M3FN codes,
-    x_s int32 logical view [T, G, PH] with strides (1, PH*TA, TA), storage [G, PH, TA])."""
+    x_s int32 logical view [T, G, PH] with strides (1, PH*TA, TA), storage [G, PH, TA]).
+    x_q / storage may be passed in (contiguous, those shapes) instead of allocated."""
     if x.dim() != 3 or not x.is_contiguous() or x.dtype != torch.bfloat16:
         raise ValueError("x must be a contiguous bf16 [T, G, D] tensor")
     T, G, D = x.shape
     _, PH, TA = packed_scale_dims(T, D)
     ctx = context(x.device)
-    x_q = torch.empty((T, G, D), dtype=torch.uint8, device=x.device)
-    storage = torch.empty((G, PH, TA), dtype=torch.int32, device=x.device)
+    if x_q is None:
+        x_q = torch.empty((T, G, D), dtype=torch.uint8, device=x.device)
+    if storage is None:
+        storage = torch.empty((G, PH, TA), dtype=torch.int32, device=x.device)
+    if tuple(x_q.shape) != (T, G, D) or not x_q.is_contiguous() or tuple(storage.shape) != (G, PH, TA) \
+            or not storage.is_contiguous() or storage.dtype != torch.int32:
+        raise ValueError("x_q must be uint8 [T, G, D] and storage int32 [G, PH, TA], both contiguous")
     if x.numel() > 0:
         st = lib().wq_group_quant_fp8_ue8m0(ctx.handle, _ptr(x), T, G, D, _ptr(x_q), _ptr(storage),
                                             _stream(x.device))
@@ -244,6 +251,18 @@ def wq_fused_quant_matmul(x, w, w_scale, *, y=None, x_q_out=None, x_scale_out=No
                                      _stream(x.device))
     _check("wq_fused_quant_matmul", st)
     return y
+
+
+FUSED_PATHS = {0: "quant kernel + GEMM (two launches)", 1: "one launch: dot4 GEMV", 2: "one launch: 8-wave MFMA"}
+
+
+def wq_fused_path(M: int, K: int, N: int, device=None) -> int:
+    """Launch sequence wq_fused_quant_matmul takes for these sizes (see FUSED_PATHS)."""
+    ctx = context(device or torch.device("cuda", torch.cuda.current_device()))
+    r = lib().wq_fused_path(ctx.handle, M, K, N)
+    if r < 0:
+        _check("wq_fused_path", -r)
+    return r
 
 
 def wq_moe_sort(ids: torch.Tensor, num_experts: int):

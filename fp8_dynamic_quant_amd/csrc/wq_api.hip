@@ -363,6 +363,21 @@ int wq_quant_matmul(wq_ctx* c, const wq_matmul_desc* d, void* stream) {
   return WQ_ERR_SHAPE;
 }
 
+namespace {
+// the launch sequence of the fused call (valid sizes, M >= 1): see wq_fused_path
+int fused_path(const wq_ctx* c, int64_t M, int64_t K) {
+  if (M <= c->fused_gemv_max_m && wq::gemv_fits((int)M, (int)K, true) && c->decode_nt == 0) return 1;
+  if (M <= c->fused_max_m && wq::fused_decode_fits((int)M, (int)K)) return 2;
+  return 0;
+}
+}  // namespace
+
+int wq_fused_path(const wq_ctx* c, int64_t M, int64_t K, int64_t N) {
+  if (!c) return -WQ_ERR_NULL;
+  if (M < 1 || K <= 0 || N <= 0 || K % 16 != 0 || N % 16 != 0 || K > 131072) return -WQ_ERR_SHAPE;
+  return fused_path(c, M, K);
+}
+
 int wq_fused_quant_matmul(wq_ctx* c, const void* x, int64_t M, int64_t K, int64_t ldx, const int8_t* w,
                           const float* w_scale, int64_t N, void* y, int64_t ldy, int8_t* x_q_out,
                           float* x_scale_out, int32_t* acc_out, void* stream) {
@@ -376,8 +391,9 @@ int wq_fused_quant_matmul(wq_ctx* c, const void* x, int64_t M, int64_t K, int64_
     return WQ_ERR_ALIGN;
   DeviceGuard g(c->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool one_launch_gemv = M <= c->fused_gemv_max_m && wq::gemv_fits((int)M, (int)K, true) && c->decode_nt == 0;
-  const bool one_launch_mfma = M <= c->fused_max_m && !one_launch_gemv && wq::fused_decode_fits((int)M, (int)K);
+  const int path = fused_path(c, M, K);
+  const bool one_launch_gemv = path == 1;
+  const bool one_launch_mfma = path == 2;
   if (!one_launch_gemv && !one_launch_mfma) {
     // quantise, then the GEMM (two launches); the INT8 payload goes through the
     // caller's buffers when given, else through the context workspace

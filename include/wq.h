@@ -179,6 +179,13 @@ int wq_fused_quant_matmul(wq_ctx* ctx, const void* x, int64_t M, int64_t K, int6
                           const int8_t* w, const float* w_scale, int64_t N, void* y, int64_t ldy,
                           int8_t* x_q_out, float* x_scale_out, int32_t* acc_out, void* stream);
 
+/* Which launch sequence wq_fused_quant_matmul takes for these sizes on this context:
+ * 0 = the quant kernel, then the GEMM (two launches); 1 = one launch of the dot4 GEMV
+ * kernel; 2 = one launch of the 8-wave MFMA kernel.  A negative value is -status for
+ * invalid sizes (M < 1, or K, N as wq_fused_quant_matmul requires).  Host only: no
+ * device work. */
+int wq_fused_path(const wq_ctx* ctx, int64_t M, int64_t K, int64_t N);
+
 /* ---- expert sort (MoE) ---------------------------------------------------------------
  * "DeepSeek V4 950" section 3.2: sort the (token, slot) pairs by expert id before the
  * gather so each expert's rows are contiguous.  topk_ids: int32 [T, topk], values in
