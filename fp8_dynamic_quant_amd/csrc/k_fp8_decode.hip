@@ -1,0 +1,126 @@
+// Grouped FP8 contraction for decode-sized token counts (T <= 64): weight streaming.
+//
+// Operation: the SGLang PR #34277 summary (功能与动机, 实现拆解): the grouped FP8 einsum
+// that consumes the activation scales exactly as the group quant writes them, packed 4
+// UE8M0 bytes per int32 in [G, ceil(HG/4), align4(T)]:
+//   out[t, g, n] = bf16( sum_kb 2^(ea(t,g,kb)) * ws[g, n/128, kb] * sum_{k in kb} q[t,g,k] w[g,n,k] )
+// with 128-wide K blocks, E4M3 payloads and f32 accumulation.
+//
+// At T <= 64 the 32 MiB of FP8 weights bound the run (a 128 x 128 output tile would put
+// only G * N / 128 = 64 workgroups on the chip).  So each workgroup owns 16 output columns
+// of one group and the whole K range, G * N / 16 = 512 workgroups for the DeepSeek shape:
+//  * four waves split K; each wave loads its weights (32 bytes per lane per 128-deep step)
+//    straight into registers in the v_mfma_scale_f32_16x16x128_f8f6f4 B layout, all before
+//    the first wait;
+//  * a 128-deep step is exactly one scale block, so the block scales ride in the MFMA's
+//    E8M0 scale operands: the activation byte is read from the packed storage as written,
+//    the weight byte is the exponent field of the f32 power-of-two block scale;
+//  * tokens go in tiles of 16 rows; the four waves' f32 16 x 16 tiles are summed in LDS in
+//    a fixed order and written as bf16.
+#include "wq_device.h"
+#include "wq_kernels.h"
+
+namespace wq {
+
+namespace {
+constexpr int kF8NT = 16;       // output columns per workgroup
+constexpr int kF8Waves = 4;
+constexpr int kF8MaxSteps = 8;  // 128-deep K steps per wave: K <= 4096
+constexpr int kF8MaxRT = 4;     // 16-token row tiles: T <= 64
+}  // namespace
+
+__global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
+  __shared__ float red[kF8Waves][kF8MaxRT][4][64];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int T = p.M, N = p.N, K = p.K, g = blockIdx.y;
+  const int n0 = blockIdx.x * kF8NT;
+  const int KT = K >> 7;                 // 128-deep blocks
+  const int steps = KT / kF8Waves;       // per wave
+  const int kb0 = wv * steps;
+  const int cl = lane & 15, kq = lane >> 4;  // column (B) / row (A) in the tile; 32-byte quarter of the step
+  const int n = n0 + cl;
+
+  // ---- weights and their block-scale exponents, all issued first ---------------------------
+  const int8_t* W = p.w + (int64_t)g * p.w_batch_stride + (int64_t)n * K + kq * 32;
+  v8i b[kF8MaxSteps];
+#pragma unroll
+  for (int j = 0; j < kF8MaxSteps; ++j) {
+    if (j < steps) {
+      const v4i lo = *reinterpret_cast<const v4i*>(W + (int64_t)(kb0 + j) * 128);
+      const v4i hi = *reinterpret_cast<const v4i*>(W + (int64_t)(kb0 + j) * 128 + 16);
+      b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      b[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  const float* wsc = p.w_scale + ((int64_t)g * (N >> 7) + (n0 >> 7)) * KT + kb0;
+  int sb[kF8MaxSteps];
+#pragma unroll
+  for (int j = 0; j < kF8MaxSteps; ++j) sb[j] = j < steps ? (int)((__float_as_uint(wsc[j]) >> 23) & 0xFF) : 127;
+
+  // ---- token tiles --------------------------------------------------------------------------
+  const int PH = (KT + 3) >> 2;
+  const int32_t* xs_g = p.a_scale_packed + (int64_t)g * PH * p.a_scale_tokens;
+  const int8_t* A = p.a + (int64_t)g * p.a_batch_stride + kq * 32;
+  const int RT = (T + 15) >> 4;
+  v4f acc[kF8MaxRT];
+#pragma unroll
+  for (int rt = 0; rt < kF8MaxRT; ++rt) acc[rt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int rt = 0; rt < kF8MaxRT; ++rt) {
+    if (rt < RT) {  // uniform
+      // rows past T read row T-1: they only feed output rows that are not stored
+      const int row = min(rt * 16 + cl, T - 1);
+      const int8_t* arow = A + (int64_t)row * p.lda;
+      v8i a[kF8MaxSteps];
+#pragma unroll
+      for (int j = 0; j < kF8MaxSteps; ++j) {
+        if (j < steps) {
+          const v4i lo = *reinterpret_cast<const v4i*>(arow + (int64_t)(kb0 + j) * 128);
+          const v4i hi = *reinterpret_cast<const v4i*>(arow + (int64_t)(kb0 + j) * 128 + 16);
+          a[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kF8MaxSteps; ++j) {
+        if (j < steps) {
+          const int kb = kb0 + j;
+          const int32_t w = xs_g[(int64_t)(kb >> 2) * p.a_scale_tokens + row];
+          const int sa = (w >> (8 * (kb & 3))) & 0xFF;
+          acc[rt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[j], b[j], acc[rt], 0, 0, 0, sa, 0, sb[j]);
+        }
+      }
+    }
+  }
+
+  // ---- the four waves' partial sums, in a fixed order, then bf16 ----------------------------
+#pragma unroll
+  for (int rt = 0; rt < kF8MaxRT; ++rt)
+    if (rt < RT)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wv][rt][i][lane] = acc[rt][i];
+  __syncthreads();
+  uint16_t* Y = reinterpret_cast<uint16_t*>(p.y) + (int64_t)g * p.y_batch_stride;
+  for (int e = t; e < RT * 4 * 64; e += 256) {
+    const int ln = e & 63, ri = e >> 6, rt = ri >> 2, i = ri & 3;
+    const int row = rt * 16 + 4 * (ln >> 4) + i;  // MFMA 16x16 output: col = lane % 16, row = 4 (lane / 16) + i
+    if (row < T) {
+      const float v = __fadd_rn(__fadd_rn(__fadd_rn(red[0][rt][i][ln], red[1][rt][i][ln]), red[2][rt][i][ln]),
+                                red[3][rt][i][ln]);
+      Y[(int64_t)row * p.ldy + n0 + (ln & 15)] = (uint16_t)f32_to_bf16_rn(v);
+    }
+  }
+}
+
+bool fp8_decode_fits(int T, int N, int K) {
+  return T >= 1 && T <= 16 * kF8MaxRT && N % kF8NT == 0 && K % (128 * kF8Waves) == 0 &&
+         K / (128 * kF8Waves) <= kF8MaxSteps;
+}
+
+hipError_t launch_fp8_decode(const TileArgs& a, hipStream_t st) {
+  if (!fp8_decode_fits(a.M, a.N, a.K)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_fp8_decode, dim3((unsigned)(a.N / kF8NT), (unsigned)a.batch), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace wq

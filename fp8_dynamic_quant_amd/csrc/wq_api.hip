@@ -342,6 +342,14 @@ static int fp8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   t.ldy = d->ldy;
   t.y_batch_stride = d->y_batch_stride;
   t.batch = (int)G;
+  if (wq::fp8_decode_fits((int)M, (int)N, (int)K)) {
+    // decode-sized token counts: weight streaming, 16 columns x whole K per workgroup
+    hipError_t e = wq::launch_fp8_decode(t, st);
+    if (c->log)
+      std::fprintf(stderr, "[wq] quant_matmul fp8 decode M=%lld N=%lld K=%lld groups=%lld grid=%lldx%lld\n",
+                   (long long)M, (long long)N, (long long)K, (long long)G, (long long)(N / 16), (long long)G);
+    return status_of(e);
+  }
   hipError_t e = wq::launch_gemm_tile(t, true, st);
   if (c->log)
     std::fprintf(stderr, "[wq] quant_matmul fp8 tile128-lds-dma M=%lld N=%lld K=%lld groups=%lld grid=%lld\n",

@@ -70,6 +70,11 @@ constexpr int kSegMaxPairs = 4096;
 hipError_t launch_gemm_i8_big(const TileArgs& a, int num_cu, hipStream_t st);
 bool big_fits(int M, int N, int K, int64_t lda, int64_t ldy);
 
+// FP8 grouped contraction for T <= 64, K % 512 == 0, K <= 4096 (k_fp8_decode.hip):
+// 16 output columns of one group per workgroup, grid (N / 16, G)
+hipError_t launch_fp8_decode(const TileArgs& a, hipStream_t st);
+bool fp8_decode_fits(int T, int N, int K);
+
 // FP8 group quant with packed UE8M0 scales (k_fp8.hip).
 hipError_t launch_group_quant_fp8(const uint16_t* x, int64_t T, int G, int D, uint8_t* xq, int32_t* xs,
                                   hipStream_t st);

@@ -139,7 +139,8 @@ def test_fp8_contraction_dsv4_wo_a(T):
     _check_contraction(payload, storage, eb, wq_codes, ws, y)
 
 
-@pytest.mark.parametrize("T,G,D,N", [(3, 3, 384, 128), (130, 2, 256, 256), (9, 1, 1152, 384)])
+@pytest.mark.parametrize("T,G,D,N", [(3, 3, 384, 128), (130, 2, 256, 256), (9, 1, 1152, 384),
+                                     (5, 2, 512, 128), (17, 1, 4096, 1024), (64, 3, 2048, 256)])
 def test_fp8_contraction_small_shapes_wide_codes(T, G, D, N):
     x = syn.fp8_group_x(T, G=G, D=D, layout_variant=True)
     payload, storage, eb = fg.group_quant_fp8_packed(x)
