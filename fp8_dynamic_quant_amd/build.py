@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libwq.so")
 
-SOURCES = ["wq_api.hip", "k_quant.hip", "k_decode.hip", "k_fused.hip", "k_gemm_i8.hip", "k_gemm_tile.hip", "k_gemm_big.hip", "k_fp8.hip", "k_fp8_decode.hip", "k_moe.hip"]
+SOURCES = ["wq_api.hip", "k_quant.hip", "k_decode.hip", "k_fused.hip", "k_gemm_i8.hip", "k_gemm_tile.hip", "k_gemm_big.hip", "k_fp8.hip", "k_fp8_decode.hip", "k_moe.hip", "k_seg_decode.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

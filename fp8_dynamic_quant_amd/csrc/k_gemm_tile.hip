@@ -263,7 +263,8 @@ __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
       int64_t lo = 0;
       if (e < p.batch) {
         lo = p.seg_offsets[e];
-        cnt = (int)((p.seg_offsets[e + 1] - lo + kBM - 1) / kBM);
+        const int64_t rows = p.seg_offsets[e + 1] - lo;
+        cnt = rows >= p.seg_min_rows ? (int)((rows + kBM - 1) / kBM) : 0;
       }
       int incl = cnt;
 #pragma unroll

@@ -33,6 +33,7 @@ struct wq_ctx {
   // Every workgroup then quantises all M rows itself (no workgroup may wait for another),
   // ~0.3 us per row, while a second launch costs a fixed ~6 us; above the limit the call
   // runs the quant kernel and then the GEMM.
+  int seg_small;         // expert segments: small experts on the streaming kernel (WQ_SEG_SMALL=0 turns off)
   int fused_max_m;       // largest M the one-launch fused kernel takes (WQ_FUSED_MAX_M)
   int fused_gemv_max_m;  // largest M the fused GEMV takes instead (WQ_FUSED_GEMV_MAX_M)
 };
@@ -157,6 +158,8 @@ int wq_ctx_create(int device, void* workspace, size_t workspace_bytes, wq_ctx** 
   const char* fm = std::getenv("WQ_FUSED_MAX_M");
   c->fused_max_m = fm ? std::atoi(fm) : 16;
   if (c->fused_max_m < 0 || c->fused_max_m > 64) c->fused_max_m = 16;
+  const char* ss = std::getenv("WQ_SEG_SMALL");
+  c->seg_small = ss ? std::atoi(ss) != 0 : 1;
   const char* gm = std::getenv("WQ_FUSED_GEMV_MAX_M");
   c->fused_gemv_max_m = gm ? std::atoi(gm) : 2;
   if (c->fused_gemv_max_m < 0 || c->fused_gemv_max_m > 4) c->fused_gemv_max_m = 2;
@@ -248,11 +251,19 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
     t.ldy = d->ldy;
     t.seg_offsets = d->seg_offsets;
     t.batch = (int)d->batch;
+    // experts with few rows stream their weights through the 16-column kernel; the tiled
+    // kernel takes the rest (both read the offsets on the device and skip the other set)
+    const bool small = c->seg_small && wq::seg_decode_fits((int)N, (int)K, d->epilogue, d->batch);
+    t.seg_min_rows = small ? wq::kSegSmallRows + 1 : 0;
+    if (small) {
+      hipError_t e = wq::launch_seg_decode(t, c->num_cu, st);
+      if (e != hipSuccess) return status_of(e);
+    }
     hipError_t e = wq::launch_gemm_tile(t, false, st);
     if (c->log)
-      std::fprintf(stderr, "[wq] quant_matmul int8 segments E=%lld rows=%lld N=%lld K=%lld epilogue=%s persistent grid=%d\n",
-                   (long long)d->batch, (long long)M, (long long)N, (long long)K,
-                   d->epilogue == WQ_EPI_SWIGLU_F32 ? "swiglu-f32" : "bf16", 2 * c->num_cu);
+      std::fprintf(stderr, "[wq] quant_matmul int8 segments E=%lld rows=%lld N=%lld K=%lld epilogue=%s persistent grid=%d "
+                   "small-expert kernel=%s\n", (long long)d->batch, (long long)M, (long long)N, (long long)K,
+                   d->epilogue == WQ_EPI_SWIGLU_F32 ? "swiglu-f32" : "bf16", 2 * c->num_cu, small ? "yes" : "no");
     return status_of(e);
   }
   if (d->epilogue != WQ_EPI_BF16) return WQ_ERR_UNSUPPORTED;

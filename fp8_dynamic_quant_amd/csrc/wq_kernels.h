@@ -59,6 +59,7 @@ struct TileArgs {
   const int32_t* a_scale_packed;  // FP8: packed UE8M0 storage [batch, PH, TA]
   int64_t a_scale_tokens;      // FP8: TA
   int64_t y_batch_stride;      // strided groups: elements between groups of y
+  int seg_min_rows;            // segments: experts with fewer rows are left to another kernel
 };
 hipError_t launch_gemm_i8_tile(const TileArgs& a, hipStream_t st);
 // 128x128 tiles with DMA-fed LDS (k_gemm_tile.hip); K % 128 == 0
@@ -66,6 +67,11 @@ hipError_t launch_gemm_tile(const TileArgs& a, bool fp8, hipStream_t st);
 bool tile_fits(int K);
 // (expert, 128-row tile) pairs the segmented kernel can hold
 constexpr int kSegMaxPairs = 4096;
+// Segments: experts with at most this many rows go to the weight-streaming kernel
+// (k_seg_decode.hip), the rest to the tiled one
+constexpr int kSegSmallRows = 16;
+hipError_t launch_seg_decode(const TileArgs& a, int num_cu, hipStream_t st);
+bool seg_decode_fits(int N, int K, int epilogue, int64_t batch);
 // persistent 256x256 INT8 tiles for large M (k_gemm_big.hip)
 hipError_t launch_gemm_i8_big(const TileArgs& a, int num_cu, hipStream_t st);
 bool big_fits(int M, int N, int K, int64_t lda, int64_t ldy);
