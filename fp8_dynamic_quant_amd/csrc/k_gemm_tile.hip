@@ -10,10 +10,11 @@
 //
 // Tile: 128 x 128 outputs per workgroup, 128-byte K slices, four waves in a 2 x 2 grid of
 // 64 x 64 wave tiles (2 x 2 MFMA tiles of 32 x 32).  Operand slices move global -> LDS with
-// global_load_lds_dwordx4 (no VGPR staging) into two LDS stages, so the next slice is in
-// flight while the current one feeds the MFMAs.  Rows of a slice are 128 bytes = 8
-// chunks of 16 bytes, stored XOR-swizzled by (row & 7) to spread the MFMA operand reads
-// over the LDS banks.
+// global_load_lds_dwordx4 (no VGPR staging) into a ring of LDS stages (4, or 3 with the
+// SwiGLU pair of B tiles), so several slices are in flight while one feeds the MFMAs.  Rows
+// of a slice are 128 bytes = 8 chunks of 16 bytes, XOR-swizzled by bits 1..3 of the row so
+// the MFMA operand reads hit distinct banks.  FP8 slices carry their 128 rows' packed scale
+// words in the same stage.
 //  * INT8: v_mfma_i32_32x32x32_i8, 4 per slice per tile; exact int32 accumulation; the
 //    epilogue computes bf16((f32(acc) * s_m) * sw_n).
 //  * FP8: v_mfma_scale_f32_32x32x64_f8f6f4, 2 per slice per tile.  A 128-byte K slice is
@@ -36,12 +37,32 @@ namespace wq {
 
 constexpr int kBM = 128, kBN = 128, kBK = 128;
 constexpr int kSlice = kBM * kBK;  // bytes of one operand slice in LDS
+constexpr int kScaleB = 1024;      // FP8: the slice's packed activation-scale words (4 waves x 256 B)
+// LDS ring: STAGES - 1 slices in flight while one is multiplied (bytes per stage: A + B
+// [+ B2] [+ scales]).  Dense tiles use 4 stages (128 KiB); the persistent segment kernels
+// keep 32 KiB of static LDS for their work list, so they use 3 stages, or 2 with the
+// SwiGLU pair of B tiles (48 KiB per stage).
+template <bool FP8, bool DUAL, int STAGES>
+struct TileRing {
+  static constexpr int kStageB = (DUAL ? 3 : 2) * kSlice + (FP8 ? kScaleB : 0);
+  static constexpr int kStages = STAGES;
+  static constexpr int kDmaPerSlice = (DUAL ? 12 : 8) + (FP8 ? 1 : 0);  // per wave
+  static constexpr int kBytes = kStages * kStageB;
+  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+};
+constexpr int kDenseStages = 4;
+template <int EPI>
+constexpr int seg_stages() { return EPI == 2 ? 2 : 3; }
 constexpr int kGroupM = 8;         // tile rows per group in the L2-friendly tile order
 constexpr int kMaxSegTiles = kSegMaxPairs;  // (expert, row tile) pairs a persistent workgroup lists
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ int tswz(int r, int c) { return r * kBK + ((c ^ (r & 7)) << 4); }
+// A 128-byte row covers half of the 64 LDS banks, so rows r and r+2 share banks: the
+// chunk is XORed with bits 1..3 of the row, and the 16 rows a ds_read_b128 pass reads at
+// one logical chunk then land on distinct banks.
+__device__ __forceinline__ int tswz_of(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int tswz(int r, int c) { return r * kBK + ((c ^ tswz_of(r)) << 4); }
 
 // DMA one 128-row x 128-byte slice: rows [r0, r0+128) of `src` (row stride ld bytes,
 // clamped to < rows), bytes [k0, k0+128); lands swizzled at `dst`
@@ -51,7 +72,7 @@ __device__ __forceinline__ void dma_slice(const int8_t* src, int64_t ld, int r0,
   for (int i = 0; i < 4; ++i) {
     const int pos = (wv * 4 + i) * 64 + lane;  // 16-byte position in the slice, 0..1023
     const int r = pos >> 3, pc = pos & 7;
-    const int c = pc ^ (r & 7);
+    const int c = pc ^ tswz_of(r);
     int gr = r0 + r;
     gr = gr < rows ? gr : rows - 1;
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + (int64_t)gr * ld + k0 + c * 16),
@@ -64,15 +85,15 @@ using acc_t = typename std::conditional<FP8, v16f, v16i>::type;
 
 // One 128 x 128 tile (two B tiles when DUAL): acc[i][j] (and acc2) over all K.
 // a: rows [m0, row_hi) clamped; b: columns [n0, ..) of w (row stride K), b2 at n0 + dual_off.
-template <bool FP8, bool DUAL>
+template <bool FP8, bool DUAL, int STAGES>
 __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, const int8_t* A, int m0, int row_hi,
                                               const int8_t* B, int n0, int dual_off, int g, acc_t<FP8> (&acc)[2][2],
                                               acc_t<FP8> (&acc2)[2][2]) {
+  using Ring = TileRing<FP8, DUAL, STAGES>;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int wm = wv >> 1, wn = wv & 1;
   const int K = p.K, N = p.N;
   const int KT = K / kBK;
-  constexpr int kStage = (DUAL ? 3 : 2) * kSlice;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -82,46 +103,58 @@ __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, c
         acc[i][j][e] = 0;
         acc2[i][j][e] = 0;
       }
-  int srow[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = m0 + wm * 64 + i * 32 + (lane & 31);
-    srow[i] = r < row_hi ? r : row_hi - 1;
-  }
   const int PH = (KT + 3) >> 2;
   const int32_t* xs_g = FP8 ? p.a_scale_packed + (int64_t)g * PH * p.a_scale_tokens : nullptr;
+  const float* ws_g = FP8 ? p.w_scale + ((int64_t)g * (N / 128) + (n0 >> 7)) * KT : nullptr;
+
+  // issue slice kt into its ring stage: A, B (, B2) and, for FP8, the 128 rows' packed
+  // scale words (wave w: rows m0 + 32w .. +31, one 4-byte word per lane 0..31) and the
+  // slice's weight block scale (lane 32; lanes 33..63 repeat row words into the unused
+  // rest of the wave's 256 bytes).  Staging the scales with the operands keeps every load
+  // of the loop an LDS DMA, so the ring's vmcnt waits count exactly these.
+  auto issue = [&](int kt) {
+    int8_t* st = smem + (kt % Ring::kStages) * Ring::kStageB;
+    dma_slice(A, p.lda, m0, row_hi, kt * kBK, st, wv, lane);
+    dma_slice(B, K, n0, N, kt * kBK, st + kSlice, wv, lane);
+    if constexpr (DUAL) dma_slice(B, K, n0 + dual_off, N, kt * kBK, st + 2 * kSlice, wv, lane);
+    if constexpr (FP8) {
+      const int r = min(m0 + wv * 32 + (lane & 31), row_hi - 1);
+      const void* src = lane == 32 ? reinterpret_cast<const void*>(ws_g + kt)
+                                   : reinterpret_cast<const void*>(xs_g + (int64_t)(kt >> 2) * p.a_scale_tokens + r);
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(st + (DUAL ? 3 : 2) * kSlice + wv * 256), 4, 0, 0);
+    }
+  };
 
   __syncthreads();  // the previous tile's LDS reads are done before the new DMA lands
-  dma_slice(A, p.lda, m0, row_hi, 0, smem, wv, lane);
-  dma_slice(B, K, n0, N, 0, smem + kSlice, wv, lane);
-  if constexpr (DUAL) dma_slice(B, K, n0 + dual_off, N, 0, smem + 2 * kSlice, wv, lane);
+  for (int kt = 0; kt < Ring::kStages - 1 && kt < KT; ++kt) issue(kt);
 
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    int8_t* sa = smem + cur * kStage;
+    // this wave's DMA of slice kt has landed once at most the later issued slices'
+    // instructions are outstanding (loads complete in order)
+    const int later = min(Ring::kStages - 2, KT - 1 - kt);
+    if (later >= 2) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * Ring::kDmaPerSlice) : "memory");
+    } else if (later == 1) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Ring::kDmaPerSlice) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();  // slice kt is in LDS for everyone; the stage of slice kt-1 is free
+    if (kt + Ring::kStages - 1 < KT) issue(kt + Ring::kStages - 1);
+    int8_t* sa = smem + (kt % Ring::kStages) * Ring::kStageB;
     int8_t* sb = sa + kSlice;
     int8_t* sb2 = sa + 2 * kSlice;
-    int sca[2] = {127, 127}, scb = 127;
-    if constexpr (FP8) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int32_t w = xs_g[(int64_t)(kt >> 2) * p.a_scale_tokens + srow[i]];
-        sca[i] = (w >> (8 * (kt & 3))) & 0xFF;
-      }
-      const float wsf = p.w_scale[((int64_t)g * (N / 128) + (n0 >> 7)) * KT + kt];
-      scb = (__float_as_uint(wsf) >> 23) & 0xFF;
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // slice kt is in LDS for everyone; the other stage is free
-    if (kt + 1 < KT) {
-      int8_t* na = smem + (cur ^ 1) * kStage;
-      dma_slice(A, p.lda, m0, row_hi, (kt + 1) * kBK, na, wv, lane);
-      dma_slice(B, K, n0, N, (kt + 1) * kBK, na + kSlice, wv, lane);
-      if constexpr (DUAL) dma_slice(B, K, n0 + dual_off, N, (kt + 1) * kBK, na + 2 * kSlice, wv, lane);
-    }
     const int ar = wm * 64 + (lane & 31), br = wn * 64 + (lane & 31);
     const int kh = lane >> 5;  // which half of the K step this lane carries
     if constexpr (FP8) {
+      const int32_t* scw = reinterpret_cast<const int32_t*>(sa + 2 * kSlice);
+      int sca[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = ar + i * 32;  // row in the tile; its word sits at (r / 32) * 64 + r % 32
+        sca[i] = (scw[(r >> 5) * 64 + (r & 31)] >> (8 * (kt & 3))) & 0xFF;
+      }
+      const int scb = (scw[32] >> 23) & 0xFF;  // exponent field of the f32 power-of-two block scale
       // two K=64 MFMAs per slice; a lane carries 32 bytes = chunks 4*ks + 2*kh, +1
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -242,7 +275,7 @@ __global__ __launch_bounds__(256) void k_gemm_tile(TileArgs p, int tiles_m, int 
   const int tm = gm0 + in % gsz, tn = in / gsz;
   const int m0 = tm * kBM, n0 = tn * kBN;
   acc_t<FP8> acc[2][2], acc2[2][2];
-  tile_mainloop<FP8, false>(p, smem, A, m0, p.M, B, n0, 0, g, acc, acc2);
+  tile_mainloop<FP8, false, kDenseStages>(p, smem, A, m0, p.M, B, n0, 0, g, acc, acc2);
   tile_epilogue<FP8, 1>(p, m0, p.M, n0, g, FP8 ? nullptr : p.w_scale + (int64_t)g * p.N, acc, acc2);
 }
 
@@ -296,7 +329,7 @@ __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
     const float* wsc = p.w_scale + (int64_t)e * p.N;
     acc_t<false> acc[2][2], acc2[2][2];
     const int n0 = tn * kBN;
-    tile_mainloop<false, EPI == 2>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, 0, acc, acc2);
+    tile_mainloop<false, EPI == 2, seg_stages<EPI>()>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, 0, acc, acc2);
     tile_epilogue<false, EPI>(p, m0, row_hi, n0, 0, wsc, acc, acc2);
   }
 }
@@ -310,7 +343,8 @@ hipError_t launch_gemm_tile(const TileArgs& a, bool fp8, hipStream_t st) {
     if (fp8) return hipErrorInvalidValue;
     if (a.epilogue == 2 && (a.N % 256) != 0) return hipErrorInvalidValue;
     const int dual = a.epilogue == 2;
-    const size_t lds = (size_t)2 * (dual ? 3 : 2) * kSlice;
+    const size_t lds = dual ? (size_t)TileRing<false, true, seg_stages<2>()>::kBytes
+                            : (size_t)TileRing<false, false, seg_stages<1>()>::kBytes;
     auto kfn = dual ? k_gemm_seg<2> : k_gemm_seg<1>;
     static bool attr[2] = {false, false};
     if (!attr[dual]) {
@@ -328,11 +362,17 @@ hipError_t launch_gemm_tile(const TileArgs& a, bool fp8, hipStream_t st) {
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int nt = tiles_m * tiles_n;
   dim3 grid((unsigned)(((nt + 7) / 8) * 8), (unsigned)a.batch), block(256);
-  const size_t lds = 2 * (size_t)2 * kSlice;
-  if (fp8)
-    hipLaunchKernelGGL((k_gemm_tile<true>), grid, block, lds, st, a, tiles_m, tiles_n);
-  else
-    hipLaunchKernelGGL((k_gemm_tile<false>), grid, block, lds, st, a, tiles_m, tiles_n);
+  const size_t lds = fp8 ? (size_t)TileRing<true, false, kDenseStages>::kBytes
+                          : (size_t)TileRing<false, false, kDenseStages>::kBytes;
+  auto kfn = fp8 ? k_gemm_tile<true> : k_gemm_tile<false>;
+  static bool attr[2] = {false, false};
+  if (!attr[fp8]) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    attr[fp8] = true;
+  }
+  hipLaunchKernelGGL(kfn, grid, block, lds, st, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
