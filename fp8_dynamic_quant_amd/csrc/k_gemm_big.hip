@@ -40,6 +40,8 @@ static_assert(kBKb == 64 || kBKb == 128, "slice width");
 static_assert(kStages >= 2 && kStages <= 4 && kStages * kStageB <= 160 * 1024, "LDS ring");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_b;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Chunk swizzle: kRowsPerBankRow consecutive rows fill the 64 banks once, so the rows that
 // land on the same banks (r, r + kRowsPerBankRow, ...) get different chunk positions; 16
@@ -195,6 +197,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
           const int n = n0 + wn * 64 + j * 32 + (lane & 31);
           const float sw = swv[j];
           const int nbase = n - (odd ? 1 : 0);  // the even column of the pair
+          // this lane's first output row (r0 for even lanes, r0 + 1 for odd) and its stride
+          // of two rows: the 8 stores below are at fixed multiples of the stride
+          uint16_t* rowp = reinterpret_cast<uint16_t*>(p.y) + (int64_t)(mrow + (odd ? 1 : 0)) * p.ldy + nbase;
+          const int64_t ld2 = 2 * p.ldy;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             // registers e = 4q + 0..3 hold rows mrow + 8q + 0..3 of column n
@@ -204,23 +210,26 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
               const int r0 = mrow + 8 * q + 2 * hp;
               const float s0 = rs[e0];
               const float s1 = rs[e0 + 1];
-              const uint32_t v0 = f32_to_bf16_rn(__fmul_rn(__fmul_rn((float)acc[i][j][e0], s0), sw));
-              const uint32_t v1 = f32_to_bf16_rn(__fmul_rn(__fmul_rn((float)acc[i][j][e0 + 1], s1), sw));
+              const float f0 = __fmul_rn(__fmul_rn((float)acc[i][j][e0], s0), sw);
+              const float f1 = __fmul_rn(__fmul_rn((float)acc[i][j][e0 + 1], s1), sw);
               // even lane keeps row r0 and takes its neighbour's (r0, n+1); odd lane keeps
-              // row r1 and takes its neighbour's (r1, n-1)
-              const uint32_t give = odd ? v0 : v1;
-              const uint32_t got = (uint32_t)__shfl_xor((int)give, 1, 64);
-              const uint32_t word = odd ? (got | (v1 << 16)) : (v0 | (got << 16));
+              // row r1 and takes its neighbour's (r1, n-1): a quad-permute DPP move swaps
+              // lanes 2k and 2k+1 without the LDS crossbar
+              const float give = odd ? f0 : f1;
+              const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(give), 0xB1, 0xF, 0xF, false));
+              // two f32 -> one word of two bf16, round to nearest even (v_cvt_pk_bf16_f32)
+              const f32x2 pair = odd ? f32x2{got, f1} : f32x2{f0, got};
+              const uint32_t word = __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, bf16x2));
               const int row = odd ? r0 + 1 : r0;
               if (row < M && nbase < N) {
-                uint16_t* dst = reinterpret_cast<uint16_t*>(p.y) + (int64_t)row * p.ldy + nbase;
+                uint16_t* dst = rowp + (4 * q + hp) * ld2;
                 // streaming store: the output is not read again here, and keeping it out of
                 // the L2's reuse set leaves room for the A and B tiles (measured ~15% faster)
                 __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(dst));  // N even: nbase + 1 < N
               }
               if (p.acc_out) {  // raw accumulators, same pairing
                 const int a0 = acc[i][j][e0], a1 = acc[i][j][e0 + 1];
-                const int ag = __shfl_xor(odd ? a0 : a1, 1, 64);
+                const int ag = __builtin_amdgcn_mov_dpp(odd ? a0 : a1, 0xB1, 0xF, 0xF, false);
                 if (row < M && nbase < N) {
                   int2 pr = odd ? int2{ag, a1} : int2{a0, ag};
                   *reinterpret_cast<int2*>(p.acc_out + (int64_t)row * N + nbase) = pr;

@@ -91,6 +91,32 @@ def test_wq_b_wide(M):
     _check_linear(x, w, sw, fused=False)
 
 
+def _bf16_rne_bits(f32):
+    u = np.ascontiguousarray(f32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("M,K,N", [(2, 4096, 1024), (8, 4096, 1024), (70, 1024, 48), (300, 1024, 528), (512, 1024, 32768)])
+def test_epilogue_is_the_documented_f32_sequence(M, K, N):
+    """Stricter than the 1-ulp bound: the bf16 output equals bf16_RN(RN(RN(f32(acc) * s_m) * sw_n))
+    bit for bit, the f32 operation sequence the kernels document (f32(acc) rounds to nearest
+    even too), here emulated with numpy float32 arithmetic on the oracle's exact accumulators."""
+    x = syn.activations((99, M, K), M, K, outlier_frac=0.01, outlier_mul=20.0)
+    w, sw = syn.int8_weights((100, N, K), N, K)
+    q, s = il.quant_int8_per_token(x)
+    acc = il.gemm_int8_int32(q, w)
+    want = _bf16_rne_bits((acc.astype(np.float32) * s[:, None]).astype(np.float32) * sw[None, :].astype(np.float32))
+    for fused in (False, True):
+        if fused:
+            y = wq.wq_fused_quant_matmul(bf16_dev(x), dev(w), dev(sw))
+        else:
+            xq, xs = wq.wq_dynamic_quant(bf16_dev(x))
+            y = wq.wq_quant_matmul(xq, xs, dev(w), dev(sw))
+        torch.cuda.synchronize()
+        got = host_bf16_bits(y)
+        assert np.array_equal(got, want), f"fused={fused}: {(got != want).sum()} outputs differ"
+
+
 def test_wq_b_prefill_8192_sampled_rows():
     M = 8192
     x = syn.wq_b_x(M)
