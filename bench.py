@@ -40,7 +40,7 @@ K_A, N_A = 4096, 1024
 ROTATE_BYTES = 512 << 20
 ROOFLINE_KERNEL = "k_fused_decode"  # the one-launch fused kernel (wq_fused_path == 2)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_fused_decode_wq_a.json")
-KERNEL_SOURCES = ("k_fused.hip", "wq_device.h", "wq_api.hip", "wq_kernels.h")
+KERNEL_SOURCES = ("k_fused.hip", "wq_device.h", "wq_kernels.h")  # the roofline kernel and the headers it includes
 
 
 def fused_bytes(M, K=K_A, N=N_A):

@@ -114,3 +114,37 @@ def test_moe_block_full_size_sampled_experts():
         assert_same(f"q2[e={e}]", host(g["q2"][lo:hi]), q2)
         y = il.epilogue_bf16(il.gemm_int8_int32(q2, host(w2[e])), s2, host(sw2[e]))
         assert nm.bf16_ulp_distance(host_bf16_bits(g["y"][lo:hi]), y).max() <= 1
+
+
+@pytest.mark.parametrize("epi", ["bf16", "swiglu"])
+def test_segments_across_the_small_expert_boundary(epi):
+    """Expert row counts on both sides of the 16-row split between the weight-streaming
+    kernel and the tiled one (0, 1, 15, 16, 17, 31, 32, 33, 129 rows), K = 1024 so both
+    kernels take part; every expert's rows against the oracle's dense per-expert product."""
+    counts = np.array([0, 1, 15, 16, 17, 31, 32, 33, 129], np.int64)
+    E, K, N = counts.size, 1024, 512
+    M = int(counts.sum())
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    x = syn.activations((62, M, K), M, K, outlier_frac=0.01, outlier_mul=20.0)
+    q, s = il.quant_int8_per_token(x)
+    w = np.empty((E, N, K), np.int8)
+    sw = np.empty((E, N), np.float32)
+    for e in range(E):
+        w[e], sw[e] = syn.int8_weights((63, e), N, K)
+    if epi == "bf16":
+        y = wq.wq_quant_matmul(dev(q), dev(s), dev(w), dev(sw), seg_offsets=dev(offsets))
+    else:
+        y = wq.wq_quant_matmul(dev(q), dev(s), dev(w), dev(sw), seg_offsets=dev(offsets), epilogue=wq.WQ_EPI_SWIGLU_F32)
+    torch.cuda.synchronize()
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if lo == hi:
+            continue
+        acc = il.gemm_int8_int32(q[lo:hi], w[e])
+        if epi == "bf16":
+            ref = il.epilogue_bf16(acc, s[lo:hi], sw[e])
+            d = nm.bf16_ulp_distance(host_bf16_bits(y[lo:hi]), ref)
+            assert d.max() <= 1, f"expert {e} ({hi - lo} rows): max ulp {d.max()}"
+        else:
+            ref = moe.silu_mul_f32(acc, s[lo:hi], np.broadcast_to(sw[e], (hi - lo, N)))
+            assert_same(f"h[expert {e}, {hi - lo} rows]", host(y[lo:hi]), ref)
