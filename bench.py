@@ -347,7 +347,7 @@ def main():
                            "contraction_TOPS": round(c_ops / us_c / 1e6, 2)}
         rows["fp8_wo_a"] = {"workload": "X bf16 [T, 8, 4096] -> E4M3 + packed UE8M0 [8, 8, align4(T)]; "
                                         "out[T,g,:] = x_q[T,g,:] W_g^T, W_g E4M3 [1024, 4096], 128x128 pow2 scales",
-                            "kernels": "k_group_quant_fp8, k_gemm_tile<FP8>", "by_T": fp8}
+                            "kernels": "k_group_quant_fp8; k_fp8_decode (T <= 64), k_gemm_tile<FP8> (T > 64)", "by_T": fp8}
         del wq8
 
         # ---- MoE block: T=256, hidden 4096, 256 experts of 2x2048, top-8 Zipf(1.1) ----------
@@ -377,7 +377,8 @@ def main():
         rows["moe_block"] = {
             "workload": "T=256, hidden 4096, E=256 experts (W13 4096->2x2048, W2 2048->4096 int8), top-8 Zipf(1.1): "
                         "sort, RMSNorm+quant+gather, gate/up segmented GEMM + SwiGLU, requant, down segmented GEMM",
-            "kernels": "k_moe_sort, k_dynamic_quant x2, k_gemm_seg<2>, k_gemm_seg<1>", "active_experts": active,
+            "kernels": "k_moe_sort, k_dynamic_quant x2, k_seg_decode<2> + k_gemm_seg<2> (gate/up), k_seg_decode<1> + k_gemm_seg<1> (down)",
+            "active_experts": active,
             "us": round(us_moe, 1), "weight_bytes": wbytes, "weight_GBps": round(wbytes / us_moe / 1e3, 1),
             "frac_hbm": round(wbytes / us_moe / 1e3 / HBM_PEAK_GBS, 4)}
         del w13, w2
