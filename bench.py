@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="skip the prefill / FP8 / MoE measurements")
     ap.add_argument("--no-sweep", action="store_true", help="skip the standalone sweep and the floors")
     ap.add_argument("--traffic-probe", action="store_true", help="only the roofline kernel's launches, for counters")
+    ap.add_argument("--prefill-probe", action="store_true",
+                    help="only two launches of the M=8192 prefill GEMM on random operands, for counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the kernels run on one MI355X and the "
@@ -197,6 +199,20 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / n
+
+    if args.prefill_probe:
+        g = torch.Generator(device="cpu").manual_seed(0)
+        Mp, Kp, Np = 8192, 1024, 32768
+        a = torch.randint(-127, 128, (Mp, Kp), dtype=torch.int8, generator=g).to(dev)
+        s = (torch.rand(Mp, generator=g) * 0.01).to(dev)
+        w = torch.randint(-127, 128, (Np, Kp), dtype=torch.int8, generator=g).to(dev)
+        sw = (torch.rand(Np, generator=g) * 0.01).to(dev)
+        y = torch.empty((Mp, Np), dtype=torch.bfloat16, device=dev)
+        for _ in range(2):
+            wq.wq_quant_matmul(a, s, w, sw, y=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"prefill_probe": {"M": Mp, "K": Kp, "N": Np, "launches": 2}}))
+        return
 
     if args.traffic_probe:
         # eager launches of the roofline kernel, each on a cold weight copy, then one copy
