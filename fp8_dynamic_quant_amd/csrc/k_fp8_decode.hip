@@ -29,7 +29,7 @@ constexpr int kF8MaxSteps = 8;  // 128-deep K steps per wave: K <= 4096
 constexpr int kF8MaxRT = 4;     // 16-token row tiles: T <= 64
 }  // namespace
 
-__global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
+__global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p, int rt_per_wg) {
   __shared__ float red[kF8Waves][kF8MaxRT][4][64];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int T = p.M, N = p.N, K = p.K, g = blockIdx.y;
@@ -62,7 +62,10 @@ __global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
   const int PH = (KT + 3) >> 2;
   const int32_t* xs_g = p.a_scale_packed + (int64_t)g * PH * p.a_scale_tokens;
   const int8_t* A = p.a + (int64_t)g * p.a_batch_stride + kq * 32;
-  const int RT = (T + 15) >> 4;
+  // this workgroup's token tiles: [rt_lo, rt_hi) of the 16-token tiles (grid z splits them)
+  const int rt_lo = blockIdx.z * rt_per_wg;
+  const int rt_hi = min((T + 15) >> 4, rt_lo + rt_per_wg);
+  const int RT = rt_hi - rt_lo;
   v4f acc[kF8MaxRT];
 #pragma unroll
   for (int rt = 0; rt < kF8MaxRT; ++rt) acc[rt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
   for (int rt = 0; rt < kF8MaxRT; ++rt) {
     if (rt < RT) {  // uniform
       // rows past T read row T-1: they only feed output rows that are not stored
-      const int row = min(rt * 16 + cl, T - 1);
+      const int row = min((rt_lo + rt) * 16 + cl, T - 1);
       const int8_t* arow = A + (int64_t)row * p.lda;
       v8i a[kF8MaxSteps];
 #pragma unroll
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
   uint16_t* Y = reinterpret_cast<uint16_t*>(p.y) + (int64_t)g * p.y_batch_stride;
   for (int e = t; e < RT * 4 * 64; e += 256) {
     const int ln = e & 63, ri = e >> 6, rt = ri >> 2, i = ri & 3;
-    const int row = rt * 16 + 4 * (ln >> 4) + i;  // MFMA 16x16 output: col = lane % 16, row = 4 (lane / 16) + i
+    const int row = (rt_lo + rt) * 16 + 4 * (ln >> 4) + i;  // MFMA 16x16 output: col = lane % 16, row = 4 (lane / 16) + i
     if (row < T) {
       const float v = __fadd_rn(__fadd_rn(__fadd_rn(red[0][rt][i][ln], red[1][rt][i][ln]), red[2][rt][i][ln]),
                                 red[3][rt][i][ln]);
@@ -117,9 +120,11 @@ bool fp8_decode_fits(int T, int N, int K) {
          K / (128 * kF8Waves) <= kF8MaxSteps;
 }
 
-hipError_t launch_fp8_decode(const TileArgs& a, hipStream_t st) {
-  if (!fp8_decode_fits(a.M, a.N, a.K)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_fp8_decode, dim3((unsigned)(a.N / kF8NT), (unsigned)a.batch), dim3(256), 0, st, a);
+hipError_t launch_fp8_decode(const TileArgs& a, int rt_per_wg, hipStream_t st) {
+  if (!fp8_decode_fits(a.M, a.N, a.K) || rt_per_wg < 1 || rt_per_wg > kF8MaxRT) return hipErrorInvalidValue;
+  const int rt = (a.M + 15) / 16;
+  const dim3 grid((unsigned)(a.N / kF8NT), (unsigned)a.batch, (unsigned)((rt + rt_per_wg - 1) / rt_per_wg));
+  hipLaunchKernelGGL(k_fp8_decode, grid, dim3(256), 0, st, a, rt_per_wg);
   return hipGetLastError();
 }
 

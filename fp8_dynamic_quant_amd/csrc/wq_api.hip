@@ -34,6 +34,7 @@ struct wq_ctx {
   // ~0.3 us per row, while a second launch costs a fixed ~6 us; above the limit the call
   // runs the quant kernel and then the GEMM.
   int seg_small;         // expert segments: small experts on the streaming kernel (WQ_SEG_SMALL=0 turns off)
+  int fp8_rt;            // FP8 decode: 16-token tiles per workgroup (WQ_FP8_RT, 1..4; 0 = automatic)
   int fused_max_m;       // largest M the one-launch fused kernel takes (WQ_FUSED_MAX_M)
   int fused_gemv_max_m;  // largest M the fused GEMV takes instead (WQ_FUSED_GEMV_MAX_M)
 };
@@ -158,6 +159,9 @@ int wq_ctx_create(int device, void* workspace, size_t workspace_bytes, wq_ctx** 
   const char* fm = std::getenv("WQ_FUSED_MAX_M");
   c->fused_max_m = fm ? std::atoi(fm) : 16;
   if (c->fused_max_m < 0 || c->fused_max_m > 64) c->fused_max_m = 16;
+  const char* fr = std::getenv("WQ_FP8_RT");
+  c->fp8_rt = fr ? std::atoi(fr) : 0;
+  if (c->fp8_rt < 0 || c->fp8_rt > 4) c->fp8_rt = 0;
   const char* ss = std::getenv("WQ_SEG_SMALL");
   c->seg_small = ss ? std::atoi(ss) != 0 : 1;
   const char* gm = std::getenv("WQ_FUSED_GEMV_MAX_M");
@@ -355,7 +359,9 @@ static int fp8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   t.batch = (int)G;
   if (wq::fp8_decode_fits((int)M, (int)N, (int)K)) {
     // decode-sized token counts: weight streaming, 16 columns x whole K per workgroup
-    hipError_t e = wq::launch_fp8_decode(t, st);
+    // all token tiles in one workgroup: splitting them over more workgroups re-reads the
+    // weights (measured at T = 64: 29.5 us whole, 34.4 us in halves, 43.3 us in quarters)
+    hipError_t e = wq::launch_fp8_decode(t, c->fp8_rt > 0 ? c->fp8_rt : 4, st);
     if (c->log)
       std::fprintf(stderr, "[wq] quant_matmul fp8 decode M=%lld N=%lld K=%lld groups=%lld grid=%lldx%lld\n",
                    (long long)M, (long long)N, (long long)K, (long long)G, (long long)(N / 16), (long long)G);
