@@ -76,7 +76,17 @@ size_t wq_workspace_bytes(void);
  *   WQ_FORCE_SPLIT=n  the K-split factor of the quant kernel (tests use it to show every
  *                     split gives the same bytes);
  *   WQ_DECODE_NT=n    columns per workgroup of the decode GEMM (4, 8 or 16; 0 = auto);
- *   WQ_FUSED_MAX_M=m  the largest M wq_fused_quant_matmul runs as one launch (default 4). */
+ *   WQ_DECODE_MT=t    16-row tiles per workgroup of the decode GEMM (1, 2 or 4; 0 = auto);
+ *   WQ_FUSED_MAX_M=m  the largest M wq_fused_quant_matmul runs as one launch (0..64,
+ *                     default 16; 0 = always two launches);
+ *   WQ_FUSED_GEMV_MAX_M=m  up to this M (0..4, default 2) that one launch is the dot4
+ *                     GEMV kernel, above it the 8-wave MFMA kernel;
+ *   WQ_SEG_SMALL=0    expert segments: run every expert on the tiled kernel instead of
+ *                     sending the experts with at most 16 rows to the streaming kernel;
+ *   WQ_FP8_RT=r       grouped FP8 contraction at T <= 64: 16-token tiles per workgroup
+ *                     (1..4; 0 = auto, all of them).
+ * Values out of range fall back to the default.  Every setting gives bit-identical
+ * results; the knobs exist for tests and measurement. */
 int wq_ctx_create(int device, void* workspace, size_t workspace_bytes, wq_ctx** out);
 void wq_ctx_destroy(wq_ctx* ctx);
 
@@ -169,7 +179,7 @@ int wq_quant_matmul(wq_ctx* ctx, const wq_matmul_desc* desc, void* stream);
  * The whole chain of section 一 of the W8A8 article: per-token quant of the bf16 x [M, K]
  * (row stride ldx), the INT8 GEMM against w [N, K] and the bf16 epilogue.  Outputs are
  * bit-identical to wq_dynamic_quant followed by wq_quant_matmul.  y: bf16 [M, N] row
- * stride ldy.  For M up to the one-launch limit (WQ_FUSED_MAX_M, default 4) one kernel
+ * stride ldy.  For M up to the one-launch limit (WQ_FUSED_MAX_M, default 16) one kernel
  * quantises in registers and never writes the INT8 payload to HBM; above it the call runs
  * the quant and the GEMM as two launches, staging the payload in x_q_out / x_scale_out
  * when given, else in the context workspace (WQ_ERR_WORKSPACE if M*K bytes exceed it).
