@@ -59,6 +59,7 @@ EXPORTS = {
     "wq_ctx_create": (ctypes.c_int, [ctypes.c_int, _c_void_p, ctypes.c_size_t, ctypes.POINTER(_c_void_p)]),
     "wq_ctx_destroy": (None, [_c_void_p]),
     "wq_ctx_set_split": (ctypes.c_int, [_c_void_p, ctypes.c_int]),
+    "wq_ctx_set_fused_shape": (ctypes.c_int, [_c_void_p, ctypes.c_int, ctypes.c_int]),
     "wq_dynamic_quant": (ctypes.c_int, [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64, _i64, _c_void_p,
                                         ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "wq_group_quant_fp8_ue8m0": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p,
@@ -116,6 +117,12 @@ _CTX: dict[int, Context] = {}
 def set_split(device, n: int) -> None:
     """Force the K-split factor of later calls on `device` (0 = automatic)."""
     _check("wq_ctx_set_split", lib().wq_ctx_set_split(context(device).handle, int(n)))
+
+
+def set_fused_shape(device, rows_per_wg: int, cols_per_wg: int) -> None:
+    """Force the one-launch fused kernel's rows and columns per workgroup on `device` (0 = automatic)."""
+    _check("wq_ctx_set_fused_shape",
+           lib().wq_ctx_set_fused_shape(context(device).handle, int(rows_per_wg), int(cols_per_wg)))
 
 
 def context(device) -> Context:

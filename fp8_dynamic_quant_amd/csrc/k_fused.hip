@@ -4,25 +4,30 @@
 // Operation: "DeepSeek-V4 W8A8 性能分析", section 一 (BF16 X -> per-token dynamic quant ->
 // INT8 GEMM -> BF16 Y, and the fused form that skips the standalone quant launch and the
 // HBM round trip of the INT8 payload); section 三 (small M: the weight stream bounds the
-// run, so the launch shape follows N, not M).
+// run, and the tiling follows the real M and N).
 //
 // Why this shape on MI355X: the 4 MiB weight of a 4096 x 1024 linear streams in ~0.5 us,
 // a dependent second launch costs several us, and a cross-workgroup handoff (fence + flag)
-// costs more than that.  So each workgroup quantises the few activation rows itself, from
-// L2, while its slice of the weights is still in flight from HBM:
-//  * 512 threads = 8 waves per workgroup, NT output columns per workgroup (N / NT
-//    workgroups, e.g. 256 for N = 1024), and wave w owns K range [w K/8, (w+1) K/8);
-//  * every global load is issued up front: first the wave's activation chunks (one 16-byte
-//    chunk of 8 bf16 per lane per row, so the rows are waited on first), then its weights
-//    straight into registers in the v_mfma_i32_16x16x64_i8 B layout;
-//  * rows go in groups of 16 (one MFMA row tile): the per-row absmax is reduced inside the
-//    wave with DPP (no LDS round trips) and across the 8 waves through LDS, then each lane
-//    quantises its own 8 values per row (quant8: one exactness check per 8 values) into the
-//    wave's private, XOR-swizzled LDS tile, which feeds the MFMA A operand;
-//  * the 8 waves' int32 16 x 16 tiles are summed exactly in LDS and the epilogue writes
+// costs more than that.  So no workgroup waits on another: each one quantises the rows it
+// needs itself, from L2, while its slice of the weights is in flight from HBM.
+//  * The grid is (column slices of nt columns) x (row tiles of R rows).  Quantising costs
+//    ~90 VALU instructions per 8 values per wave, so a workgroup that quantised all M rows
+//    would spend most of the call on VALU work every other workgroup repeats; a row tile
+//    of R rows bounds that, and the R-row tiles of one column slice run on one XCD
+//    (workgroups are dispatched to the 8 XCDs round robin), whose L2 then fetches the
+//    slice's weights from HBM once for all of them.
+//  * 512 threads = 8 waves, wave w owns K range [w K/8, (w+1) K/8).  Every global load is
+//    issued up front: the wave's chunk of each of its rows (16 bytes of 8 bf16 per lane),
+//    then its weights straight into registers in the v_mfma_i32_16x16x64_i8 B layout
+//    (CT = nt / 16 column tiles, or one partly used tile for nt < 16).
+//  * The per-row absmax is reduced inside the wave with DPP and across the 8 waves through
+//    LDS; each lane quantises its 8 values per row into the wave's private XOR-swizzled
+//    LDS tile (the MFMA A operand).  Only the fast path (multiply by RN(1/s), one
+//    near-tie check per 8 values) is inline; the rare chunks that fail it, and rows whose
+//    scale is zero or not normal, go through one rolled loop with the exact quant_i8, so
+//    the unrolled code stays small.
+//  * The 8 waves' int32 16 x 16 tiles are summed exactly in LDS and the epilogue writes
 //    bf16((f32(acc) * s_m) * sw_n).
-// Every workgroup quantises all M rows (M K values); at M <= 16 that costs less VALU time
-// than the weight stream takes to arrive.
 #include "wq_device.h"
 #include "wq_kernels.h"
 
@@ -33,9 +38,6 @@ namespace {
 constexpr int kFW = 8;            // waves per workgroup
 constexpr int kFMaxKW = 512;      // K per wave: one 8-value chunk per lane per row
 constexpr int kFMaxSteps = kFMaxKW / 64;
-constexpr int kFMaxGroups = 4;    // 16-row groups: M <= 64
-
-typedef __attribute__((address_space(3))) void* lds_ptr_f;
 
 // byte offset of 16-byte chunk c of row r (r < 16) in a tile of rows of `rowb` bytes;
 // chunks XOR-swizzled by the row within aligned groups of g chunks so the MFMA A reads
@@ -69,142 +71,216 @@ __device__ __forceinline__ uint32_t bf16x8_absmax_bits(const uint4 u) {
   return max((uint32_t)e.x, (uint32_t)e.y);
 }
 
+// INT8 codes of 8 bf16 values by the fast path of quant_i8 (multiply by inv = RN(1/s));
+// *ok is false when a value lies near a rounding tie (the codes are then not used)
+__device__ __forceinline__ uint2 quant8_bf16_fast(const uint4 u, float inv, bool* ok) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  float v[8], r[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  *ok = quant_fast<8>(v, inv, r);
+  return uint2{pack4_rounded(r[0], r[1], r[2], r[3]), pack4_rounded(r[4], r[5], r[6], r[7])};
+}
+
+// INT8 codes of 8 bf16 values by the exact quant_i8 (correctly rounded division)
+__device__ __forceinline__ uint2 quant8_bf16_exact(const uint4 u, float s) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  int c[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[2 * i] = quant_i8(__uint_as_float(w[i] << 16), s);
+    c[2 * i + 1] = quant_i8(__uint_as_float(w[i] & 0xFFFF0000u), s);
+  }
+  return uint2{pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7])};
+}
+
 }  // namespace
 
-__global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt) {
+template <int R, int CT>
+__global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int slices, int rtiles) {
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int M = p.M, N = p.N, K = p.K;
   const int KW = K / kFW;           // this wave's K range (a multiple of 64, <= 512)
   const int steps = KW >> 6;
   const int kbase = wv * KW;
-  const int n0 = blockIdx.x * nt;
+
+  // block -> (column slice, row tile): with slices % 8 == 0, XCD x (blocks b with b % 8 == x)
+  // gets slices [x S/8, (x+1) S/8) with all their row tiles
+  int slice, rt;
+  if ((slices & 7) == 0) {
+    const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+    slice = x * (slices >> 3) + i / rtiles;
+    rt = i - (i / rtiles) * rtiles;
+  } else {
+    slice = blockIdx.x / rtiles;
+    rt = blockIdx.x - slice * rtiles;
+  }
+  const int n0 = slice * nt, row0 = rt * R;
+  const int rows = min(R, M - row0);  // >= 1
   const int cl = lane & 15, kg = lane >> 4;
-  const int col = n0 + cl;
-  const bool bvalid = cl < nt && col < N;
-  const int G = (M + 15) >> 4;
   const bool xlane = lane * 8 < KW;  // this lane holds a chunk of every row
 
-  // LDS: [8 wave tiles of 16 x KW][red 8 x G x 4 x 64 ints][wmax G x 16 x 8][s_lds 64][wsc 16]
-  int8_t* tile = smem + wv * 16 * KW;
-  int* red = reinterpret_cast<int*>(smem + kFW * 16 * KW);
-  uint32_t* wmax = reinterpret_cast<uint32_t*>(red + kFW * kFMaxGroups * 4 * 64);
-  float* s_lds = reinterpret_cast<float*>(wmax + kFMaxGroups * 16 * kFW);
-  float* wsc_lds = s_lds + 64;
+  // LDS: [8 wave tiles of R x KW][red 8 x CT x 4 x 64 ints][wmax R x 8][s_lds R][wsc nt]
+  int8_t* tile = smem + wv * R * KW;
+  int* red = reinterpret_cast<int*>(smem + kFW * R * KW);
+  uint32_t* wmax = reinterpret_cast<uint32_t*>(red + kFW * CT * 4 * 64);
+  float* s_lds = reinterpret_cast<float*>(wmax + R * kFW);
+  float* wsc_lds = s_lds + R;
 
-  // ---- loads: this wave's chunks of the first row group, then its weights ----------------
-  uint4 xr[16];
-  auto load_rows = [&](int g) {
+  // ---- loads: this wave's chunk of each row, then its weights ------------------------------
+  uint4 xr[R];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = g * 16 + r;
-      xr[r] = (row < M && xlane) ? *reinterpret_cast<const uint4*>(p.x + (int64_t)row * p.ldx + kbase + lane * 8)
-                                 : uint4{0u, 0u, 0u, 0u};
-    }
-  };
-  load_rows(0);
-  v4i b[kFMaxSteps];
-  const int8_t* wcol = p.w + (int64_t)col * K + kbase + 16 * kg;
+  for (int r = 0; r < R; ++r)
+    xr[r] = (r < rows && xlane) ? *reinterpret_cast<const uint4*>(p.x + (int64_t)(row0 + r) * p.ldx + kbase + lane * 8)
+                                : uint4{0u, 0u, 0u, 0u};
+  v4i b[CT][kFMaxSteps];
 #pragma unroll
-  for (int j = 0; j < kFMaxSteps; ++j)
-    b[j] = (bvalid && j < steps) ? *reinterpret_cast<const v4i*>(wcol + j * 64) : v4i{0, 0, 0, 0};
+  for (int ct = 0; ct < CT; ++ct) {
+    const int c = ct * 16 + cl;
+    const bool bvalid = c < nt && n0 + c < N;
+    const int8_t* wcol = p.w + (int64_t)(n0 + c) * K + kbase + 16 * kg;
+#pragma unroll
+    for (int j = 0; j < kFMaxSteps; ++j)
+      b[ct][j] = (bvalid && j < steps) ? *reinterpret_cast<const v4i*>(wcol + j * 64) : v4i{0, 0, 0, 0};
+  }
   if (t < nt) wsc_lds[t] = (n0 + t < N) ? p.w_scale[n0 + t] : 0.0f;
 
-  v4i acc[kFMaxGroups];
+  // ---- per-row absmax: in-wave DPP reduction, then across waves through LDS ---------------
 #pragma unroll
-  for (int g = 0; g < kFMaxGroups; ++g) acc[g] = v4i{0, 0, 0, 0};
+  for (int r = 0; r < R; ++r) {
+    const uint32_t a = r < rows ? wave_umax(bf16x8_absmax_bits(xr[r])) : 0u;  // uniform
+    if (lane == 0) wmax[r * kFW + wv] = a;
+  }
+  __syncthreads();
+  // lane r < R combines row r's 8 wave maxima and derives s = RN(a/127), inv = RN(1/s)
+  float s_l = 0.0f, inv_l = 0.0f;
+  if (lane < R) {
+    const uint4 q0 = *reinterpret_cast<const uint4*>(wmax + lane * kFW);
+    const uint4 q1 = *reinterpret_cast<const uint4*>(wmax + lane * kFW + 4);
+    const uint32_t a = max(max(max(q0.x, q0.y), max(q0.z, q0.w)), max(max(q1.x, q1.y), max(q1.z, q1.w)));
+    s_l = __fdiv_rn(__uint_as_float(a << 16), 127.0f);
+    inv_l = __fdiv_rn(1.0f, s_l);
+    if (wv == 0) s_lds[lane] = s_l;
+    if (p.xs_out && slice == 0 && wv == 0 && lane < rows) p.xs_out[row0 + lane] = s_l;
+  }
 
+  // ---- quantise this lane's 8 values of each row into the wave's tile ----------------------
+  const bool export_q = p.xq_out != nullptr && slice == 0;
+  uint32_t bad = 0;  // rows whose chunk needs the exact path (bit r)
 #pragma unroll
-  for (int g = 0; g < kFMaxGroups; ++g) {
-    if (g < G) {  // uniform
-      if (g > 0) load_rows(g);
-      // ---- per-row absmax: in-wave DPP reduction, then across waves through LDS ---------
-      uint32_t* wm = wmax + g * 16 * kFW;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t a = (g * 16 + r < M) ? wave_umax(bf16x8_absmax_bits(xr[r])) : 0u;  // uniform
-        if (lane == 0) wm[r * kFW + wv] = a;
-      }
-      __syncthreads();
-      // lane r < 16 combines row r's 8 wave maxima and derives s = RN(a/127), inv = RN(1/s)
-      float s_l = 0.0f, inv_l = 0.0f;
-      if (lane < 16) {
-        const uint4 q0 = *reinterpret_cast<const uint4*>(wm + lane * kFW);
-        const uint4 q1 = *reinterpret_cast<const uint4*>(wm + lane * kFW + 4);
-        const uint32_t a = max(max(max(q0.x, q0.y), max(q0.z, q0.w)), max(max(q1.x, q1.y), max(q1.z, q1.w)));
-        s_l = __fdiv_rn(__uint_as_float(a << 16), 127.0f);
-        inv_l = __fdiv_rn(1.0f, s_l);
-        if (wv == 0) s_lds[g * 16 + lane] = s_l;
-        if (p.xs_out && blockIdx.x == 0 && wv == 0 && g * 16 + lane < M) p.xs_out[g * 16 + lane] = s_l;
-      }
-      // ---- quantise this lane's 8 values of each row into the wave's tile ----------------
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_l), r));
-        const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_l), r));
-        if (xlane) {
-          // rows past M quantise to zero (their accumulator rows are not stored)
-          const uint2 q = (g * 16 + r < M) ? quant8_bf16(xr[r], s, inv) : uint2{0u, 0u};
+  for (int r = 0; r < R; ++r) {
+    if (r < rows) {  // uniform
+      const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_l), r));
+      const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_l), r));
+      if (xlane) {
+        bool ok;
+        const uint2 q = quant8_bf16_fast(xr[r], inv, &ok);
+        if (ok && quant_scale_normal(s)) {
           *reinterpret_cast<uint2*>(tile + fswz(r, lane >> 1, KW) + (lane & 1) * 8) = q;
-          const int row = g * 16 + r;
-          if (p.xq_out && blockIdx.x == 0 && row < M)
-            *reinterpret_cast<uint2*>(p.xq_out + (int64_t)row * K + kbase + lane * 8) = q;
+          if (export_q) *reinterpret_cast<uint2*>(p.xq_out + (int64_t)(row0 + r) * K + kbase + lane * 8) = q;
+        } else {
+          bad |= 1u << r;
         }
       }
-      // ---- MFMA over this wave's K range (the tile is private to the wave) ---------------
+    }
+  }
+  // the exact path, one affected row per iteration (each lane re-reads its chunk from L2)
+  while (__any(bad != 0)) {
+    const int r = bad != 0 ? __builtin_ctz(bad) : 0;
+    const float s = __shfl(s_l, r, 64);
+    if (bad != 0) {
+      const uint4 u = *reinterpret_cast<const uint4*>(p.x + (int64_t)(row0 + r) * p.ldx + kbase + lane * 8);
+      const uint2 q = quant8_bf16_exact(u, s);
+      *reinterpret_cast<uint2*>(tile + fswz(r, lane >> 1, KW) + (lane & 1) * 8) = q;
+      if (export_q) *reinterpret_cast<uint2*>(p.xq_out + (int64_t)(row0 + r) * K + kbase + lane * 8) = q;
+      bad &= bad - 1;
+    }
+  }
+
+  // ---- MFMA over this wave's K range (the tile is private to the wave); MFMA rows past
+  // the tile's rows repeat its last row and are not stored -----------------------------------
+  v4i acc[CT];
 #pragma unroll
-      for (int j = 0; j < kFMaxSteps; ++j) {
-        if (j < steps) {
-          const v4i a = *reinterpret_cast<const v4i*>(tile + fswz(cl, j * 4 + kg, KW));
-          acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acc[g], 0, 0, 0);
-        }
-      }
+  for (int ct = 0; ct < CT; ++ct) acc[ct] = v4i{0, 0, 0, 0};
+  const int ar = min(cl, rows - 1);
+#pragma unroll
+  for (int j = 0; j < kFMaxSteps; ++j) {
+    if (j < steps) {
+      const v4i a = *reinterpret_cast<const v4i*>(tile + fswz(ar, j * 4 + kg, KW));
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[ct][j], acc[ct], 0, 0, 0);
     }
   }
 
   // ---- sum the 8 waves' tiles, epilogue -----------------------------------------------------
 #pragma unroll
-  for (int g = 0; g < kFMaxGroups; ++g)
-    if (g < G)
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[((wv * kFMaxGroups + g) * 4 + i) * 64 + lane] = acc[g][i];
+    for (int i = 0; i < 4; ++i) red[((wv * CT + ct) * 4 + i) * 64 + lane] = acc[ct][i];
   __syncthreads();
-  for (int o = t; o < M * nt; o += kFW * 64) {
-    const int row = o / nt, c = o - row * nt;
+  for (int o = t; o < rows * nt; o += kFW * 64) {
+    const int r = o / nt, c = o - r * nt;
     const int n = n0 + c;
     if (n < N) {
-      const int g = row >> 4, rr = row & 15;
-      const int ln = c + 16 * (rr >> 2), i = rr & 3;  // MFMA 16x16 output: col = lane % 16, row = 4 (lane / 16) + i
+      const int ct = c >> 4;
+      const int ln = (c & 15) + 16 * (r >> 2), i = r & 3;  // MFMA 16x16 output: col = lane % 16, row = 4 (lane / 16) + i
       int v = 0;
 #pragma unroll
-      for (int w = 0; w < kFW; ++w) v += red[((w * kFMaxGroups + g) * 4 + i) * 64 + ln];
-      p.y[(int64_t)row * p.ldy + n] = (uint16_t)f32_to_bf16_rn(__fmul_rn(__fmul_rn((float)v, s_lds[row]), wsc_lds[c]));
-      if (p.acc_out) p.acc_out[(int64_t)row * N + n] = v;
+      for (int w = 0; w < kFW; ++w) v += red[((w * CT + ct) * 4 + i) * 64 + ln];
+      const int64_t m = row0 + r;
+      p.y[m * p.ldy + n] = (uint16_t)f32_to_bf16_rn(__fmul_rn(__fmul_rn((float)v, s_lds[r]), wsc_lds[c]));
+      if (p.acc_out) p.acc_out[m * N + n] = v;
     }
   }
 }
 
-size_t fused_decode_lds_bytes(int K) {
-  return (size_t)kFW * 16 * (K / kFW) + (size_t)kFW * kFMaxGroups * 4 * 64 * 4 + (size_t)kFMaxGroups * 16 * kFW * 4 +
-         64 * 4 + 16 * 4;
+namespace {
+
+size_t fused_lds_bytes(int R, int CT, int K) {
+  return (size_t)kFW * R * (K / kFW) + (size_t)kFW * CT * 4 * 64 * 4 + (size_t)R * kFW * 4 + (size_t)R * 4 + 32 * 4;
 }
 
-bool fused_decode_fits(int M, int K) {
-  return M >= 1 && M <= 16 * kFMaxGroups && K % (kFW * 64) == 0 && K / kFW <= kFMaxKW;
-}
-
-hipError_t launch_fused_decode(const DecodeArgs& a, int nt, hipStream_t st) {
-  if (!fused_decode_fits(a.M, a.K) || a.x == nullptr || !(nt == 4 || nt == 8 || nt == 16)) return hipErrorInvalidValue;
-  const size_t lds = fused_decode_lds_bytes(a.K);
+template <int R, int CT>
+hipError_t launch_fused_rt(const DecodeArgs& a, int nt, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_fused_decode),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_fused_decode<R, CT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL(k_fused_decode, dim3((unsigned)((a.N + nt - 1) / nt)), dim3(kFW * 64), lds, st, a, nt);
+  const int slices = (a.N + nt - 1) / nt, rtiles = (a.M + R - 1) / R;
+  hipLaunchKernelGGL((k_fused_decode<R, CT>), dim3((unsigned)(slices * rtiles)), dim3(kFW * 64),
+                     fused_lds_bytes(R, CT, a.K), st, a, nt, slices, rtiles);
   return hipGetLastError();
+}
+
+template <int R>
+hipError_t launch_fused_r(const DecodeArgs& a, int nt, hipStream_t st) {
+  return nt > 16 ? launch_fused_rt<R, 2>(a, nt, st) : launch_fused_rt<R, 1>(a, nt, st);
+}
+
+}  // namespace
+
+bool fused_decode_fits(int M, int K) {
+  return M >= 1 && M <= 64 && K % (kFW * 64) == 0 && K / kFW <= kFMaxKW;
+}
+
+hipError_t launch_fused_decode(const DecodeArgs& a, int nt, int rows_per_wg, hipStream_t st) {
+  if (!fused_decode_fits(a.M, a.K) || a.x == nullptr || !(nt == 4 || nt == 8 || nt == 16 || nt == 32))
+    return hipErrorInvalidValue;
+  switch (rows_per_wg) {
+    case 1: return launch_fused_r<1>(a, nt, st);
+    case 2: return launch_fused_r<2>(a, nt, st);
+    case 4: return launch_fused_r<4>(a, nt, st);
+    case 8: return launch_fused_r<8>(a, nt, st);
+    case 16: return launch_fused_r<16>(a, nt, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace wq

@@ -11,6 +11,7 @@
 //    64 * ksteps; the slice shrinks (down to 256) until the grid covers every CU with a
 //    distinct piece of W.
 //  * INT8 GEMM, M > 64: 128x128 tiles.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -37,6 +38,8 @@ struct wq_ctx {
   int fp8_rt;            // FP8 decode: 16-token tiles per workgroup (WQ_FP8_RT, 1..4; 0 = automatic)
   int fused_max_m;       // largest M the one-launch fused kernel takes (WQ_FUSED_MAX_M)
   int fused_gemv_max_m;  // largest M the fused GEMV takes instead (WQ_FUSED_GEMV_MAX_M)
+  int fused_r;           // one-launch fused kernel: rows per workgroup (WQ_FUSED_R; 0 = automatic)
+  int fused_nt;          // one-launch fused kernel: columns per workgroup (WQ_FUSED_NT; 0 = automatic)
 };
 
 namespace {
@@ -157,16 +160,24 @@ int wq_ctx_create(int device, void* workspace, size_t workspace_bytes, wq_ctx** 
   c->decode_mt = dm ? std::atoi(dm) : 0;
   if (c->decode_mt != 0 && c->decode_mt != 1 && c->decode_mt != 2 && c->decode_mt != 4) c->decode_mt = 0;
   const char* fm = std::getenv("WQ_FUSED_MAX_M");
-  c->fused_max_m = fm ? std::atoi(fm) : 16;
-  if (c->fused_max_m < 0 || c->fused_max_m > 64) c->fused_max_m = 16;
+  c->fused_max_m = fm ? std::atoi(fm) : 64;
+  if (c->fused_max_m < 0 || c->fused_max_m > 64) c->fused_max_m = 64;
   const char* fr = std::getenv("WQ_FP8_RT");
   c->fp8_rt = fr ? std::atoi(fr) : 0;
   if (c->fp8_rt < 0 || c->fp8_rt > 4) c->fp8_rt = 0;
   const char* ss = std::getenv("WQ_SEG_SMALL");
   c->seg_small = ss ? std::atoi(ss) != 0 : 1;
   const char* gm = std::getenv("WQ_FUSED_GEMV_MAX_M");
-  c->fused_gemv_max_m = gm ? std::atoi(gm) : 2;
-  if (c->fused_gemv_max_m < 0 || c->fused_gemv_max_m > 4) c->fused_gemv_max_m = 2;
+  c->fused_gemv_max_m = gm ? std::atoi(gm) : 0;
+  if (c->fused_gemv_max_m < 0 || c->fused_gemv_max_m > 4) c->fused_gemv_max_m = 0;
+  const char* fr2 = std::getenv("WQ_FUSED_R");
+  c->fused_r = fr2 ? std::atoi(fr2) : 0;
+  if (c->fused_r != 0 && c->fused_r != 1 && c->fused_r != 2 && c->fused_r != 4 && c->fused_r != 8 && c->fused_r != 16)
+    c->fused_r = 0;
+  const char* fn = std::getenv("WQ_FUSED_NT");
+  c->fused_nt = fn ? std::atoi(fn) : 0;
+  if (c->fused_nt != 0 && c->fused_nt != 4 && c->fused_nt != 8 && c->fused_nt != 16 && c->fused_nt != 32)
+    c->fused_nt = 0;
   *out = c;
   return WQ_OK;
 }
@@ -177,6 +188,17 @@ int wq_ctx_set_split(wq_ctx* c, int n) {
   if (!c) return WQ_ERR_NULL;
   if (n < 0) return WQ_ERR_SHAPE;
   c->force_split = n;
+  return WQ_OK;
+}
+
+int wq_ctx_set_fused_shape(wq_ctx* c, int rows_per_wg, int cols_per_wg) {
+  if (!c) return WQ_ERR_NULL;
+  const bool r_ok = rows_per_wg == 0 || rows_per_wg == 1 || rows_per_wg == 2 || rows_per_wg == 4 ||
+                    rows_per_wg == 8 || rows_per_wg == 16;
+  const bool n_ok = cols_per_wg == 0 || cols_per_wg == 4 || cols_per_wg == 8 || cols_per_wg == 16 || cols_per_wg == 32;
+  if (!r_ok || !n_ok) return WQ_ERR_SHAPE;
+  c->fused_r = rows_per_wg;
+  c->fused_nt = cols_per_wg;
   return WQ_OK;
 }
 
@@ -389,10 +411,37 @@ int wq_quant_matmul(wq_ctx* c, const wq_matmul_desc* d, void* stream) {
 }
 
 namespace {
+// Shape of the one-launch fused kernel: nt columns and r rows per workgroup.  Every
+// workgroup quantises its r rows (VALU time ~ r) and streams nt K weight bytes (the row
+// tiles of one column slice share them through their XCD's L2).  The cost of a shape is
+// the rounds of workgroups per CU times the per-workgroup time 4 r + nt: measured at
+// K = 4096, N = 1024 on 256 CUs, one row of quantisation costs about as much as four
+// columns of weights, and for every M in 1..64 the fastest shape is the one this picks.
+// Ties go to the smaller r (a smaller kernel instance: less code, fewer registers); r is
+// at most the power of two at or above M.
+void fused_shape(const wq_ctx* c, int64_t M, int64_t N, int* nt, int* r) {
+  int64_t best = -1;
+  for (int rr : {1, 2, 4, 8, 16}) {
+    if (c->fused_r > 0 ? rr != c->fused_r : rr >= 2 * M) continue;
+    for (int w : {4, 8, 16, 32}) {
+      if (c->fused_nt > 0 && w != c->fused_nt) continue;
+      const int64_t wgs = (N + w - 1) / w * ((M + rr - 1) / rr);
+      const int64_t rounds = (wgs + c->num_cu - 1) / c->num_cu;
+      const int64_t cost = rounds * (4 * std::min<int64_t>(rr, M) + w);
+      if (best < 0 || cost < best) {
+        best = cost;
+        *nt = w;
+        *r = rr;
+      }
+    }
+  }
+}
+
 // the launch sequence of the fused call (valid sizes, M >= 1): see wq_fused_path
 int fused_path(const wq_ctx* c, int64_t M, int64_t K) {
-  if (M <= c->fused_gemv_max_m && wq::gemv_fits((int)M, (int)K, true) && c->decode_nt == 0) return 1;
+  if (M <= c->fused_gemv_max_m && wq::gemv_fits((int)M, (int)K, true)) return 1;
   if (M <= c->fused_max_m && wq::fused_decode_fits((int)M, (int)K)) return 2;
+  if (M <= c->fused_max_m && wq::gemv_fits((int)M, (int)K, true)) return 1;  // K the MFMA kernel does not take
   return 0;
 }
 }  // namespace
@@ -453,11 +502,14 @@ int wq_fused_quant_matmul(wq_ctx* c, const void* x, int64_t M, int64_t K, int64_
                    (long long)N, (long long)K, (long long)((N + 3) / 4));
     return status_of(e);
   }
-  const int nt = decode_nt(c, N);
-  hipError_t e = wq::launch_fused_decode(a, nt, st);
+  int nt = 16, rr = 16;  // fused_shape always sets both: the loops hold every knob value
+  fused_shape(c, M, N, &nt, &rr);
+  hipError_t e = wq::launch_fused_decode(a, nt, rr, st);
   if (c->log)
-    std::fprintf(stderr, "[wq] fused_quant_matmul one launch M=%lld N=%lld K=%lld cols/wg=%d grid=%lld cus=%d\n",
-                 (long long)M, (long long)N, (long long)K, nt, (long long)((N + nt - 1) / nt), c->num_cu);
+    std::fprintf(stderr,
+                 "[wq] fused_quant_matmul one launch M=%lld N=%lld K=%lld cols/wg=%d rows/wg=%d grid=%lldx%lld cus=%d\n",
+                 (long long)M, (long long)N, (long long)K, nt, rr, (long long)((N + nt - 1) / nt),
+                 (long long)((M + rr - 1) / rr), c->num_cu);
   return status_of(e);
 }
 

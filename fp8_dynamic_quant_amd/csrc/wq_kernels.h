@@ -33,8 +33,9 @@ struct DecodeArgs {
 // (1, 2 or 4), the grid's second dimension covering ceil(M / (16 mt)) row tiles.
 hipError_t launch_decode(const DecodeArgs& a, int nt, int mt, hipStream_t st);
 // One-launch fused quant + GEMM for M <= 64, K % 512 == 0, K <= 4096 (k_fused.hip);
-// nt output columns per workgroup (4, 8 or 16)
-hipError_t launch_fused_decode(const DecodeArgs& a, int nt, hipStream_t st);
+// nt output columns (4, 8, 16 or 32) and rows_per_wg rows (1, 2, 4, 8 or 16) per
+// workgroup, ceil(N / nt) * ceil(M / rows_per_wg) workgroups
+hipError_t launch_fused_decode(const DecodeArgs& a, int nt, int rows_per_wg, hipStream_t st);
 bool fused_decode_fits(int M, int K);
 // GEMV-style kernel for M <= 8 (k_decode.hip); fused needs M <= 4 and K <= 8192
 hipError_t launch_gemv(const DecodeArgs& a, hipStream_t st);

@@ -75,12 +75,15 @@ size_t wq_workspace_bytes(void);
  *   WQ_LOG=1          one line per call describing the chosen launch;
  *   WQ_FORCE_SPLIT=n  the K-split factor of the quant kernel (tests use it to show every
  *                     split gives the same bytes);
- *   WQ_DECODE_NT=n    columns per workgroup of the decode GEMM (4, 8 or 16; 0 = auto);
+ *   WQ_DECODE_NT=n    columns per workgroup of the decode GEMM of wq_quant_matmul (4, 8
+ *                     or 16; 0 = auto);
  *   WQ_DECODE_MT=t    16-row tiles per workgroup of the decode GEMM (1, 2 or 4; 0 = auto);
  *   WQ_FUSED_MAX_M=m  the largest M wq_fused_quant_matmul runs as one launch (0..64,
- *                     default 16; 0 = always two launches);
- *   WQ_FUSED_GEMV_MAX_M=m  up to this M (0..4, default 2) that one launch is the dot4
- *                     GEMV kernel, above it the 8-wave MFMA kernel;
+ *                     default 64; 0 = always two launches);
+ *   WQ_FUSED_GEMV_MAX_M=m  up to this M (0..4, default 0) that one launch is the dot4
+ *                     GEMV kernel rather than the 8-wave MFMA kernel;
+ *   WQ_FUSED_R=r, WQ_FUSED_NT=n  rows (1, 2, 4, 8, 16) and columns (4, 8, 16, 32) per
+ *                     workgroup of that MFMA kernel (0 = auto; see wq_ctx_set_fused_shape);
  *   WQ_SEG_SMALL=0    expert segments: run every expert on the tiled kernel instead of
  *                     sending the experts with at most 16 rows to the streaming kernel;
  *   WQ_FP8_RT=r       grouped FP8 contraction at T <= 64: 16-token tiles per workgroup
@@ -95,6 +98,13 @@ void wq_ctx_destroy(wq_ctx* ctx);
  * every split; tests use this to show it.  Returns WQ_ERR_SHAPE for n < 0; a split larger
  * than K / 512 makes later quant calls return WQ_ERR_SHAPE. */
 int wq_ctx_set_split(wq_ctx* ctx, int n);
+
+/* Force the shape of the one-launch fused kernel of wq_fused_quant_matmul on this context
+ * (the same knobs as WQ_FUSED_R / WQ_FUSED_NT): rows_per_wg rows (1, 2, 4, 8 or 16) and
+ * cols_per_wg output columns (4, 8, 16 or 32) per workgroup; 0 restores the automatic
+ * choice of that dimension.  Results are bit-identical for every shape; tests use this to
+ * show it.  Returns WQ_ERR_SHAPE for other values and changes nothing then. */
+int wq_ctx_set_fused_shape(wq_ctx* ctx, int rows_per_wg, int cols_per_wg);
 
 /* ---- per-token dynamic INT8 quantisation --------------------------------------------
  * Follows section 一 of the W8A8 article (npu_dynamic_quant: BF16 X -> INT8 X plus a
@@ -179,7 +189,7 @@ int wq_quant_matmul(wq_ctx* ctx, const wq_matmul_desc* desc, void* stream);
  * The whole chain of section 一 of the W8A8 article: per-token quant of the bf16 x [M, K]
  * (row stride ldx), the INT8 GEMM against w [N, K] and the bf16 epilogue.  Outputs are
  * bit-identical to wq_dynamic_quant followed by wq_quant_matmul.  y: bf16 [M, N] row
- * stride ldy.  For M up to the one-launch limit (WQ_FUSED_MAX_M, default 16) one kernel
+ * stride ldy.  For M up to the one-launch limit (WQ_FUSED_MAX_M, default 64) one kernel
  * quantises in registers and never writes the INT8 payload to HBM; above it the call runs
  * the quant and the GEMM as two launches, staging the payload in x_q_out / x_scale_out
  * when given, else in the context workspace (WQ_ERR_WORKSPACE if M*K bytes exceed it).
@@ -191,9 +201,11 @@ int wq_fused_quant_matmul(wq_ctx* ctx, const void* x, int64_t M, int64_t K, int6
 
 /* Which launch sequence wq_fused_quant_matmul takes for these sizes on this context:
  * 0 = the quant kernel, then the GEMM (two launches); 1 = one launch of the dot4 GEMV
- * kernel; 2 = one launch of the 8-wave MFMA kernel.  A negative value is -status for
- * invalid sizes (M < 1, or K, N as wq_fused_quant_matmul requires).  Host only: no
- * device work. */
+ * kernel (M <= WQ_FUSED_GEMV_MAX_M, or M <= 4 with a K the MFMA kernel does not take:
+ * K % 512 != 0 or 4096 < K <= 8192); 2 = one launch of the 8-wave MFMA kernel
+ * (K % 512 == 0, K <= 4096), its rows and columns per workgroup chosen from M and N.
+ * A negative value is -status for invalid sizes (M < 1, or K, N as wq_fused_quant_matmul
+ * requires).  Host only: no device work. */
 int wq_fused_path(const wq_ctx* ctx, int64_t M, int64_t K, int64_t N);
 
 /* ---- expert sort (MoE) ---------------------------------------------------------------

@@ -77,6 +77,63 @@ def test_fused_one_launch_shapes(M, K, N):
     _check_linear(x, w, sw, fused=True)
 
 
+@pytest.mark.parametrize("M,K,N", [(1, 16, 16), (3, 1040, 96), (2, 8192, 256), (4, 6144, 64)])
+def test_fused_gemv_for_k_the_mfma_kernel_does_not_take(M, K, N):
+    # K % 512 != 0 or 4096 < K <= 8192 at M <= 4: one launch of the dot4 GEMV kernel
+    assert wq.wq_fused_path(M, K, N) == 1
+    x = syn.activations((105, M, K), M, K, outlier_frac=0.005, outlier_mul=30.0)
+    w, sw = syn.int8_weights((106, N, K), N, K)
+    _check_linear(x, w, sw, fused=True)
+
+
+FUSED_SHAPES = [(r, nt) for r in (1, 2, 4, 8, 16) for nt in (4, 8, 16, 32)]
+
+
+@pytest.mark.parametrize("R,NT", FUSED_SHAPES)
+def test_every_fused_shape_gives_identical_bytes(R, NT):
+    # the one-launch kernel with each rows x columns per workgroup: ragged row tiles (M = 23)
+    # and column slices (N = 1040 is not a multiple of 32), x_q / x_scale / acc exported
+    for (M, K, N, seed) in ((23, 2048, 1040, 101), (64, 4096, 256, 102)):
+        x = syn.activations((seed, M, K), M, K, outlier_frac=0.005, outlier_mul=30.0)
+        w, sw = syn.int8_weights((seed + 50, N, K), N, K)
+        wq.set_fused_shape(DEV, R, NT)
+        try:
+            assert wq.wq_fused_path(M, K, N) == 2
+            _check_linear(x, w, sw, fused=True)
+        finally:
+            wq.set_fused_shape(DEV, 0, 0)
+
+
+def _tie_rows(M, K, seed):
+    """Rows whose values sit on or next to rounding ties of v / s: every chunk of them fails
+    the multiply-by-reciprocal check and takes the exact division."""
+    rng = np.random.default_rng(seed)
+    x = syn.activations((seed, M, K), M, K)
+    for m in range(0, M, 2):
+        a = np.float32([127.0, 100.0, 0.375, 7.5][(m // 2) % 4])
+        s = np.float32(a / np.float32(127.0))
+        k = rng.integers(-127, 127, size=K).astype(np.float32)
+        v = (k + np.float32(0.5)) * s
+        row = syn.to_bf16_bits(v.astype(np.float32))
+        row[0] = syn.to_bf16_bits(np.array([a], np.float32))[0]
+        x[m] = row
+    return x
+
+
+@pytest.mark.parametrize("R,NT", [(1, 4), (4, 16), (16, 32), (0, 0)])
+def test_fused_ties_take_the_exact_path(R, NT):
+    M, K, N = 16, 4096, 512
+    x = _tie_rows(M, K, 103)
+    x[5] = 0  # zero scale: the exact path's s == 0 rule
+    x[7, :] = syn.to_bf16_bits(np.full(K, 1.0e-38, np.float32))[:]  # subnormal scale
+    w, sw = syn.int8_weights((104, N, K), N, K)
+    wq.set_fused_shape(DEV, R, NT)
+    try:
+        _check_linear(x, w, sw, fused=True)
+    finally:
+        wq.set_fused_shape(DEV, 0, 0)
+
+
 @pytest.mark.parametrize("split", [1, 2, 4, 8, 16, 64])
 def test_every_split_gives_identical_bytes(split):
     x, w, sw = syn.wq_a_linear(7)
