@@ -22,7 +22,7 @@
 //    (CT = nt / 16 column tiles, or one partly used tile for nt < 16).
 //  * The per-row absmax is reduced inside the wave with DPP and across the 8 waves through
 //    LDS; each lane quantises its 8 values per row into the wave's private XOR-swizzled
-//    LDS tile (the MFMA A operand).  Only the fast path (multiply by RN(1/s), one
+//    LDS tile (the MFMA A operand).  Only the fast path (an fma with RN(1/s), one
 //    near-tie check per 8 values) is inline; the rare chunks that fail it, and rows whose
 //    scale is zero or not normal, go through one rolled loop with the exact quant_i8, so
 //    the unrolled code stays small.
@@ -71,18 +71,19 @@ __device__ __forceinline__ uint32_t bf16x8_absmax_bits(const uint4 u) {
   return max((uint32_t)e.x, (uint32_t)e.y);
 }
 
-// INT8 codes of 8 bf16 values by the fast path of quant_i8 (multiply by inv = RN(1/s));
+// INT8 codes of 8 bf16 values by the fast path of quant_i8 (fma with inv = RN(1/s));
 // *ok is false when a value lies near a rounding tie (the codes are then not used)
 __device__ __forceinline__ uint2 quant8_bf16_fast(const uint4 u, float inv, bool* ok) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-  float v[8], r[8];
+  float v[8];
+  uint32_t b[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = __uint_as_float(w[i] << 16);
     v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
-  *ok = quant_fast<8>(v, inv, r);
-  return uint2{pack4_rounded(r[0], r[1], r[2], r[3]), pack4_rounded(r[4], r[5], r[6], r[7])};
+  *ok = quant_fast<8>(v, inv, b);
+  return uint2{pack4_biased(b), pack4_biased(b + 4)};
 }
 
 // INT8 codes of 8 bf16 values by the exact quant_i8 (correctly rounded division)
@@ -131,23 +132,27 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
   float* s_lds = reinterpret_cast<float*>(wmax + R * kFW);
   float* wsc_lds = s_lds + R;
 
-  // ---- loads: this wave's chunk of each row, then its weights ------------------------------
+  // ---- loads, all issued before the first wait: this wave's chunk of each row, the slice's
+  // column scales, then the weights.  No load sits under a branch: lanes, rows and K steps
+  // out of range read a clamped in-range address and their values go unused (a load under
+  // a per-lane branch let the compiler wait for the first loads before issuing the rest,
+  // which cost a second memory round trip).
+  const int xl = min(lane, (KW >> 3) - 1);
   uint4 xr[R];
 #pragma unroll
   for (int r = 0; r < R; ++r)
-    xr[r] = (r < rows && xlane) ? *reinterpret_cast<const uint4*>(p.x + (int64_t)(row0 + r) * p.ldx + kbase + lane * 8)
-                                : uint4{0u, 0u, 0u, 0u};
+    xr[r] = *reinterpret_cast<const uint4*>(p.x + (int64_t)(row0 + min(r, rows - 1)) * p.ldx + kbase + xl * 8);
+  const float wsc_v = p.w_scale[min(n0 + min(t, nt - 1), N - 1)];
   v4i b[CT][kFMaxSteps];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    const int c = ct * 16 + cl;
-    const bool bvalid = c < nt && n0 + c < N;
-    const int8_t* wcol = p.w + (int64_t)(n0 + c) * K + kbase + 16 * kg;
+    // B column cl of tile ct is output column ct * 16 + cl; columns past nt or N read a
+    // column in range and are not stored
+    const int c = CT == 1 ? (cl & (nt - 1)) : ct * 16 + cl;
+    const int8_t* wcol = p.w + (int64_t)min(n0 + c, N - 1) * K + kbase + 16 * kg;
 #pragma unroll
-    for (int j = 0; j < kFMaxSteps; ++j)
-      b[ct][j] = (bvalid && j < steps) ? *reinterpret_cast<const v4i*>(wcol + j * 64) : v4i{0, 0, 0, 0};
+    for (int j = 0; j < kFMaxSteps; ++j) b[ct][j] = *reinterpret_cast<const v4i*>(wcol + min(j, steps - 1) * 64);
   }
-  if (t < nt) wsc_lds[t] = (n0 + t < N) ? p.w_scale[n0 + t] : 0.0f;
 
   // ---- per-row absmax: in-wave DPP reduction, then across waves through LDS ---------------
 #pragma unroll
@@ -217,6 +222,9 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
   }
 
   // ---- sum the 8 waves' tiles, epilogue -----------------------------------------------------
+  // (the column scales go to LDS only now: storing them earlier would wait for every load
+  // issued before them, the weights included, ahead of the quantisation)
+  if (t < nt) wsc_lds[t] = n0 + t < N ? wsc_v : 0.0f;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll

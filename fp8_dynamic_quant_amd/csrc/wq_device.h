@@ -49,41 +49,38 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
          ((uint32_t)(d & 0xFF) << 24);
 }
 
-// Four f32 values that hold integers in [-127, 127] -> their INT8 codes packed little
-// endian.  Adding 1.5 * 2^23 (exact for such integers) leaves the integer, in two's
-// complement, in the low mantissa bits; v_perm_b32 gathers the four low bytes.
-__device__ __forceinline__ uint32_t pack4_rounded(float r0, float r1, float r2, float r3) {
-  const float kPlace = 12582912.0f;  // 1.5 * 2^23
-  const uint32_t b0 = __float_as_uint(__fadd_rn(r0, kPlace));
-  const uint32_t b1 = __float_as_uint(__fadd_rn(r1, kPlace));
-  const uint32_t b2 = __float_as_uint(__fadd_rn(r2, kPlace));
-  const uint32_t b3 = __float_as_uint(__fadd_rn(r3, kPlace));
-  // selector byte k picks output byte k: 0..3 = bytes of the second operand, 4..7 = bytes
-  // of the first, 0x0c = zero
-  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);  // b0.byte0, b1.byte0, 0, 0
-  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x04000c0cu);  // 0, 0, b2.byte0, b3.byte0
-  return lo | hi;
-}
-
 // Fast path of quant_i8 for N values at once, without the division, for a normal finite
 // scale s (s = RN(absmax/127), so |v/s| <= 127 (1 + 2^-23) for every value of the row).
-// With inv = RN(1/s), t = RN(v * inv) lies within 3 * 2^-24 * |v/s| < 2.3e-5 of RN(v/s).
-// When every t is at least 2^-14 from the nearest half-integer, RN(v/s) rounds to the same
-// integer as t, which is within [-127, 127], so rint(t) is the code and the clamp is moot.
-// Returns false for a near-tie (the caller then takes the exact path for these N values;
-// a wave branches once per N values, not per value).  Only the largest |t - rint(t)| is
-// compared: one compare per N values.
+// With inv = RN(1/s) and e = v * inv (exact product), |e - v/s| < 2^-17.  One fma gives
+// u = RN(e + P) with P = 1.5 * 2^23: in that binade the unit is 1, so u = P + n with
+// n = e rounded to the nearest integer, and u's low byte is n in two's complement.  A second
+// fma gives d = RN(e - n) (P - u = -n is exact).  When every |d| < 0.5 - 2^-14, RN(v/s),
+// which lies within 2^-16 of e, rounds to the same integer n, which is within [-127, 127],
+// so n is quant_i8's code and the clamp is moot.  Returns false for a near-tie (the caller
+// then takes the exact path for these N values; a wave branches once per N values, not per
+// value).  u[i] receives the bit patterns of the biased sums.
 template <int N>
-__device__ __forceinline__ bool quant_fast(const float* v, float inv, float* r) {
-  constexpr float kGuard = 0.49993896484375f;  // 0.5 - 2^-14
+__device__ __forceinline__ bool quant_fast(const float* v, float inv, uint32_t* u) {
+  constexpr float kPlace = 12582912.0f;          // 1.5 * 2^23
+  constexpr float kGuard = 0.49993896484375f;    // 0.5 - 2^-14
   float dmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const float t = __fmul_rn(v[i], inv);
-    r[i] = rintf(t);
-    dmax = fmaxf(dmax, fabsf(__fsub_rn(t, r[i])));
+    const float b = __builtin_fmaf(v[i], inv, kPlace);
+    u[i] = __float_as_uint(b);
+    dmax = fmaxf(dmax, fabsf(__builtin_fmaf(v[i], inv, __fsub_rn(kPlace, b))));
   }
   return dmax < kGuard;
+}
+
+// four biased sums P + n (n in [-128, 127]) -> the four codes n packed little endian:
+// v_perm_b32 gathers the low bytes
+__device__ __forceinline__ uint32_t pack4_biased(const uint32_t* u) {
+  // selector byte k picks output byte k: 0..3 = bytes of the second operand, 4..7 = bytes
+  // of the first, 0x0c = zero
+  const uint32_t lo = __builtin_amdgcn_perm(u[1], u[0], 0x0c0c0400u);  // u0.byte0, u1.byte0, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(u[3], u[2], 0x04000c0cu);  // 0, 0, u2.byte0, u3.byte0
+  return lo | hi;
 }
 
 // the fast path's precondition on the scale: normal and finite (a zero, subnormal or
@@ -94,17 +91,16 @@ __device__ __forceinline__ bool quant_scale_normal(float s) {
 
 // INT8 codes of 8 values (two packed words), bit-identical to quant_i8 on each value.
 __device__ __forceinline__ uint2 quant8(const float* v, float s, float inv) {
-  float r[8];
-  if (quant_scale_normal(s) && quant_fast<8>(v, inv, r))
-    return uint2{pack4_rounded(r[0], r[1], r[2], r[3]), pack4_rounded(r[4], r[5], r[6], r[7])};
+  uint32_t u[8];
+  if (quant_scale_normal(s) && quant_fast<8>(v, inv, u)) return uint2{pack4_biased(u), pack4_biased(u + 4)};
   return uint2{pack4_i8(quant_i8(v[0], s), quant_i8(v[1], s), quant_i8(v[2], s), quant_i8(v[3], s)),
                pack4_i8(quant_i8(v[4], s), quant_i8(v[5], s), quant_i8(v[6], s), quant_i8(v[7], s))};
 }
 
 // INT8 codes of 4 values (one packed word), bit-identical to quant_i8 on each value.
 __device__ __forceinline__ uint32_t quant4(const float* v, float s, float inv) {
-  float r[4];
-  if (quant_scale_normal(s) && quant_fast<4>(v, inv, r)) return pack4_rounded(r[0], r[1], r[2], r[3]);
+  uint32_t u[4];
+  if (quant_scale_normal(s) && quant_fast<4>(v, inv, u)) return pack4_biased(u);
   return pack4_i8(quant_i8(v[0], s), quant_i8(v[1], s), quant_i8(v[2], s), quant_i8(v[3], s));
 }
 
