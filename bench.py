@@ -17,7 +17,9 @@ per-token-group quant with packed UE8M0 scales and the grouped FP8 contraction, 
 expert-sorted MoE block; then the CPU oracle baseline.
 
 --traffic-probe runs only the roofline kernel's launches (plus a copy kernel of known
-size that calibrates the counters) for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs.
+size that calibrates the counters) for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs;
+--traffic-summary FETCH_DIR WRITE_DIR PROBE_LOG turns the two runs' counter CSVs (and the
+probe's printed line) into the JSON the roofline object reads its `traffic` from.
 """
 
 from __future__ import annotations
@@ -38,7 +40,7 @@ FP8_PEAK_TOPS = 5000.0
 SWEEP = (1, 2, 4, 7, 8, 16, 32, 64)
 K_A, N_A = 4096, 1024
 ROTATE_BYTES = 512 << 20
-ROOFLINE_KERNEL = "k_fused_decode"  # the one-launch fused kernel (wq_fused_path == 2)
+ROOFLINE_KERNEL = "k_fused_decode"  # the one-launch fused kernel (wq_fused_path == 2), every <R, CT> instance
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_fused_decode_wq_a.json")
 KERNEL_SOURCES = ("k_fused.hip", "wq_device.h", "wq_kernels.h")  # the roofline kernel and the headers it includes
 
@@ -59,6 +61,61 @@ def kernel_source_hash():
         with open(os.path.join(ROOT, "fp8_dynamic_quant_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def traffic_summary(fetch_dir, write_dir, probe_log):
+    """HBM bytes per roofline-kernel launch from two rocprofv3 --pmc runs of --traffic-probe
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
+    reads for the probe's final 64 MiB device copy."""
+    import csv
+
+    probe = None
+    for line in open(probe_log):
+        line = line.strip()
+        if line.startswith("{") and "traffic_probe" in line:
+            probe = json.loads(line)["traffic_probe"]
+    if probe is None:
+        raise SystemExit(f"no traffic_probe line in {probe_log}")
+
+    def dispatches(d):
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        fused = [float(r["Counter_Value"]) for r in rows if ROOFLINE_KERNEL in r["Kernel_Name"]]
+        copies = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"] == "__amd_rocclr_copyBuffer"]
+        return fused, copies[-1]
+
+    fetch, fetch_cal = dispatches(fetch_dir)
+    write, write_cal = dispatches(write_dir)
+    ms, per = probe["roofline_ms"], probe["launches_per_m"]
+    if len(fetch) != len(ms) * per or len(write) != len(ms) * per:
+        raise SystemExit(f"expected {len(ms) * per} roofline launches, got {len(fetch)} / {len(write)}")
+    nbytes = probe["calibration_copy_bytes"]
+    ff, wf = nbytes / 1024 / fetch_cal, nbytes / 1024 / write_cal  # true KiB per counted KiB
+    per_m = {}
+    for i, M in enumerate(ms):
+        fk = sum(fetch[i * per:(i + 1) * per]) / per
+        wk = sum(write[i * per:(i + 1) * per]) / per
+        per_m[str(M)] = {"fetch_kib_raw": round(fk, 2), "write_kib_raw": round(wk, 2),
+                         "hbm_bytes": round((fk * ff + wk * wf) * 1024), "algorithmic_bytes": fused_bytes(M)}
+    return {
+        "kernel": ROOFLINE_KERNEL,
+        "workload": f"wq_fused_quant_matmul X bf16 [M,4096] x W int8 [4096->1024], M in {ms}, {per} launches "
+                    "per M, each on a cold weight copy",
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/tr_fetch -o run --output-format csv -- python bench.py "
+            "--traffic-probe > gpurun_out/tr_fetch.log",
+            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/tr_write -o run --output-format csv -- python bench.py "
+            "--traffic-probe > gpurun_out/tr_write.log",
+            "python bench.py --traffic-summary gpurun_out/tr_fetch gpurun_out/tr_write gpurun_out/tr_fetch.log",
+        ],
+        "calibration": {"kernel": "__amd_rocclr_copyBuffer (torch copy_ of 64 MiB)", "bytes_read": nbytes,
+                        "bytes_written": nbytes, "fetch_size_kib_read": fetch_cal, "write_size_kib_read": write_cal,
+                        "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+        "per_M": per_m,
+        "hbm_bytes_per_launch_mean": round(sum(v["hbm_bytes"] for v in per_m.values()) / len(per_m)),
+        "algorithmic_bytes_per_launch_mean": round(sum(v["algorithmic_bytes"] for v in per_m.values()) / len(per_m)),
+        "kernel_source_hash": probe["kernel_source_hash"],
+    }
 
 
 def cpu_baseline(budget_s=10.0):
@@ -102,6 +159,8 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="skip the prefill / FP8 / MoE measurements")
     ap.add_argument("--no-sweep", action="store_true", help="skip the standalone sweep and the floors")
     ap.add_argument("--traffic-probe", action="store_true", help="only the roofline kernel's launches, for counters")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_LOG"),
+                    help="write the traffic JSON from two --traffic-probe counter runs (no GPU)")
     ap.add_argument("--prefill-probe", action="store_true",
                     help="only two launches of the M=8192 prefill GEMM on random operands, for counters")
     args = ap.parse_args()
@@ -109,6 +168,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the kernels run on one MI355X and the "
               f"multi-GPU sharding is described, not run.", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_summary:
+        print(json.dumps(traffic_summary(*args.traffic_summary), indent=1))
+        return
 
     import numpy as np
     import torch
