@@ -10,8 +10,9 @@
 // only G * N / 128 = 64 workgroups on the chip).  So each workgroup owns 16 output columns
 // of one group and the whole K range, G * N / 16 = 512 workgroups for the DeepSeek shape:
 //  * four waves split K; each wave loads its weights (32 bytes per lane per 128-deep step)
-//    straight into registers in the v_mfma_scale_f32_16x16x128_f8f6f4 B layout, all before
-//    the first wait;
+//    straight into registers in the v_mfma_scale_f32_16x16x128_f8f6f4 B layout, after the
+//    scale words and before the first wait; the token tiles follow, each loading while the
+//    previous one multiplies;
 //  * a 128-deep step is exactly one scale block, so the block scales ride in the MFMA's
 //    E8M0 scale operands: the activation byte is read from the packed storage as written,
 //    the weight byte is the exponent field of the f32 power-of-two block scale;
@@ -29,82 +30,103 @@ constexpr int kF8MaxSteps = 8;  // 128-deep K steps per wave: K <= 4096
 constexpr int kF8MaxRT = 4;     // 16-token row tiles: T <= 64
 }  // namespace
 
-__global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p, int rt_per_wg) {
-  __shared__ float red[kF8Waves][kF8MaxRT][4][64];
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+template <int TPW>
+__global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
+  __shared__ float red[4][TPW][4][64];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: the weight-scale loads go scalar
   const int T = p.M, N = p.N, K = p.K, g = blockIdx.y;
   const int n0 = blockIdx.x * kF8NT;
   const int KT = K >> 7;                 // 128-deep blocks
-  const int steps = KT / kF8Waves;       // per wave
+  const int steps = KT / 4;              // per wave
   const int kb0 = wv * steps;
   const int cl = lane & 15, kq = lane >> 4;  // column (B) / row (A) in the tile; 32-byte quarter of the step
   const int n = n0 + cl;
+  const int PH = (KT + 3) >> 2;
+  const int32_t* xs_g = p.a_scale_packed + (int64_t)g * PH * p.a_scale_tokens;
+  const int8_t* A = p.a + (int64_t)g * p.a_batch_stride + kq * 32;
+  const int rt_lo = blockIdx.z * TPW;    // this workgroup's 16-token tiles [rt_lo, rt_lo + TPW)
 
-  // ---- weights and their block-scale exponents, all issued first ---------------------------
+  // Every load is issued before the first wait and none sits under a branch (K steps and
+  // rows out of range read clamped in-range addresses; their values go unused), so the
+  // compiler keeps them in flight together: a scale load waited for next to each MFMA
+  // had cost a memory round trip per MFMA.  (At most 63 vector loads can be counted in
+  // flight; the weight block scales are wave-uniform scalar loads outside that count.)
+  // this wave's K blocks [kb0, kb0 + steps) touch at most 3 packed activation-scale words
+  const int w0 = kb0 >> 2;
+  // ---- weights, 32 bytes per lane per 128-deep step, straight into the B layout ----------
   const int8_t* W = p.w + (int64_t)g * p.w_batch_stride + (int64_t)n * K + kq * 32;
   v8i b[kF8MaxSteps];
 #pragma unroll
   for (int j = 0; j < kF8MaxSteps; ++j) {
-    if (j < steps) {
-      const v4i lo = *reinterpret_cast<const v4i*>(W + (int64_t)(kb0 + j) * 128);
-      const v4i hi = *reinterpret_cast<const v4i*>(W + (int64_t)(kb0 + j) * 128 + 16);
-      b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    } else {
-      b[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    const int8_t* src = W + (int64_t)(kb0 + min(j, steps - 1)) * 128;
+    const v4i lo = *reinterpret_cast<const v4i*>(src);
+    const v4i hi = *reinterpret_cast<const v4i*>(src + 16);
+    b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
+  // ---- token tiles (fragments and packed scale words): the next tile loads while the
+  // current one multiplies -------------------------------------------------------------------
+  auto load_tile = [&](int rt, v8i (&a)[kF8MaxSteps], int32_t (&wd)[3]) {
+    // rows past T read row T-1: they only feed output rows that are not stored
+    const int row = min((rt_lo + rt) * 16 + cl, T - 1);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) wd[q] = xs_g[(int64_t)min(w0 + q, PH - 1) * p.a_scale_tokens + row];
+    const int8_t* arow = A + (int64_t)row * p.lda;
+#pragma unroll
+    for (int j = 0; j < kF8MaxSteps; ++j) {
+      const int8_t* src = arow + (int64_t)(kb0 + min(j, steps - 1)) * 128;
+      const v4i lo = *reinterpret_cast<const v4i*>(src);
+      const v4i hi = *reinterpret_cast<const v4i*>(src + 16);
+      a[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  v8i abuf[2][kF8MaxSteps];
+  int32_t words[2][3];
+  load_tile(0, abuf[0], words[0]);
+  if (TPW > 1) load_tile(1, abuf[1], words[1]);
+  // keep the issue order: a load the scheduler sinks next to its use is waited for at once
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- the weight block-scale exponents (wave-uniform scalar loads, while the vector loads
+  // are in flight; the empty asm pins each value here, so no load is sunk next to its MFMA)
   const float* wsc = p.w_scale + ((int64_t)g * (N >> 7) + (n0 >> 7)) * KT + kb0;
-  int sb[kF8MaxSteps];
+  uint32_t wsb[kF8MaxSteps];
 #pragma unroll
-  for (int j = 0; j < kF8MaxSteps; ++j) sb[j] = j < steps ? (int)((__float_as_uint(wsc[j]) >> 23) & 0xFF) : 127;
-
-  // ---- token tiles --------------------------------------------------------------------------
-  const int PH = (KT + 3) >> 2;
-  const int32_t* xs_g = p.a_scale_packed + (int64_t)g * PH * p.a_scale_tokens;
-  const int8_t* A = p.a + (int64_t)g * p.a_batch_stride + kq * 32;
-  // this workgroup's token tiles: [rt_lo, rt_hi) of the 16-token tiles (grid z splits them)
-  const int rt_lo = blockIdx.z * rt_per_wg;
-  const int rt_hi = min((T + 15) >> 4, rt_lo + rt_per_wg);
-  const int RT = rt_hi - rt_lo;
-  v4f acc[kF8MaxRT];
+  for (int j = 0; j < kF8MaxSteps; ++j) wsb[j] = __float_as_uint(wsc[min(j, steps - 1)]);
+  static_assert(kF8MaxSteps == 8, "one pin for the eight scales");
+  asm volatile("" : "+s"(wsb[0]), "+s"(wsb[1]), "+s"(wsb[2]), "+s"(wsb[3]), "+s"(wsb[4]), "+s"(wsb[5]), "+s"(wsb[6]),
+               "+s"(wsb[7]));
+  int sbx[kF8MaxSteps];
 #pragma unroll
-  for (int rt = 0; rt < kF8MaxRT; ++rt) acc[rt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < kF8MaxSteps; ++j) sbx[j] = (int)((wsb[j] >> 23) & 0xFF);
+  v4f acc[TPW];
 #pragma unroll
-  for (int rt = 0; rt < kF8MaxRT; ++rt) {
-    if (rt < RT) {  // uniform
-      // rows past T read row T-1: they only feed output rows that are not stored
-      const int row = min((rt_lo + rt) * 16 + cl, T - 1);
-      const int8_t* arow = A + (int64_t)row * p.lda;
-      v8i a[kF8MaxSteps];
+  for (int rt = 0; rt < TPW; ++rt) {
+    if (rt >= 1 && rt + 1 < TPW) {
+      load_tile(rt + 1, abuf[(rt + 1) & 1], words[(rt + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    acc[rt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < kF8MaxSteps; ++j) {
-        if (j < steps) {
-          const v4i lo = *reinterpret_cast<const v4i*>(arow + (int64_t)(kb0 + j) * 128);
-          const v4i hi = *reinterpret_cast<const v4i*>(arow + (int64_t)(kb0 + j) * 128 + 16);
-          a[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kF8MaxSteps; ++j) {
-        if (j < steps) {
-          const int kb = kb0 + j;
-          const int32_t w = xs_g[(int64_t)(kb >> 2) * p.a_scale_tokens + row];
-          const int sa = (w >> (8 * (kb & 3))) & 0xFF;
-          acc[rt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[j], b[j], acc[rt], 0, 0, 0, sa, 0, sb[j]);
-        }
+    for (int j = 0; j < kF8MaxSteps; ++j) {
+      if (j < steps) {  // uniform
+        const int kb = kb0 + j;
+        const int q = (kb >> 2) - w0;  // 0, 1 or 2
+        const int32_t w = q == 0 ? words[rt & 1][0] : (q == 1 ? words[rt & 1][1] : words[rt & 1][2]);
+        const int sa = (w >> (8 * (kb & 3))) & 0xFF;
+        // sbx[j]: the exponent field of the power-of-two weight block scale
+        acc[rt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(abuf[rt & 1][j], b[j], acc[rt], 0, 0, 0, sa, 0, sbx[j]);
       }
     }
   }
 
   // ---- the four waves' partial sums, in a fixed order, then bf16 ----------------------------
 #pragma unroll
-  for (int rt = 0; rt < kF8MaxRT; ++rt)
-    if (rt < RT)
+  for (int rt = 0; rt < TPW; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wv][rt][i][lane] = acc[rt][i];
+    for (int i = 0; i < 4; ++i) red[wv][rt][i][lane] = acc[rt][i];
   __syncthreads();
   uint16_t* Y = reinterpret_cast<uint16_t*>(p.y) + (int64_t)g * p.y_batch_stride;
-  for (int e = t; e < RT * 4 * 64; e += 256) {
+  for (int e = t; e < TPW * 4 * 64; e += 256) {
     const int ln = e & 63, ri = e >> 6, rt = ri >> 2, i = ri & 3;
     const int row = (rt_lo + rt) * 16 + 4 * (ln >> 4) + i;  // MFMA 16x16 output: col = lane % 16, row = 4 (lane / 16) + i
     if (row < T) {
@@ -123,8 +145,14 @@ bool fp8_decode_fits(int T, int N, int K) {
 hipError_t launch_fp8_decode(const TileArgs& a, int rt_per_wg, hipStream_t st) {
   if (!fp8_decode_fits(a.M, a.N, a.K) || rt_per_wg < 1 || rt_per_wg > kF8MaxRT) return hipErrorInvalidValue;
   const int rt = (a.M + 15) / 16;
-  const dim3 grid((unsigned)(a.N / kF8NT), (unsigned)a.batch, (unsigned)((rt + rt_per_wg - 1) / rt_per_wg));
-  hipLaunchKernelGGL(k_fp8_decode, grid, dim3(256), 0, st, a, rt_per_wg);
+  const int tpw = min(rt_per_wg, rt);  // token tiles per workgroup
+  const dim3 grid((unsigned)(a.N / kF8NT), (unsigned)a.batch, (unsigned)((rt + tpw - 1) / tpw));
+  switch (tpw) {
+    case 1: hipLaunchKernelGGL(k_fp8_decode<1>, grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(k_fp8_decode<2>, grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL(k_fp8_decode<3>, grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL(k_fp8_decode<4>, grid, dim3(256), 0, st, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -78,8 +78,8 @@ hipError_t launch_gemm_i8_big(const TileArgs& a, int num_cu, hipStream_t st);
 bool big_fits(int M, int N, int K, int64_t lda, int64_t ldy);
 
 // FP8 grouped contraction for T <= 64, K % 512 == 0, K <= 4096 (k_fp8_decode.hip):
-// 16 output columns of one group and rt_per_wg 16-token tiles per workgroup,
-// grid (N / 16, G, ceil(ceil(T / 16) / rt_per_wg))
+// 16 output columns of one group and min(rt_per_wg, ceil(T / 16)) 16-token tiles per
+// workgroup, grid (N / 16, G, ceil(ceil(T / 16) / that))
 hipError_t launch_fp8_decode(const TileArgs& a, int rt_per_wg, hipStream_t st);
 bool fp8_decode_fits(int T, int N, int K);
 

@@ -134,6 +134,23 @@ def test_fused_ties_take_the_exact_path(R, NT):
         wq.set_fused_shape(DEV, 0, 0)
 
 
+@pytest.mark.parametrize("M,K,N", [(5, 4096, 1024), (64, 2048, 272), (3, 1040, 96), (80, 1024, 256)])
+def test_fused_strided_rows(M, K, N):
+    # x rows ldx = K + 64 apart and y rows ldy = N + 8 apart (views into wider buffers), on
+    # the one-launch MFMA kernel, the GEMV and the two-launch path; the padding of y stays
+    # untouched
+    xw = syn.activations((107, M, K + 64), M, K + 64, outlier_frac=0.005, outlier_mul=30.0)
+    x = np.ascontiguousarray(xw[:, :K])
+    w, sw = syn.int8_weights((108, N, K), N, K)
+    ref = il.linear_w8a8(x, w, sw)
+    yw = poison((M, N + 8), torch.bfloat16)
+    y = wq.wq_fused_quant_matmul(bf16_dev(xw)[:, :K], dev(w), dev(sw), y=yw[:, :N])
+    torch.cuda.synchronize()
+    assert y.stride(0) == N + 8
+    _y_within_one_ulp(host_bf16_bits(y), ref["y"])
+    assert (host_bf16_bits(yw[:, N:]) == 0xA5A5).all()
+
+
 @pytest.mark.parametrize("split", [1, 2, 4, 8, 16, 64])
 def test_every_split_gives_identical_bytes(split):
     x, w, sw = syn.wq_a_linear(7)
