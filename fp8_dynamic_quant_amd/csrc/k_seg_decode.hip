@@ -31,25 +31,28 @@ constexpr int kSDMaxSteps = 8;    // 64-deep K steps per wave: K <= 4096
 constexpr int kSDMaxExperts = 4096;
 }  // namespace
 
-template <int EPI>
+template <int EPI, int STEPS>
 __global__ __launch_bounds__(512) void k_seg_decode(TileArgs p) {
-  __shared__ int exp_list[kSDMaxExperts];
+  __shared__ int exp_list[kSDMaxExperts];  // listed expert: id | rows << 16
+  __shared__ int exp_row0[kSDMaxExperts];  // its first row
   __shared__ int nexp;
   __shared__ int red[kSDW][2][4][64];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int K = p.K, N = p.N;
   const int ncols = EPI == 2 ? N / 2 : N;  // output columns
-  const int KW = K / kSDW, steps = KW >> 6, kbase = wv * KW;
+  const int KW = STEPS * 64, kbase = wv * KW;  // K = 8 waves x STEPS 64-deep steps
   const int cl = lane & 15, kg = lane >> 4;
 
-  // the experts with 1 <= rows <= kSegSmallRows, in expert order (one wave, shuffle scan)
+  // the experts with 1 <= rows <= kSegSmallRows, in expert order (one wave, shuffle scan),
+  // with their first rows and row counts, so items read them from LDS, not global memory
   if (t < 64) {
     int base = 0;
     for (int e0 = 0; e0 < p.batch; e0 += 64) {
       const int e = e0 + t;
-      int take = 0;
+      int take = 0, rows = 0, row0 = 0;
       if (e < p.batch) {
-        const int64_t rows = p.seg_offsets[e + 1] - p.seg_offsets[e];
+        row0 = (int)p.seg_offsets[e];
+        rows = (int)(p.seg_offsets[e + 1] - p.seg_offsets[e]);
         take = rows >= 1 && rows <= kSegSmallRows;
       }
       int incl = take;
@@ -58,7 +61,10 @@ __global__ __launch_bounds__(512) void k_seg_decode(TileArgs p) {
         const int u = __shfl_up(incl, o, 64);
         if (t >= o) incl += u;
       }
-      if (take) exp_list[base + incl - 1] = e;
+      if (take) {
+        exp_list[base + incl - 1] = e | (rows << 16);
+        exp_row0[base + incl - 1] = row0;
+      }
       base += __shfl(incl, 63, 64);
     }
     if (t == 0) nexp = base;
@@ -68,41 +74,67 @@ __global__ __launch_bounds__(512) void k_seg_decode(TileArgs p) {
   const int col2 = EPI == 2 ? ncols : kSDNT;                  // offset of an item's second tile
   const int items = nexp * tiles;
 
+  // this thread's output in an item's epilogue: MFMA 16x16 output row r, column c of tile
+  // `otile` (col = lane % 16, row = 4 (lane / 16) + i)
+  const int oi = (t >> 6) & 3, otile = t >> 8;
+  const int orow = 4 * (lane >> 4) + oi, ocol = lane & 15;
+  struct Item {
+    int e, rows, row0, n0;
+  };
+  auto item_of = [&](int item) {
+    const int x = item / tiles;
+    const int info = exp_list[x];
+    Item it;
+    it.e = info & 0xFFFF;
+    it.rows = info >> 16;
+    it.row0 = exp_row0[x];
+    it.n0 = (item - x * tiles) * (EPI == 2 ? kSDNT : 2 * kSDNT);
+    return it;
+  };
+
   // Items are software-pipelined in pairs of register buffers: the loads of the next item
-  // are issued right after the MFMAs of the current one, so they stream while the current
-  // item's cross-wave sum and epilogue run.
-  v4i g0[kSDMaxSteps], u0[kSDMaxSteps], a0[kSDMaxSteps];
-  v4i g1[kSDMaxSteps], u1[kSDMaxSteps], a1[kSDMaxSteps];
-  auto issue = [&](int item, v4i (&bg)[kSDMaxSteps], v4i (&bu)[kSDMaxSteps], v4i (&a)[kSDMaxSteps]) {
-    const int e = exp_list[item / tiles];
-    const int n0 = (item - (item / tiles) * tiles) * (EPI == 2 ? kSDNT : 2 * kSDNT);
-    const int row0 = (int)p.seg_offsets[e];
-    const int rows = (int)p.seg_offsets[e + 1] - row0;
-    const int8_t* W = p.w + (int64_t)e * p.w_batch_stride + kbase + kg * 16;
+  // (weights, activation rows and this thread's epilogue scales) are issued right after the
+  // MFMAs of the current one, so they stream while the current item's cross-wave sum and
+  // epilogue run.  No load sits under a branch (the step count is a template parameter, and
+  // rows past the segment read clamped addresses whose values go unused), and the epilogue
+  // reads no global memory: a load waited for there would also wait for the next item's.
+  v4i g0[STEPS], u0[STEPS], a0[STEPS];
+  v4i g1[STEPS], u1[STEPS], a1[STEPS];
+  float sc0[3], sc1[3];  // s_m, sw_n (gate), sw_n (up)
+  auto issue = [&](int item, v4i (&bg)[STEPS], v4i (&bu)[STEPS], v4i (&a)[STEPS], float (&sc)[3]) {
+    const Item it = item_of(item);
+    const int8_t* W = p.w + (int64_t)it.e * p.w_batch_stride + kbase + kg * 16;
     // rows past the segment read its last row: they only feed output rows not stored
-    const int8_t* arow = p.a + (int64_t)(row0 + min(cl, rows - 1)) * p.lda + kbase + kg * 16;
+    const int8_t* arow = p.a + (int64_t)(it.row0 + min(cl, it.rows - 1)) * p.lda + kbase + kg * 16;
 #pragma unroll
-    for (int j = 0; j < kSDMaxSteps; ++j) {
-      if (j < steps) {
-        bg[j] = *reinterpret_cast<const v4i*>(W + (int64_t)(n0 + cl) * K + j * 64);
-        bu[j] = *reinterpret_cast<const v4i*>(W + (int64_t)(col2 + n0 + cl) * K + j * 64);
-      }
+    for (int j = 0; j < STEPS; ++j) {
+      bg[j] = *reinterpret_cast<const v4i*>(W + (int64_t)(it.n0 + cl) * K + j * 64);
+      bu[j] = *reinterpret_cast<const v4i*>(W + (int64_t)(col2 + it.n0 + cl) * K + j * 64);
     }
 #pragma unroll
-    for (int j = 0; j < kSDMaxSteps; ++j)
-      if (j < steps) a[j] = *reinterpret_cast<const v4i*>(arow + j * 64);
+    for (int j = 0; j < STEPS; ++j) a[j] = *reinterpret_cast<const v4i*>(arow + j * 64);
+    const float* wsc = p.w_scale + (int64_t)it.e * N;
+    sc[0] = p.a_scale[it.row0 + min(orow, it.rows - 1)];
+    if constexpr (EPI == 2) {
+      sc[1] = wsc[it.n0 + ocol];
+      sc[2] = wsc[it.n0 + ocol + ncols];
+    } else {
+      sc[1] = wsc[it.n0 + otile * kSDNT + ocol];
+      sc[2] = 0.0f;
+    }
   };
-  auto finish = [&](int item, const v4i (&bg)[kSDMaxSteps], const v4i (&bu)[kSDMaxSteps], const v4i (&a)[kSDMaxSteps],
-                    int next, v4i (&ng)[kSDMaxSteps], v4i (&nu)[kSDMaxSteps], v4i (&na)[kSDMaxSteps]) {
+  auto finish = [&](int item, const v4i (&bg)[STEPS], const v4i (&bu)[STEPS], const v4i (&a)[STEPS],
+                    const float (&sc)[3], int next, v4i (&ng)[STEPS], v4i (&nu)[STEPS], v4i (&na)[STEPS],
+                    float (&nsc)[3]) {
     v4i accg = v4i{0, 0, 0, 0}, accu = v4i{0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < kSDMaxSteps; ++j) {
-      if (j < steps) {
-        accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j], bg[j], accg, 0, 0, 0);
-        accu = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j], bu[j], accu, 0, 0, 0);
-      }
+    for (int j = 0; j < STEPS; ++j) {
+      accg = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j], bg[j], accg, 0, 0, 0);
+      accu = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j], bu[j], accu, 0, 0, 0);
     }
-    if (next < items) issue(next, ng, nu, na);
+    // unconditional (past the last item it reloads the last one, unused): under a branch,
+    // the waits for this item's epilogue scales would also wait for the next item's loads
+    issue(min(next, items - 1), ng, nu, na, nsc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       red[wv][0][i][lane] = accg[i];
@@ -110,32 +142,25 @@ __global__ __launch_bounds__(512) void k_seg_decode(TileArgs p) {
     }
     __syncthreads();
     if (EPI == 2 ? t < 256 : true) {
-      const int e = exp_list[item / tiles];
-      const int n0 = (item - (item / tiles) * tiles) * (EPI == 2 ? kSDNT : 2 * kSDNT);
-      const int row0 = (int)p.seg_offsets[e];
-      const int rows = (int)p.seg_offsets[e + 1] - row0;
-      const int ln = t & 63, i = (t >> 6) & 3, tile = t >> 8;  // tile: which of the item's two (bf16 epilogue)
-      const int r = 4 * (ln >> 4) + i, c = ln & 15;  // MFMA 16x16 output: col = lane % 16, row = 4 (lane / 16) + i
-      if (r < rows) {
+      const Item it = item_of(item);
+      if (orow < it.rows) {
         int vg = 0, vu = 0;
 #pragma unroll
         for (int w = 0; w < kSDW; ++w) {
-          vg += red[w][tile][i][ln];
-          if constexpr (EPI == 2) vu += red[w][1][i][ln];
+          vg += red[w][otile][oi][lane];
+          if constexpr (EPI == 2) vu += red[w][1][oi][lane];
         }
-        const int m = row0 + r;
-        const float s = p.a_scale[m];
-        const float* wsc = p.w_scale + (int64_t)e * N;
+        const int m = it.row0 + orow;
         if constexpr (EPI == 2) {
-          const int n = n0 + c;
-          const float gv = __fmul_rn(__fmul_rn((float)vg, s), wsc[n]);
-          const float uv = __fmul_rn(__fmul_rn((float)vu, s), wsc[n + ncols]);
+          const int n = it.n0 + ocol;
+          const float gv = __fmul_rn(__fmul_rn((float)vg, sc[0]), sc[1]);
+          const float uv = __fmul_rn(__fmul_rn((float)vu, sc[0]), sc[2]);
           const float sg = __fdiv_rn(gv, __fadd_rn(1.0f, exp_fixed(-gv)));
           reinterpret_cast<float*>(p.y)[(int64_t)m * p.ldy + n] = __fmul_rn(sg, uv);
         } else {
-          const int n = n0 + tile * kSDNT + c;
+          const int n = it.n0 + otile * kSDNT + ocol;
           reinterpret_cast<uint16_t*>(p.y)[(int64_t)m * p.ldy + n] =
-              (uint16_t)f32_to_bf16_rn(__fmul_rn(__fmul_rn((float)vg, s), wsc[n]));
+              (uint16_t)f32_to_bf16_rn(__fmul_rn(__fmul_rn((float)vg, sc[0]), sc[1]));
         }
       }
     }
@@ -144,12 +169,12 @@ __global__ __launch_bounds__(512) void k_seg_decode(TileArgs p) {
 
   int item = blockIdx.x;
   const int stride = gridDim.x;
-  if (item < items) issue(item, g0, u0, a0);
+  if (item < items) issue(item, g0, u0, a0, sc0);
   while (item < items) {  // uniform
-    finish(item, g0, u0, a0, item + stride, g1, u1, a1);
+    finish(item, g0, u0, a0, sc0, item + stride, g1, u1, a1, sc1);
     item += stride;
     if (item >= items) break;
-    finish(item, g1, u1, a1, item + stride, g0, u0, a0);
+    finish(item, g1, u1, a1, sc1, item + stride, g0, u0, a0, sc0);
     item += stride;
   }
 }
@@ -162,11 +187,29 @@ bool seg_decode_fits(int N, int K, int epilogue, int64_t batch) {
 
 hipError_t launch_seg_decode(const TileArgs& a, int num_cu, hipStream_t st) {
   if (!seg_decode_fits(a.N, a.K, a.epilogue, a.batch) || !a.seg_offsets) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)num_cu), block(kSDW * 64);  // one persistent workgroup per CU
-  if (a.epilogue == 2)
-    hipLaunchKernelGGL(k_seg_decode<2>, grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL(k_seg_decode<1>, grid, block, 0, st, a);
+  const int steps = a.K / (kSDW * 64);
+  // persistent workgroups: two per CU when the register buffers of up to 4 steps per wave
+  // leave room for them (<= 128 VGPRs), else one
+  const dim3 grid((unsigned)(num_cu * (steps <= 4 ? 2 : 1))), block(kSDW * 64);
+#define WQ_SEG_CASE(S)                                                                         \
+  case S:                                                                                      \
+    if (a.epilogue == 2)                                                                       \
+      hipLaunchKernelGGL((k_seg_decode<2, S>), grid, block, 0, st, a);                         \
+    else                                                                                       \
+      hipLaunchKernelGGL((k_seg_decode<1, S>), grid, block, 0, st, a);                         \
+    break;
+  switch (steps) {
+    WQ_SEG_CASE(1)
+    WQ_SEG_CASE(2)
+    WQ_SEG_CASE(3)
+    WQ_SEG_CASE(4)
+    WQ_SEG_CASE(5)
+    WQ_SEG_CASE(6)
+    WQ_SEG_CASE(7)
+    WQ_SEG_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef WQ_SEG_CASE
   return hipGetLastError();
 }
 
