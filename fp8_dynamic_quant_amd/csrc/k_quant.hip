@@ -22,8 +22,8 @@ struct In;
 template <>
 struct In<uint16_t> {  // bf16
   static constexpr int EPC = 8;  // elements per 16-byte chunk
-  __device__ static void load(const uint16_t* p, float* v) {
-    uint4 u = *reinterpret_cast<const uint4*>(p);
+  __device__ static void load(const uint16_t* p, float* v) { unpack(*reinterpret_cast<const uint4*>(p), v); }
+  __device__ static void unpack(const uint4 u, float* v) {
     uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -35,9 +35,9 @@ struct In<uint16_t> {  // bf16
 template <>
 struct In<float> {
   static constexpr int EPC = 4;
-  __device__ static void load(const float* p, float* v) {
-    float4 u = *reinterpret_cast<const float4*>(p);
-    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+  __device__ static void load(const float* p, float* v) { unpack(*reinterpret_cast<const uint4*>(p), v); }
+  __device__ static void unpack(const uint4 u, float* v) {
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y); v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
   }
 };
 
@@ -100,16 +100,35 @@ __global__ __launch_bounds__(256) void k_dynamic_quant(const TIn* __restrict__ x
   int8_t* qr = xq + row * (int64_t)K;
 
   if constexpr (CH > 0) {
+    // Every chunk load (and, with RMSNorm, every gamma chunk) is issued before the first
+    // wait, and none sits under a branch: lanes past the row re-read its last chunk and
+    // their values are zeroed after the load.  (Loads under a per-lane branch made the
+    // compiler wait for each one before issuing the next.)
+    uint4 raw[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      raw[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)min(lane + 64 * i, C - 1) * EPC);
+    uint4 graw[RMS ? CH : 1];
+    if constexpr (RMS) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int c = min(lane + 64 * i, C - 1);
+        if constexpr (EPC == 8) {
+          graw[i] = *reinterpret_cast<const uint4*>(gamma + (int64_t)c * 8);
+        } else {
+          const uint2 g2 = *reinterpret_cast<const uint2*>(gamma + (int64_t)c * 4);
+          graw[i] = uint4{g2.x, g2.y, 0u, 0u};
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use
     float v[CH][EPC];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int c = lane + 64 * i;
-      if (c < C) {
-        In<TIn>::load(xr + (int64_t)c * EPC, v[i]);
-      } else {
+      const bool in = lane + 64 * i < C;
+      In<TIn>::unpack(raw[i], v[i]);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) v[i][e] = 0.0f;
-      }
+      for (int e = 0; e < EPC; ++e) v[i][e] = in ? v[i][e] : 0.0f;
     }
     if constexpr (RMS) {
       double ss = 0.0;
@@ -121,12 +140,12 @@ __global__ __launch_bounds__(256) void k_dynamic_quant(const TIn* __restrict__ x
       const float inv = rms_inv(ss, K, eps);
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
-        const int c = lane + 64 * i;
-        if (c < C) {
-          float g[EPC];
-          load_gamma<EPC>(gamma + (int64_t)c * EPC, g);
+        const bool in = lane + 64 * i < C;
+        const uint32_t gw[4] = {graw[i].x, graw[i].y, graw[i].z, graw[i].w};
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) v[i][e] = __fmul_rn(__fmul_rn(v[i][e], inv), g[e]);
+        for (int e = 0; e < EPC; ++e) {
+          const float g = (e & 1) ? __uint_as_float(gw[e >> 1] & 0xFFFF0000u) : __uint_as_float(gw[e >> 1] << 16);
+          v[i][e] = in ? __fmul_rn(__fmul_rn(v[i][e], inv), g) : 0.0f;
         }
       }
     }
