@@ -100,7 +100,9 @@ __device__ __forceinline__ uint2 quant8_bf16_exact(const uint4 u, float s) {
 
 }  // namespace
 
-template <int R, int CT>
+// PREQ: the rows arrive quantised (p.a int8 with p.a_scale, the decode GEMM of
+// wq_quant_matmul): the same kernel without the quantisation
+template <int R, int CT, bool PREQ>
 __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int slices, int rtiles) {
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -138,10 +140,17 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
   // a per-lane branch let the compiler wait for the first loads before issuing the rest,
   // which cost a second memory round trip).
   const int xl = min(lane, (KW >> 3) - 1);
-  uint4 xr[R];
+  uint4 xr[PREQ ? 1 : R];   // bf16 rows: 8 values per lane
+  uint2 xq8[PREQ ? R : 1];  // quantised rows: 8 codes per lane
+  float s_pre = 0.0f;       // quantised rows: lane r < R holds row r's scale
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    xr[r] = *reinterpret_cast<const uint4*>(p.x + (int64_t)(row0 + min(r, rows - 1)) * p.ldx + kbase + xl * 8);
+  for (int r = 0; r < R; ++r) {
+    if constexpr (PREQ)
+      xq8[r] = *reinterpret_cast<const uint2*>(p.a + (int64_t)(row0 + min(r, rows - 1)) * p.lda + kbase + xl * 8);
+    else
+      xr[r] = *reinterpret_cast<const uint4*>(p.x + (int64_t)(row0 + min(r, rows - 1)) * p.ldx + kbase + xl * 8);
+  }
+  if constexpr (PREQ) s_pre = p.a_scale[row0 + min(lane, rows - 1)];
   const float wsc_v = p.w_scale[min(n0 + min(t, nt - 1), N - 1)];
   v4i b[CT][kFMaxSteps];
 #pragma unroll
@@ -154,6 +163,13 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
     for (int j = 0; j < kFMaxSteps; ++j) b[ct][j] = *reinterpret_cast<const v4i*>(wcol + min(j, steps - 1) * 64);
   }
 
+  if constexpr (PREQ) {
+    // ---- the given codes into the wave's tile, the given scales into LDS ----------------
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < rows && xlane) *reinterpret_cast<uint2*>(tile + fswz(r, lane >> 1, KW) + (lane & 1) * 8) = xq8[r];
+    if (wv == 0 && lane < R) s_lds[lane] = s_pre;
+  } else {
   // ---- per-row absmax: in-wave DPP reduction, then across waves through LDS ---------------
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -205,6 +221,7 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
       bad &= bad - 1;
     }
   }
+  }  // quantisation
 
   // ---- MFMA over this wave's K range (the tile is private to the wave); MFMA rows past
   // the tile's rows repeat its last row and are not stored -----------------------------------
@@ -252,24 +269,25 @@ size_t fused_lds_bytes(int R, int CT, int K) {
   return (size_t)kFW * R * (K / kFW) + (size_t)kFW * CT * 4 * 64 * 4 + (size_t)R * kFW * 4 + (size_t)R * 4 + 32 * 4;
 }
 
-template <int R, int CT>
+template <int R, int CT, bool PREQ>
 hipError_t launch_fused_rt(const DecodeArgs& a, int nt, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_fused_decode<R, CT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_fused_decode<R, CT, PREQ>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const int slices = (a.N + nt - 1) / nt, rtiles = (a.M + R - 1) / R;
-  hipLaunchKernelGGL((k_fused_decode<R, CT>), dim3((unsigned)(slices * rtiles)), dim3(kFW * 64),
+  hipLaunchKernelGGL((k_fused_decode<R, CT, PREQ>), dim3((unsigned)(slices * rtiles)), dim3(kFW * 64),
                      fused_lds_bytes(R, CT, a.K), st, a, nt, slices, rtiles);
   return hipGetLastError();
 }
 
 template <int R>
 hipError_t launch_fused_r(const DecodeArgs& a, int nt, hipStream_t st) {
-  return nt > 16 ? launch_fused_rt<R, 2>(a, nt, st) : launch_fused_rt<R, 1>(a, nt, st);
+  if (a.x == nullptr) return nt > 16 ? launch_fused_rt<R, 2, true>(a, nt, st) : launch_fused_rt<R, 1, true>(a, nt, st);
+  return nt > 16 ? launch_fused_rt<R, 2, false>(a, nt, st) : launch_fused_rt<R, 1, false>(a, nt, st);
 }
 
 }  // namespace
@@ -279,7 +297,8 @@ bool fused_decode_fits(int M, int K) {
 }
 
 hipError_t launch_fused_decode(const DecodeArgs& a, int nt, int rows_per_wg, hipStream_t st) {
-  if (!fused_decode_fits(a.M, a.K) || a.x == nullptr || !(nt == 4 || nt == 8 || nt == 16 || nt == 32))
+  if (!fused_decode_fits(a.M, a.K) || (a.x == nullptr && (a.a == nullptr || a.a_scale == nullptr)) ||
+      !(nt == 4 || nt == 8 || nt == 16 || nt == 32))
     return hipErrorInvalidValue;
   switch (rows_per_wg) {
     case 1: return launch_fused_r<1>(a, nt, st);

@@ -114,6 +114,34 @@ int quant_split(const wq_ctx* c, int64_t M, int64_t K) {
   return S;
 }
 
+// Shape of the one-launch fused kernel: nt columns and r rows per workgroup.  Every
+// workgroup quantises its r rows (VALU time ~ r) and streams nt K weight bytes (the row
+// tiles of one column slice share them through their XCD's L2).  The cost of a shape is
+// the rounds of workgroups per CU times the per-workgroup time 4 r + nt: measured at
+// K = 4096, N = 1024 on 256 CUs, one row of quantisation costs about as much as four
+// columns of weights, and for every M in 1..64 the fastest shape is the one this picks.
+// Ties go to the smaller r (a smaller kernel instance: less code, fewer registers); r is
+// at most the power of two at or above M.
+// row_cost: a row's cost in columns (4 with the quantisation; the decode GEMM on given
+// codes passes 1 above M = 16)
+void fused_shape(const wq_ctx* c, int64_t M, int64_t N, int* nt, int* r, int row_cost = 4) {
+  int64_t best = -1;
+  for (int rr : {1, 2, 4, 8, 16}) {
+    if (c->fused_r > 0 ? rr != c->fused_r : rr >= 2 * M) continue;
+    for (int w : {4, 8, 16, 32}) {
+      if (c->fused_nt > 0 && w != c->fused_nt) continue;
+      const int64_t wgs = (N + w - 1) / w * ((M + rr - 1) / rr);
+      const int64_t rounds = (wgs + c->num_cu - 1) / c->num_cu;
+      const int64_t cost = rounds * (row_cost * std::min<int64_t>(rr, M) + w);
+      if (best < 0 || cost < best) {
+        best = cost;
+        *nt = w;
+        *r = rr;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -304,8 +332,22 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
     a.y = static_cast<uint16_t*>(d->y);
     a.ldy = d->ldy;
     a.acc_out = d->acc_out;
-    // M <= 4: dense dot4 rows beat the MFMA layout (measured on MI355X; at M = 8 the
-    // MFMA decode kernel is already faster)
+    // M > 2: the fused decode kernel without its quantisation, the given codes and scales
+    // going straight to its tiles (row tiles x column slices; at M <= 2 the dot4 GEMV below
+    // measured faster)
+    if (M > 2 && wq::fused_decode_fits((int)M, (int)K) && c->decode_nt == 0 && c->decode_mt == 0) {
+      // shape: the fused call's model up to M = 16; above, a row without quantisation
+      // costs about a column (both measured fastest at K = 4096, N = 1024)
+      int nt = 16, rr = 16;
+      fused_shape(c, M, N, &nt, &rr, M > 16 ? 1 : 4);
+      hipError_t e = wq::launch_fused_decode(a, nt, rr, st);
+      if (c->log)
+        std::fprintf(stderr, "[wq] quant_matmul int8 decode (fused kernel, given codes) M=%lld N=%lld K=%lld cols/wg=%d "
+                     "rows/wg=%d\n", (long long)M, (long long)N, (long long)K, nt, rr);
+      return status_of(e);
+    }
+    // other K.  M <= 4: dense dot4 rows beat the MFMA layout (measured on MI355X; at M = 8
+    // the MFMA decode kernel is already faster)
     if (M <= 4 && wq::gemv_fits((int)M, (int)K, false) && c->decode_nt == 0) {
       hipError_t e = wq::launch_gemv(a, st);
       if (c->log)
@@ -411,32 +453,6 @@ int wq_quant_matmul(wq_ctx* c, const wq_matmul_desc* d, void* stream) {
 }
 
 namespace {
-// Shape of the one-launch fused kernel: nt columns and r rows per workgroup.  Every
-// workgroup quantises its r rows (VALU time ~ r) and streams nt K weight bytes (the row
-// tiles of one column slice share them through their XCD's L2).  The cost of a shape is
-// the rounds of workgroups per CU times the per-workgroup time 4 r + nt: measured at
-// K = 4096, N = 1024 on 256 CUs, one row of quantisation costs about as much as four
-// columns of weights, and for every M in 1..64 the fastest shape is the one this picks.
-// Ties go to the smaller r (a smaller kernel instance: less code, fewer registers); r is
-// at most the power of two at or above M.
-void fused_shape(const wq_ctx* c, int64_t M, int64_t N, int* nt, int* r) {
-  int64_t best = -1;
-  for (int rr : {1, 2, 4, 8, 16}) {
-    if (c->fused_r > 0 ? rr != c->fused_r : rr >= 2 * M) continue;
-    for (int w : {4, 8, 16, 32}) {
-      if (c->fused_nt > 0 && w != c->fused_nt) continue;
-      const int64_t wgs = (N + w - 1) / w * ((M + rr - 1) / rr);
-      const int64_t rounds = (wgs + c->num_cu - 1) / c->num_cu;
-      const int64_t cost = rounds * (4 * std::min<int64_t>(rr, M) + w);
-      if (best < 0 || cost < best) {
-        best = cost;
-        *nt = w;
-        *r = rr;
-      }
-    }
-  }
-}
-
 // the launch sequence of the fused call (valid sizes, M >= 1): see wq_fused_path
 int fused_path(const wq_ctx* c, int64_t M, int64_t K) {
   if (M <= c->fused_gemv_max_m && wq::gemv_fits((int)M, (int)K, true)) return 1;

@@ -86,6 +86,15 @@ def test_fused_gemv_for_k_the_mfma_kernel_does_not_take(M, K, N):
     _check_linear(x, w, sw, fused=True)
 
 
+@pytest.mark.parametrize("M,K,N", [(33, 1040, 272), (64, 8192, 96), (7, 1552, 48), (2, 4112, 64)])
+def test_quant_matmul_decode_other_k(M, K, N):
+    # given codes at decode M with a K the fused kernel does not take (K % 512 != 0 or
+    # K > 4096): the decode GEMM kernel, or the dot4 GEMV at M <= 4
+    x = syn.activations((109, M, K), M, K, outlier_frac=0.005, outlier_mul=30.0)
+    w, sw = syn.int8_weights((110, N, K), N, K)
+    _check_linear(x, w, sw, fused=False)
+
+
 FUSED_SHAPES = [(r, nt) for r in (1, 2, 4, 8, 16) for nt in (4, 8, 16, 32)]
 
 
@@ -100,6 +109,7 @@ def test_every_fused_shape_gives_identical_bytes(R, NT):
         try:
             assert wq.wq_fused_path(M, K, N) == 2
             _check_linear(x, w, sw, fused=True)
+            _check_linear(x, w, sw, fused=False)  # the same kernel on the given codes
         finally:
             wq.set_fused_shape(DEV, 0, 0)
 
