@@ -206,42 +206,69 @@ __device__ __forceinline__ void tile_epilogue(const TileArgs& p, int m0, int row
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wm = wv >> 1, wn = wv & 1;
   const int N = p.N;
+  const int mb = m0 + wm * 64 + 4 * (lane >> 5);  // this lane's rows: mb + 32 i + 8 (e / 4) + e % 4
+  // Every scale this lane needs is loaded first, at clamped in-range indices, with no branch
+  // between the loads: a scale loaded next to each store made every store group wait for
+  // the stores before it.
+  float rs[2][16];
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rs[i][e] = p.a_scale[min(mb + i * 32 + 8 * (e >> 2) + (e & 3), row_hi - 1)];
+  }
+  float sw[2] = {1.0f, 1.0f}, sw2[2] = {0.0f, 0.0f};
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+      if constexpr (EPI == 2) {
+        const int I = N / 2;
+        sw[j] = wsc[min(n, I - 1)];
+        sw2[j] = wsc[min(n, I - 1) + I];
+      } else {
+        sw[j] = wsc[min(n, N - 1)];
+      }
+    }
+    // one wait for all of them, as a real s_waitcnt (vmcnt(0)) that the compiler's wait
+    // accounting sees: without it, the per-row store branches made it wait again before
+    // each scale's use, and so for every store issued before
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int n = n0 + wn * 64 + j * 32 + (lane & 31);
     if constexpr (EPI == 2) {
       const int I = N / 2;
       if (n >= I) continue;
-      const float swg = wsc[n], swu = wsc[n + I];
       float* H = reinterpret_cast<float*>(p.y);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int m = mb + i * 32 + 8 * (e >> 2) + (e & 3);
           if (m < row_hi) {
-            const float s = p.a_scale[m];
-            const float gv = __fmul_rn(__fmul_rn((float)acc[i][j][e], s), swg);
-            const float uv = __fmul_rn(__fmul_rn((float)acc2[i][j][e], s), swu);
+            const float s = rs[i][e];
+            const float gv = __fmul_rn(__fmul_rn((float)acc[i][j][e], s), sw[j]);
+            const float uv = __fmul_rn(__fmul_rn((float)acc2[i][j][e], s), sw2[j]);
             const float sg = __fdiv_rn(gv, __fadd_rn(1.0f, exp_fixed(-gv)));
             H[(int64_t)m * p.ldy + n] = __fmul_rn(sg, uv);
           }
         }
     } else {
       if (n >= N) continue;
-      const float sw = FP8 ? 1.0f : wsc[n];
       uint16_t* Y = reinterpret_cast<uint16_t*>(p.y) + (p.seg_offsets ? 0 : (int64_t)g * p.y_batch_stride);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int m = mb + i * 32 + 8 * (e >> 2) + (e & 3);
           if (m < row_hi) {
             uint16_t out;
             if constexpr (FP8) {
               out = (uint16_t)f32_to_bf16_rn(acc[i][j][e]);
             } else {
-              out = (uint16_t)f32_to_bf16_rn(__fmul_rn(__fmul_rn((float)acc[i][j][e], p.a_scale[m]), sw));
+              out = (uint16_t)f32_to_bf16_rn(__fmul_rn(__fmul_rn((float)acc[i][j][e], rs[i][e]), sw[j]));
               if (p.acc_out) p.acc_out[(int64_t)m * N + n] = acc[i][j][e];
             }
             Y[(int64_t)m * p.ldy + n] = out;
