@@ -78,6 +78,8 @@ __device__ __forceinline__ void wait_vm_slices(int n) {
   }
 }
 
+__device__ __forceinline__ void sc_store_now(float* dst, int t, float v) { dst[t] = v; }
+
 struct BigTiles {
   int tiles_m, tiles_n, per_xcd, nt;
   __device__ void tile(int lin, int& tm, int& tn) const {
@@ -92,6 +94,8 @@ struct BigTiles {
 
 __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt, int wgs_per_xcd) {
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
+  // the row (0..255) and column (256..511) scales of two tiles, by tile parity
+  __shared__ __attribute__((aligned(16))) float scl[2][512];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int wm = wv >> 2, wn = wv & 3;  // 2 x 4 waves of 128 x 64
   const int M = p.M, N = p.N, K = p.K;
@@ -129,6 +133,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
 
   const int ar = wm * 128 + (lane & 31), br = wn * 64 + (lane & 31);
   const int kh = lane >> 5;
+  // Each thread fetches one of the current tile's 512 scales with its first slice and
+  // stores it to LDS one slice later, after the slice wait has covered it, so the epilogue
+  // reads no global memory: a scale load there waited for the stores issued before it.
+  float scale_v = 0.0f;
+  auto load_scale = [&](int s) {
+    int m0, n0;
+    tile_of(s, m0, n0);
+    scale_v = t < 256 ? p.a_scale[min(m0 + t, M - 1)] : p.w_scale[min(n0 + t - 256, N - 1)];
+  };
   for (int s = 0; s < kStages - 1 && s < total; ++s) issue(s);
   for (int s = 0; s < total; ++s) {
     // wait for this wave's DMA of slice s while the later slices already issued (up to
@@ -141,6 +154,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
       wait_vm_slices(later);
     }
     __syncthreads();  // slice s is in LDS everywhere; the stage of slice s-1 is free
+    if (KT > 1 && s % KT == 1) scl[(s / KT) & 1][t] = scale_v;  // loaded with slice s - 1, now waited for
+    if (s % KT == 0) load_scale(s);
     if (s + kStages - 1 < total) issue(s + kStages - 1);
     const int8_t* sa = smem + (s % kStages) * kStageB;
     const int8_t* sb = sa + kSliceB;
@@ -175,21 +190,27 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
       int m0, n0;
       tile_of(s, m0, n0);
       const bool odd = lane & 1;
+      const float* sc = scl[(s / KT) & 1];
+      if (KT <= 2) {  // the scales were stored in this iteration (KT = 2) or are still in registers
+        if (KT == 1) sc_store_now(scl[(s / KT) & 1], t, scale_v);
+        __syncthreads();
+      }
       float swv[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-        swv[j] = p.w_scale[n < N ? n : N - 1];
-      }
+      for (int j = 0; j < 2; ++j) swv[j] = sc[256 + wn * 64 + j * 32 + (lane & 31)];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int mrow = m0 + wm * 128 + i * 32 + 4 * kh;
-        // row scales of the 16 rows this lane holds in the i-th 32-row block
+        // row scales of the 16 rows this lane holds in the i-th 32-row block: rows
+        // mrow + 8q + 0..3, four consecutive floats per q
         float rs[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = mrow + 8 * (e >> 2) + (e & 3);
-          rs[e] = p.a_scale[r < M ? r : M - 1];
+        for (int q = 0; q < 4; ++q) {
+          const float4 r4 = *reinterpret_cast<const float4*>(sc + (mrow - m0) + 8 * q);
+          rs[4 * q] = r4.x;
+          rs[4 * q + 1] = r4.y;
+          rs[4 * q + 2] = r4.z;
+          rs[4 * q + 3] = r4.w;
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {

@@ -95,6 +95,15 @@ def test_quant_matmul_decode_other_k(M, K, N):
     _check_linear(x, w, sw, fused=False)
 
 
+@pytest.mark.parametrize("M,K,N", [(260, 128, 272), (300, 256, 512), (512, 384, 256)])
+def test_prefill_short_k(M, K, N):
+    # the persistent 256 x 256 kernel with 1, 2 and 3 K slices per tile (its tile scales
+    # reach LDS one slice after the tile's first), ragged M and N
+    x = syn.activations((111, M, K), M, K, outlier_frac=0.01, outlier_mul=20.0)
+    w, sw = syn.int8_weights((112, N, K), N, K)
+    _check_linear(x, w, sw, fused=False)
+
+
 FUSED_SHAPES = [(r, nt) for r in (1, 2, 4, 8, 16) for nt in (4, 8, 16, 32)]
 
 
