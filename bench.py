@@ -425,7 +425,7 @@ def main():
                            "contraction_TOPS": round(c_ops / us_c / 1e6, 2)}
         rows["fp8_wo_a"] = {"workload": "X bf16 [T, 8, 4096] -> E4M3 + packed UE8M0 [8, 8, align4(T)]; "
                                         "out[T,g,:] = x_q[T,g,:] W_g^T, W_g E4M3 [1024, 4096], 128x128 pow2 scales",
-                            "kernels": "k_group_quant_fp8; k_fp8_decode (T <= 64), k_gemm_tile<FP8> (T > 64)", "by_T": fp8}
+                            "kernels": "k_group_quant_fp8; k_fp8_decode (T <= 16), k_fp8_decode32 (16 < T <= 64), k_gemm_tile<FP8> (T > 64)", "by_T": fp8}
         del wq8
 
         # ---- MoE block: T=256, hidden 4096, 256 experts of 2x2048, top-8 Zipf(1.1) ----------

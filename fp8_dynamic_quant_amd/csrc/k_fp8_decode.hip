@@ -18,6 +18,8 @@
 //    the weight byte is the exponent field of the f32 power-of-two block scale;
 //  * tokens go in tiles of 16 rows; the four waves' f32 16 x 16 tiles are summed in LDS in
 //    a fixed order and written as bf16.
+// Above 16 tokens every workgroup re-reads each token tile from L2, 64 times per group at
+// N = 1024; k_fp8_decode32 below halves that with 32 columns per workgroup.
 #include "wq_device.h"
 #include "wq_kernels.h"
 
@@ -135,6 +137,126 @@ __global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
       Y[(int64_t)row * p.ldy + n0 + (ln & 15)] = (uint16_t)f32_to_bf16_rn(v);
     }
   }
+}
+
+// Wider variant: 32 output columns (two 16-column MFMA tiles) per workgroup of 8 waves,
+// each wave owning K/8 and multiplying every activation fragment it loads into both column
+// tiles.  Half as many workgroups read each token tile from L2 as with 16 columns, and all
+// token tiles are in flight at once (at most 56 vector loads per wave: 16 for the weights,
+// 8 per token tile for the fragments and 2 for its packed scale words).
+template <int TPW>
+__global__ __launch_bounds__(512) void k_fp8_decode32(TileArgs p) {
+  __shared__ float red[8][TPW][2][4][64];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int T = p.M, N = p.N, K = p.K, g = blockIdx.y;
+  const int n0 = blockIdx.x * 32;
+  const int KT = K >> 7;
+  const int steps = KT >> 3;             // 128-deep blocks per wave (1..4)
+  const int kb0 = wv * steps;
+  const int cl = lane & 15, kq = lane >> 4;
+  const int PH = (KT + 3) >> 2;
+  const int32_t* xs_g = p.a_scale_packed + (int64_t)g * PH * p.a_scale_tokens;
+  const int8_t* A = p.a + (int64_t)g * p.a_batch_stride + kq * 32;
+  const int rt_lo = blockIdx.z * TPW;
+  const int w0 = kb0 >> 2;               // the wave's blocks touch packed words w0 and w0 + 1 at most
+
+  // ---- weights of both column tiles, 32 bytes per lane per block ----------------------------
+  v8i b[2][4];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int8_t* W = p.w + (int64_t)g * p.w_batch_stride + (int64_t)(n0 + ct * 16 + cl) * K + kq * 32;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int8_t* src = W + (int64_t)(kb0 + min(j, steps - 1)) * 128;
+      const v4i lo = *reinterpret_cast<const v4i*>(src);
+      const v4i hi = *reinterpret_cast<const v4i*>(src + 16);
+      b[ct][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+  // ---- every token tile's fragments and packed scale words --------------------------------
+  v8i a[TPW][4];
+  int32_t wd[TPW][2];
+#pragma unroll
+  for (int rt = 0; rt < TPW; ++rt) {
+    // rows past T read row T-1: they only feed output rows that are not stored
+    const int row = min((rt_lo + rt) * 16 + cl, T - 1);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) wd[rt][q] = xs_g[(int64_t)min(w0 + q, PH - 1) * p.a_scale_tokens + row];
+    const int8_t* arow = A + (int64_t)row * p.lda;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int8_t* src = arow + (int64_t)(kb0 + min(j, steps - 1)) * 128;
+      const v4i lo = *reinterpret_cast<const v4i*>(src);
+      const v4i hi = *reinterpret_cast<const v4i*>(src + 16);
+      a[rt][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- weight block-scale exponents: both column tiles lie in one 128-column block --------
+  const float* wsc = p.w_scale + ((int64_t)g * (N >> 7) + (n0 >> 7)) * KT + kb0;
+  uint32_t wsb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wsb[j] = __float_as_uint(wsc[min(j, steps - 1)]);
+  asm volatile("" : "+s"(wsb[0]), "+s"(wsb[1]), "+s"(wsb[2]), "+s"(wsb[3]));
+  int sbx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sbx[j] = (int)((wsb[j] >> 23) & 0xFF);
+
+  v4f acc[TPW][2];
+#pragma unroll
+  for (int rt = 0; rt < TPW; ++rt) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < steps) {  // uniform
+        const int kb = kb0 + j;
+        const int32_t w = (kb >> 2) == w0 ? wd[rt][0] : wd[rt][1];
+        const int sa = (w >> (8 * (kb & 3))) & 0xFF;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          acc[rt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[rt][j], b[ct][j], acc[rt][ct], 0, 0, 0, sa,
+                                                                         0, sbx[j]);
+      }
+    }
+  }
+
+  // ---- the eight waves' partial sums, in a fixed order, then bf16 ---------------------------
+#pragma unroll
+  for (int rt = 0; rt < TPW; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wv][rt][ct][i][lane] = acc[rt][ct][i];
+  __syncthreads();
+  uint16_t* Y = reinterpret_cast<uint16_t*>(p.y) + (int64_t)g * p.y_batch_stride;
+  for (int e = t; e < TPW * 2 * 4 * 64; e += 512) {
+    const int ln = e & 63, ri = e >> 6, i = ri & 3, ct = (ri >> 2) & 1, rt = ri >> 3;
+    const int row = (rt_lo + rt) * 16 + 4 * (ln >> 4) + i;  // MFMA 16x16 output: col = lane % 16, row = 4 (lane / 16) + i
+    if (row < T) {
+      float v = red[0][rt][ct][i][ln];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) v = __fadd_rn(v, red[w][rt][ct][i][ln]);
+      Y[(int64_t)row * p.ldy + n0 + ct * 16 + (ln & 15)] = (uint16_t)f32_to_bf16_rn(v);
+    }
+  }
+}
+
+bool fp8_decode32_fits(int T, int N, int K) {
+  return T > 16 && T <= 16 * kF8MaxRT && N % 32 == 0 && K % 1024 == 0 && K <= 4096;
+}
+
+hipError_t launch_fp8_decode32(const TileArgs& a, hipStream_t st) {
+  if (!fp8_decode32_fits(a.M, a.N, a.K)) return hipErrorInvalidValue;
+  const int rt = (a.M + 15) / 16;
+  const dim3 grid((unsigned)(a.N / 32), (unsigned)a.batch, 1);
+  switch (rt) {
+    case 2: hipLaunchKernelGGL(k_fp8_decode32<2>, grid, dim3(512), 0, st, a); break;
+    case 3: hipLaunchKernelGGL(k_fp8_decode32<3>, grid, dim3(512), 0, st, a); break;
+    default: hipLaunchKernelGGL(k_fp8_decode32<4>, grid, dim3(512), 0, st, a); break;
+  }
+  return hipGetLastError();
 }
 
 bool fp8_decode_fits(int T, int N, int K) {

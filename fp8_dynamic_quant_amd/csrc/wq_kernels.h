@@ -82,6 +82,11 @@ bool big_fits(int M, int N, int K, int64_t lda, int64_t ldy);
 // workgroup, grid (N / 16, G, ceil(ceil(T / 16) / that))
 hipError_t launch_fp8_decode(const TileArgs& a, int rt_per_wg, hipStream_t st);
 bool fp8_decode_fits(int T, int N, int K);
+// 32 output columns of one group per workgroup of 8 waves, all token tiles (16 < T <= 64,
+// K % 1024 == 0, K <= 4096, N % 32 == 0), grid (N / 32, G); at T <= 16 the 16-column
+// kernel is faster (one token tile: the activation re-reads it saves are few)
+hipError_t launch_fp8_decode32(const TileArgs& a, hipStream_t st);
+bool fp8_decode32_fits(int T, int N, int K);
 
 // FP8 group quant with packed UE8M0 scales (k_fp8.hip).
 hipError_t launch_group_quant_fp8(const uint16_t* x, int64_t T, int G, int D, uint8_t* xq, int32_t* xs,

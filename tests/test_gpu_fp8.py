@@ -153,6 +153,21 @@ def test_fp8_contraction_small_shapes_wide_codes(T, G, D, N):
     _check_contraction(payload, storage, eb, wq_codes, ws, y, bound_mult=4.0)
 
 
+@pytest.mark.parametrize("T,G,D,N", [(33, 2, 3072, 256), (48, 1, 1024, 384), (64, 2, 4096, 128), (20, 3, 2048, 512),
+                                     (17, 1, 1024, 128), (50, 1, 4096, 256)])
+def test_fp8_contraction_wide_decode_kernel(T, G, D, N):
+    """Shapes of the 32-column decode kernel (17 <= T <= 64, K % 1024 == 0, K <= 4096): two
+    to four token tiles with ragged ends, K ranges of one to four blocks per wave, and a wave's blocks
+    spanning two packed scale words (K = 3072)."""
+    x = syn.fp8_group_x(T, G=G, D=D, layout_variant=True)
+    payload, storage, eb = fg.group_quant_fp8_packed(x)
+    wq_codes, ws = syn.fp8_weights(11, G=G, N=N, D=D)
+    y = wq.wq_quant_matmul(dev(payload), dev(storage), dev(wq_codes), dev(ws), fp8_groups=G)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (T, G, N)
+    _check_contraction(payload, storage, eb, wq_codes, ws, y)
+
+
 def test_fp8_chain_gpu_quant_then_contraction():
     T, G, D, N = 64, 8, 4096, 1024
     x = syn.fp8_group_x(T, G=G, D=D)
