@@ -278,23 +278,27 @@ __device__ __forceinline__ void tile_epilogue(const TileArgs& p, int m0, int row
   }
 }
 
-// Dense or strided groups: one tile per workgroup (groups on blockIdx.y).
+// Dense or strided groups: one tile per workgroup, (group, tile) items on a 1-D grid.
 template <bool FP8>
 __global__ __launch_bounds__(256) void k_gemm_tile(TileArgs p, int tiles_m, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-  const int g = blockIdx.y;
-  const int8_t* A = p.a + (int64_t)g * p.a_batch_stride;
-  const int8_t* B = p.w + (int64_t)g * p.w_batch_stride;
-  // XCD-aware order: consecutive workgroups land on different XCDs (round robin), so each
-  // XCD gets a contiguous run of tile indices; within a run, tiles go in groups of
-  // kGroupM tile rows sweeping the tile columns, so the A rows and B columns a CU group
-  // works on at once stay in that XCD's L2
+  // XCD-aware order over all (group, tile) items: consecutive workgroups land on different
+  // XCDs (round robin), so each XCD gets a contiguous run of items, whole groups first
+  // (8 groups of 32 tiles: one group per XCD, whose L2 then fetches that group's
+  // activations and weights from HBM once); within a group, tiles go in groups of kGroupM
+  // tile rows sweeping the tile columns, so the A rows and B columns a CU group works on
+  // at once stay in that XCD's L2
   const int nt = tiles_m * tiles_n;
+  const int total = nt * p.batch;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, slot = bid >> 3;
-  const int per_xcd = (nt + 7) >> 3;
-  const int lin = xcd * per_xcd + slot;
-  if (lin >= nt) return;
+  const int per_xcd = (total + 7) >> 3;
+  const int item = xcd * per_xcd + slot;
+  if (slot >= per_xcd || item >= total) return;
+  const int g = item / nt;
+  const int lin = item - g * nt;
+  const int8_t* A = p.a + (int64_t)g * p.a_batch_stride;
+  const int8_t* B = p.w + (int64_t)g * p.w_batch_stride;
   const int group = lin / (kGroupM * tiles_n);
   const int gm0 = group * kGroupM;
   const int gsz = min(kGroupM, tiles_m - gm0);
@@ -388,7 +392,8 @@ hipError_t launch_gemm_tile(const TileArgs& a, bool fp8, hipStream_t st) {
   }
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int nt = tiles_m * tiles_n;
-  dim3 grid((unsigned)(((nt + 7) / 8) * 8), (unsigned)a.batch), block(256);
+  const int64_t total = (int64_t)nt * a.batch;
+  dim3 grid((unsigned)(((total + 7) / 8) * 8)), block(256);
   const size_t lds = fp8 ? (size_t)TileRing<true, false, kDenseStages>::kBytes
                           : (size_t)TileRing<false, false, kDenseStages>::kBytes;
   auto kfn = fp8 ? k_gemm_tile<true> : k_gemm_tile<false>;
