@@ -40,7 +40,7 @@ FP8_PEAK_TOPS = 5000.0
 SWEEP = (1, 2, 4, 7, 8, 16, 32, 64)
 K_A, N_A = 4096, 1024
 ROTATE_BYTES = 512 << 20
-ROOFLINE_KERNEL = "k_fused_decode"  # the one-launch fused kernel (wq_fused_path == 2), every <R, CT> instance
+ROOFLINE_KERNEL = "k_fused_decode"  # the one-launch fused kernel on fragment-order weights, every <R, CT> instance
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_fused_decode_wq_a.json")
 KERNEL_SOURCES = ("k_fused.hip", "wq_device.h", "wq_kernels.h")  # the roofline kernel and the headers it includes
 
@@ -196,6 +196,8 @@ def main():
     ys = {M: [torch.empty((M, N_A), dtype=torch.bfloat16, device=dev) for _ in range(R)] for M in SWEEP}
     paths = {M: wq.wq_fused_path(M, K_A, N_A) for M in SWEEP}
     roof_ms = [M for M in SWEEP if paths[M] == 2]
+    if roof_ms != list(SWEEP):
+        raise SystemExit(f"the packed fused call needs the one-launch MFMA path at every M; paths {paths}")
 
     def graph_len(steps):
         """Steps per captured graph: the largest divisor of `steps` not above R, so the
@@ -235,7 +237,15 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / (reps * n_per_graph)
 
+    # the weights as a deployment stores them: cast once at load time, untimed, into the
+    # fragment order the MFMA kernel reads (wq_pack_weight_i8), one packed copy per slot
+    wps = [wq.wq_pack_weight_i8(ws[r]) for r in range(R)]
+
     def fused_step(r, Ms=SWEEP):
+        for M in Ms:
+            wq.wq_fused_quant_matmul_packed(xs[M][r], wps[r], sws[r], N_A, y=ys[M][r])
+
+    def fused_plain_step(r, Ms=SWEEP):
         for M in Ms:
             wq.wq_fused_quant_matmul(xs[M][r], ws[r], sws[r], y=ys[M][r])
 
@@ -297,10 +307,11 @@ def main():
     from oracle.numerics import bf16_ulp_distance  # noqa: E402
 
     for M in (1, 8, 64):
-        y = wq.wq_fused_quant_matmul(xs[M][0], ws[0], sws[0])
         ref = il.linear_w8a8(x_host[M], w_host, sw_host)["y"]
-        got = y.view(torch.int16).cpu().numpy().view(np.uint16)
-        assert bf16_ulp_distance(got, ref).max() <= 1, "fused linear disagrees with the oracle"
+        for y in (wq.wq_fused_quant_matmul_packed(xs[M][0], wps[0], sws[0], N_A),
+                  wq.wq_fused_quant_matmul(xs[M][0], ws[0], sws[0])):
+            got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+            assert bf16_ulp_distance(got, ref).max() <= 1, "fused linear disagrees with the oracle"
 
     # ---- headline: fused decode linear over the sweep -------------------------------------
     G = graph_len(args.steps)
@@ -325,11 +336,15 @@ def main():
         gf = capture(lambda r, M=M: fused_step(r, (M,)), R)
         us_fused[M] = time_graph(gf, R, 4 * R, R)
         del gf
-        row = {"M": M, "path": wq.FUSED_PATHS[paths[M]], "us_fused": round(us_fused[M], 3)}
+        row = {"M": M, "path": wq.FUSED_PATHS[paths[M]] + ", fragment-order weights", "us_fused": round(us_fused[M], 3)}
         if not args.no_sweep:
             gs = capture(lambda r, M=M: standalone_step(r, (M,)), R)
             row["us_standalone_quant_plus_gemm"] = round(time_graph(gs, R, 4 * R, R), 3)
             del gs
+            # the same call on the plain [N, K] weights
+            gp = capture(lambda r, M=M: fused_plain_step(r, (M,)), R)
+            row["us_fused_plain_weights"] = round(time_graph(gp, R, 4 * R, R), 3)
+            del gp
         bf = fused_bytes(M)
         row.update({"fused_GBps": round(bf / us_fused[M] / 1e3, 1),
                     "fused_frac_hbm": round(bf / us_fused[M] / 1e3 / HBM_PEAK_GBS, 4),
@@ -368,7 +383,8 @@ def main():
                 traffic = None
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "kernel": ROOFLINE_KERNEL, "launches": f"one per fused call at M in {roof_ms} (K=4096, N=1024)",
+                    "kernel": ROOFLINE_KERNEL + "<R, CT, false, true> (fragment-order weights)",
+                    "launches": f"one per fused call at M in {roof_ms} (K=4096, N=1024)",
                     "bytes_per_launch_mean": round(b_sum / len(roof_ms)),
                     "us_per_launch_mean": round(t_sum / len(roof_ms), 3),
                     "us_per_launch": {str(M): round(us_fused[M], 3) for M in roof_ms}}
@@ -476,7 +492,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": "wq_a decode linear, fused quant+GEMM: X bf16 [M,4096] x W int8 [4096->1024], "
                                "M in 1,2,4,7,8,16,32,64",
-                   "K": K_A, "N": N_A, "M_sweep": list(SWEEP), "rotating_copies": R},
+                   "K": K_A, "N": N_A, "M_sweep": list(SWEEP), "rotating_copies": R,
+                   "weights": "int8, cast once at load (untimed) to the MFMA fragment order (wq_pack_weight_i8); "
+                              "plain [N, K] times in sweep[].us_fused_plain_weights"},
         "roofline": roofline,
         "sweep": sweep,
         "floors": floors,

@@ -70,6 +70,10 @@ EXPORTS = {
     "wq_moe_sort": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                    _c_void_p]),
     "wq_fused_path": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64]),
+    "wq_pack_weight_i8": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p]),
+    "wq_fused_quant_matmul_packed": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p,
+                                                    _i64, _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                                    _c_void_p]),
 }
 
 _LIB = None
@@ -257,6 +261,37 @@ def wq_fused_quant_matmul(x, w, w_scale, *, y=None, x_q_out=None, x_scale_out=No
                                      y.stride(0), _ptr(x_q_out), _ptr(x_scale_out), _ptr(acc_out),
                                      _stream(x.device))
     _check("wq_fused_quant_matmul", st)
+    return y
+
+
+def wq_pack_weight_i8(w, wp=None):
+    """int8 w [N, K] (unit stride along K) -> the same bytes in fragment order (wq.h), as a
+    flat int8 tensor of N*K bytes for wq_fused_quant_matmul_packed."""
+    if w.dim() != 2 or w.stride(1) != 1 or w.dtype != torch.int8:
+        raise ValueError("w must be int8 [N, K] with unit stride along K")
+    N, K = w.shape
+    if wp is None:
+        wp = torch.empty((N * K,), dtype=torch.int8, device=w.device)
+    ctx = context(w.device)
+    _check("wq_pack_weight_i8", lib().wq_pack_weight_i8(ctx.handle, _ptr(w), N, K, w.stride(0), _ptr(wp),
+                                                         _stream(w.device)))
+    return wp
+
+
+def wq_fused_quant_matmul_packed(x, wp, w_scale, N, *, y=None, x_q_out=None, x_scale_out=None, acc_out=None):
+    """x bf16 [M, K], wp from wq_pack_weight_i8 (N*K bytes), w_scale f32 [N] -> y bf16 [M, N]."""
+    if x.dim() != 2 or x.stride(1) != 1 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16 [M, K] with unit stride along K")
+    M, K = x.shape
+    if wp.numel() != N * K:
+        raise ValueError("wp must hold N*K bytes")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    ctx = context(x.device)
+    st = lib().wq_fused_quant_matmul_packed(ctx.handle, _ptr(x), M, K, x.stride(0), _ptr(wp), _ptr(w_scale), N,
+                                            _ptr(y), y.stride(0), _ptr(x_q_out), _ptr(x_scale_out), _ptr(acc_out),
+                                            _stream(x.device))
+    _check("wq_fused_quant_matmul_packed", st)
     return y
 
 

@@ -101,8 +101,11 @@ __device__ __forceinline__ uint2 quant8_bf16_exact(const uint4 u, float s) {
 }  // namespace
 
 // PREQ: the rows arrive quantised (p.a int8 with p.a_scale, the decode GEMM of
-// wq_quant_matmul): the same kernel without the quantisation
-template <int R, int CT, bool PREQ>
+// wq_quant_matmul): the same kernel without the quantisation.
+// PK: p.w holds the weights in fragment order (wq_pack_weight_i8): byte (n, k) at
+// ((k/64 * N/4 + n/4) * 4 + (k%64)/16) * 64 + (n%4) * 16 + k%16, so the 16 columns x 64 K
+// bytes of one MFMA B fragment are 1 KiB contiguous, in lane order.
+template <int R, int CT, bool PREQ, bool PK>
 __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int slices, int rtiles) {
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -158,9 +161,18 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
     // B column cl of tile ct is output column ct * 16 + cl; columns past nt or N read a
     // column in range and are not stored
     const int c = CT == 1 ? (cl & (nt - 1)) : ct * 16 + cl;
-    const int8_t* wcol = p.w + (int64_t)min(n0 + c, N - 1) * K + kbase + 16 * kg;
+    const int n = min(n0 + c, N - 1);
+    if constexpr (PK) {
+      // fragment j of this wave: K step kbase/64 + j, a (N/4) x 256-byte row of 4-column blocks
+      const int8_t* wfr = p.w + ((int64_t)(kbase >> 6) * (N >> 2) + (n >> 2)) * 256 + kg * 64 + (n & 3) * 16;
 #pragma unroll
-    for (int j = 0; j < kFMaxSteps; ++j) b[ct][j] = *reinterpret_cast<const v4i*>(wcol + min(j, steps - 1) * 64);
+      for (int j = 0; j < kFMaxSteps; ++j)
+        b[ct][j] = *reinterpret_cast<const v4i*>(wfr + (int64_t)min(j, steps - 1) * (N >> 2) * 256);
+    } else {
+      const int8_t* wcol = p.w + (int64_t)n * K + kbase + 16 * kg;
+#pragma unroll
+      for (int j = 0; j < kFMaxSteps; ++j) b[ct][j] = *reinterpret_cast<const v4i*>(wcol + min(j, steps - 1) * 64);
+    }
   }
 
   if constexpr (PREQ) {
@@ -269,25 +281,44 @@ size_t fused_lds_bytes(int R, int CT, int K) {
   return (size_t)kFW * R * (K / kFW) + (size_t)kFW * CT * 4 * 64 * 4 + (size_t)R * kFW * 4 + (size_t)R * 4 + 32 * 4;
 }
 
-template <int R, int CT, bool PREQ>
+template <int R, int CT, bool PREQ, bool PK>
 hipError_t launch_fused_rt(const DecodeArgs& a, int nt, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_fused_decode<R, CT, PREQ>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_fused_decode<R, CT, PREQ, PK>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const int slices = (a.N + nt - 1) / nt, rtiles = (a.M + R - 1) / R;
-  hipLaunchKernelGGL((k_fused_decode<R, CT, PREQ>), dim3((unsigned)(slices * rtiles)), dim3(kFW * 64),
+  hipLaunchKernelGGL((k_fused_decode<R, CT, PREQ, PK>), dim3((unsigned)(slices * rtiles)), dim3(kFW * 64),
                      fused_lds_bytes(R, CT, a.K), st, a, nt, slices, rtiles);
   return hipGetLastError();
 }
 
 template <int R>
-hipError_t launch_fused_r(const DecodeArgs& a, int nt, hipStream_t st) {
-  if (a.x == nullptr) return nt > 16 ? launch_fused_rt<R, 2, true>(a, nt, st) : launch_fused_rt<R, 1, true>(a, nt, st);
-  return nt > 16 ? launch_fused_rt<R, 2, false>(a, nt, st) : launch_fused_rt<R, 1, false>(a, nt, st);
+hipError_t launch_fused_r(const DecodeArgs& a, int nt, bool packed, hipStream_t st) {
+  if (a.x == nullptr)
+    return nt > 16 ? launch_fused_rt<R, 2, true, false>(a, nt, st) : launch_fused_rt<R, 1, true, false>(a, nt, st);
+  if (packed)
+    return nt > 16 ? launch_fused_rt<R, 2, false, true>(a, nt, st) : launch_fused_rt<R, 1, false, true>(a, nt, st);
+  return nt > 16 ? launch_fused_rt<R, 2, false, false>(a, nt, st) : launch_fused_rt<R, 1, false, false>(a, nt, st);
+}
+
+// fragment-order weights: thread i writes the i-th 16-byte piece of wp, read from row
+// n = 4 (i / 16 % (N/4)) + i % 4, bytes 64 (i / (4 N)) + 16 (i / 4 % 4) of w
+__global__ __launch_bounds__(256) void k_pack_weight_i8(const int8_t* __restrict__ w, int64_t ldw, int N, int K,
+                                                        int8_t* __restrict__ wp) {
+  const int64_t pieces = (int64_t)N * (K / 16);
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < pieces; i += (int64_t)gridDim.x * 256) {
+    const int c = (int)(i & 3), kg = (int)((i >> 2) & 3);
+    const int64_t blk = i >> 4;  // ks * (N/4) + nb4
+    const int nb4 = (int)(blk % (N >> 2));
+    const int64_t ks = blk / (N >> 2);
+    const int n = nb4 * 4 + c;
+    const int64_t k = ks * 64 + kg * 16;
+    *reinterpret_cast<uint4*>(wp + i * 16) = *reinterpret_cast<const uint4*>(w + (int64_t)n * ldw + k);
+  }
 }
 
 }  // namespace
@@ -296,18 +327,27 @@ bool fused_decode_fits(int M, int K) {
   return M >= 1 && M <= 64 && K % (kFW * 64) == 0 && K / kFW <= kFMaxKW;
 }
 
-hipError_t launch_fused_decode(const DecodeArgs& a, int nt, int rows_per_wg, hipStream_t st) {
+hipError_t launch_fused_decode(const DecodeArgs& a, int nt, int rows_per_wg, hipStream_t st, bool packed) {
   if (!fused_decode_fits(a.M, a.K) || (a.x == nullptr && (a.a == nullptr || a.a_scale == nullptr)) ||
-      !(nt == 4 || nt == 8 || nt == 16 || nt == 32))
+      !(nt == 4 || nt == 8 || nt == 16 || nt == 32) || (packed && (a.x == nullptr || a.N % 4 != 0)))
     return hipErrorInvalidValue;
   switch (rows_per_wg) {
-    case 1: return launch_fused_r<1>(a, nt, st);
-    case 2: return launch_fused_r<2>(a, nt, st);
-    case 4: return launch_fused_r<4>(a, nt, st);
-    case 8: return launch_fused_r<8>(a, nt, st);
-    case 16: return launch_fused_r<16>(a, nt, st);
+    case 1: return launch_fused_r<1>(a, nt, packed, st);
+    case 2: return launch_fused_r<2>(a, nt, packed, st);
+    case 4: return launch_fused_r<4>(a, nt, packed, st);
+    case 8: return launch_fused_r<8>(a, nt, packed, st);
+    case 16: return launch_fused_r<16>(a, nt, packed, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_pack_weight_i8(const int8_t* w, int64_t ldw, int N, int K, int8_t* wp, hipStream_t st) {
+  if (N % 4 != 0 || K % 64 != 0 || ldw < K || ldw % 16 != 0) return hipErrorInvalidValue;
+  const int64_t pieces = (int64_t)N * (K / 16);
+  if (pieces == 0) return hipSuccess;
+  const int64_t blocks = min((pieces + 255) / 256, (int64_t)65536);
+  hipLaunchKernelGGL(k_pack_weight_i8, dim3((unsigned)blocks), dim3(256), 0, st, w, ldw, N, K, wp);
+  return hipGetLastError();
 }
 
 }  // namespace wq

@@ -208,6 +208,28 @@ int wq_fused_quant_matmul(wq_ctx* ctx, const void* x, int64_t M, int64_t K, int6
  * requires).  Host only: no device work. */
 int wq_fused_path(const wq_ctx* ctx, int64_t M, int64_t K, int64_t N);
 
+/* ---- weight pre-pack (fragment order) ------------------------------------------------
+ * Section 四 of the W8A8 article: the weights are cast once at load time into the layout
+ * the matrix unit reads (FRACTAL_NZ there).  The gfx950 form here is fragment order: for
+ * the int8 weight w [N, K] (row stride ldw bytes), byte (n, k) goes to
+ *   wp[((k/64 * N/4 + n/4) * 4 + (k%64)/16) * 64 + (n%4) * 16 + k%16],
+ * so for each 64-deep K step the 4-column blocks follow one another, each 256 bytes as
+ * [K quarter 0..3][column 0..3][16 bytes], and the 16 columns x 64 K bytes of one
+ * v_mfma_i32_16x16x64_i8 B operand are 1 KiB contiguous in lane order.  wp: int8, N*K
+ * bytes, caller-allocated, 16-byte aligned; w 16-byte aligned, ldw % 16 == 0, ldw >= K.
+ * N % 16 == 0, K % 64 == 0 (else WQ_ERR_SHAPE).  One device-side permutation on `stream`;
+ * w and wp must not overlap. */
+int wq_pack_weight_i8(wq_ctx* ctx, const int8_t* w, int64_t N, int64_t K, int64_t ldw, int8_t* wp,
+                      void* stream);
+
+/* wq_fused_quant_matmul with the weights in fragment order (wp from wq_pack_weight_i8),
+ * same arguments otherwise and bit-identical outputs.  Only the one-launch MFMA path:
+ * 1 <= M <= 64 (and M <= WQ_FUSED_MAX_M), K % 512 == 0, K <= 4096, N % 16 == 0; other
+ * sizes give WQ_ERR_SHAPE (M = 0 returns WQ_OK with nothing launched). */
+int wq_fused_quant_matmul_packed(wq_ctx* ctx, const void* x, int64_t M, int64_t K, int64_t ldx,
+                                 const int8_t* wp, const float* w_scale, int64_t N, void* y, int64_t ldy,
+                                 int8_t* x_q_out, float* x_scale_out, int32_t* acc_out, void* stream);
+
 /* ---- expert sort (MoE) ---------------------------------------------------------------
  * "DeepSeek V4 950" section 3.2: sort the (token, slot) pairs by expert id before the
  * gather so each expert's rows are contiguous.  topk_ids: int32 [T, topk], values in
