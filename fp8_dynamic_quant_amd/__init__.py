@@ -27,6 +27,7 @@ WQ_OK = 0
 WQ_IN_BF16, WQ_IN_F32 = 1, 2
 WQ_PAYLOAD_INT8, WQ_PAYLOAD_FP8_E4M3 = 1, 2
 WQ_EPI_BF16, WQ_EPI_SWIGLU_F32 = 1, 2
+WQ_LAYOUT_PLAIN, WQ_LAYOUT_FRAGMENT = 0, 1
 
 _c_void_p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -49,6 +50,7 @@ class MatmulDesc(ctypes.Structure):
         ("b_scale", _c_void_p),
         ("y", _c_void_p), ("ldy", _i64), ("y_batch_stride", _i64),
         ("acc_out", _c_void_p),
+        ("b_layout", ctypes.c_int32),
     ]
 
 
@@ -209,12 +211,15 @@ def wq_group_quant_fp8_ue8m0(x: torch.Tensor, x_q: torch.Tensor | None = None, s
 
 
 def wq_quant_matmul(a, a_scale, b, b_scale, *, y=None, acc_out=None, seg_offsets=None,
-                    epilogue=WQ_EPI_BF16, fp8_groups=None, a_scale_tokens=0):
+                    epilogue=WQ_EPI_BF16, fp8_groups=None, a_scale_tokens=0, b_fragment=False):
     """INT8: a int8 [M, K] (row stride a.stride(0)), a_scale f32 [M], b int8 [N, K] (or
     [E, N, K] with seg_offsets int64 [E+1]), b_scale f32 [N] (or [E, N]) -> y.
     FP8 (fp8_groups=G): a uint8 [M, G, K], a_scale = packed storage [G, PH, TA],
-    b uint8 [G, N, K], b_scale f32 [G, N/128, K/128] -> y bf16 [M, G, N]."""
+    b uint8 [G, N, K], b_scale f32 [G, N/128, K/128] -> y bf16 [M, G, N].
+    b_fragment: INT8 expert weights [E, N, K] cast per expert by wq_pack_weight_i8 (same
+    shape and strides; segments only)."""
     d = MatmulDesc()
+    d.b_layout = WQ_LAYOUT_FRAGMENT if b_fragment else WQ_LAYOUT_PLAIN
     dev = a.device
     if fp8_groups is not None:
         G = fp8_groups
@@ -266,7 +271,16 @@ def wq_fused_quant_matmul(x, w, w_scale, *, y=None, x_q_out=None, x_scale_out=No
 
 def wq_pack_weight_i8(w, wp=None):
     """int8 w [N, K] (unit stride along K) -> the same bytes in fragment order (wq.h), as a
-    flat int8 tensor of N*K bytes for wq_fused_quant_matmul_packed."""
+    flat int8 tensor of N*K bytes for wq_fused_quant_matmul_packed.  For expert weights
+    [E, N, K] (contiguous) each expert is cast in place of its own [N, K] block: the result
+    has w's shape, for wq_quant_matmul(..., seg_offsets=..., b_fragment=True)."""
+    if w.dim() == 3:
+        if not w.is_contiguous() or w.dtype != torch.int8:
+            raise ValueError("expert weights must be contiguous int8 [E, N, K]")
+        out = torch.empty_like(w) if wp is None else wp
+        for e in range(w.shape[0]):
+            wq_pack_weight_i8(w[e], out[e].view(-1))
+        return out
     if w.dim() != 2 or w.stride(1) != 1 or w.dtype != torch.int8:
         raise ValueError("w must be int8 [N, K] with unit stride along K")
     N, K = w.shape

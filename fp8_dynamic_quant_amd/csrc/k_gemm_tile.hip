@@ -66,8 +66,11 @@ __device__ __forceinline__ int tswz(int r, int c) { return r * kBK + ((c ^ tswz_
 
 // DMA one 128-row x 128-byte slice: rows [r0, r0+128) of `src` (row stride ld bytes,
 // clamped to < rows), bytes [k0, k0+128); lands swizzled at `dst`
+// frag_n > 0: src holds INT8 weights in the fragment order of launch_pack_weight_i8 for
+// N = frag_n (the rows here are its columns): chunk c (bytes 16c.. of the slice at k0) of
+// row n sits at ((k0/64 + c/4) N/4 + n/4) 256 + 64 (c%4) + 16 (n%4)
 __device__ __forceinline__ void dma_slice(const int8_t* src, int64_t ld, int r0, int rows, int k0, int8_t* dst,
-                                          int wv, int lane) {
+                                          int wv, int lane, int frag_n = 0) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int pos = (wv * 4 + i) * 64 + lane;  // 16-byte position in the slice, 0..1023
@@ -75,7 +78,10 @@ __device__ __forceinline__ void dma_slice(const int8_t* src, int64_t ld, int r0,
     const int c = pc ^ tswz_of(r);
     int gr = r0 + r;
     gr = gr < rows ? gr : rows - 1;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + (int64_t)gr * ld + k0 + c * 16),
+    const int64_t off = frag_n > 0 ? ((int64_t)((k0 >> 6) + (c >> 2)) * (frag_n >> 2) + (gr >> 2)) * 256 +
+                                         (c & 3) * 64 + (gr & 3) * 16
+                                   : (int64_t)gr * ld + k0 + c * 16;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + off),
                                      (lds_ptr_t)(dst + (wv * 4 + i) * 1024), 16, 0, 0);
   }
 }
@@ -115,8 +121,9 @@ __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, c
   auto issue = [&](int kt) {
     int8_t* st = smem + (kt % Ring::kStages) * Ring::kStageB;
     dma_slice(A, p.lda, m0, row_hi, kt * kBK, st, wv, lane);
-    dma_slice(B, K, n0, N, kt * kBK, st + kSlice, wv, lane);
-    if constexpr (DUAL) dma_slice(B, K, n0 + dual_off, N, kt * kBK, st + 2 * kSlice, wv, lane);
+    const int frag_n = (!FP8 && p.b_frag) ? N : 0;
+    dma_slice(B, K, n0, N, kt * kBK, st + kSlice, wv, lane, frag_n);
+    if constexpr (DUAL) dma_slice(B, K, n0 + dual_off, N, kt * kBK, st + 2 * kSlice, wv, lane, frag_n);
     if constexpr (FP8) {
       const int r = min(m0 + wv * 32 + (lane & 31), row_hi - 1);
       const void* src = lane == 32 ? reinterpret_cast<const void*>(ws_g + kt)

@@ -31,7 +31,9 @@ constexpr int kSDMaxSteps = 8;    // 64-deep K steps per wave: K <= 4096
 constexpr int kSDMaxExperts = 4096;
 }  // namespace
 
-template <int EPI, int STEPS>
+// PK: each expert's weights in fragment order (launch_pack_weight_i8): the 16 columns x 64
+// K bytes of one B operand are then 1 KiB contiguous
+template <int EPI, int STEPS, bool PK>
 __global__ __launch_bounds__(512) void k_seg_decode(TileArgs p) {
   __shared__ int exp_list[kSDMaxExperts];  // listed expert: id | rows << 16
   __shared__ int exp_row0[kSDMaxExperts];  // its first row
@@ -103,13 +105,26 @@ __global__ __launch_bounds__(512) void k_seg_decode(TileArgs p) {
   float sc0[3], sc1[3];  // s_m, sw_n (gate), sw_n (up)
   auto issue = [&](int item, v4i (&bg)[STEPS], v4i (&bu)[STEPS], v4i (&a)[STEPS], float (&sc)[3]) {
     const Item it = item_of(item);
-    const int8_t* W = p.w + (int64_t)it.e * p.w_batch_stride + kbase + kg * 16;
     // rows past the segment read its last row: they only feed output rows not stored
     const int8_t* arow = p.a + (int64_t)(it.row0 + min(cl, it.rows - 1)) * p.lda + kbase + kg * 16;
+    if constexpr (PK) {
+      // byte (n, k) at ((k/64 * N/4 + n/4) * 4 + (k%64)/16) * 64 + (n%4) * 16 + k%16
+      const int8_t* We = p.w + (int64_t)it.e * p.w_batch_stride + (int64_t)(kbase >> 6) * (N >> 2) * 256 + kg * 64;
+      const int ngt = it.n0 + cl, nup = col2 + it.n0 + cl;
+      const int8_t* Wg = We + (ngt >> 2) * 256 + (ngt & 3) * 16;
+      const int8_t* Wu = We + (nup >> 2) * 256 + (nup & 3) * 16;
 #pragma unroll
-    for (int j = 0; j < STEPS; ++j) {
-      bg[j] = *reinterpret_cast<const v4i*>(W + (int64_t)(it.n0 + cl) * K + j * 64);
-      bu[j] = *reinterpret_cast<const v4i*>(W + (int64_t)(col2 + it.n0 + cl) * K + j * 64);
+      for (int j = 0; j < STEPS; ++j) {
+        bg[j] = *reinterpret_cast<const v4i*>(Wg + (int64_t)j * N * 64);
+        bu[j] = *reinterpret_cast<const v4i*>(Wu + (int64_t)j * N * 64);
+      }
+    } else {
+      const int8_t* W = p.w + (int64_t)it.e * p.w_batch_stride + kbase + kg * 16;
+#pragma unroll
+      for (int j = 0; j < STEPS; ++j) {
+        bg[j] = *reinterpret_cast<const v4i*>(W + (int64_t)(it.n0 + cl) * K + j * 64);
+        bu[j] = *reinterpret_cast<const v4i*>(W + (int64_t)(col2 + it.n0 + cl) * K + j * 64);
+      }
     }
 #pragma unroll
     for (int j = 0; j < STEPS; ++j) a[j] = *reinterpret_cast<const v4i*>(arow + j * 64);
@@ -193,10 +208,14 @@ hipError_t launch_seg_decode(const TileArgs& a, int num_cu, hipStream_t st) {
   const dim3 grid((unsigned)(num_cu * (steps <= 4 ? 2 : 1))), block(kSDW * 64);
 #define WQ_SEG_CASE(S)                                                                         \
   case S:                                                                                      \
-    if (a.epilogue == 2)                                                                       \
-      hipLaunchKernelGGL((k_seg_decode<2, S>), grid, block, 0, st, a);                         \
+    if (a.epilogue == 2 && a.b_frag)                                                           \
+      hipLaunchKernelGGL((k_seg_decode<2, S, true>), grid, block, 0, st, a);                   \
+    else if (a.epilogue == 2)                                                                  \
+      hipLaunchKernelGGL((k_seg_decode<2, S, false>), grid, block, 0, st, a);                  \
+    else if (a.b_frag)                                                                         \
+      hipLaunchKernelGGL((k_seg_decode<1, S, true>), grid, block, 0, st, a);                   \
     else                                                                                       \
-      hipLaunchKernelGGL((k_seg_decode<1, S>), grid, block, 0, st, a);                         \
+      hipLaunchKernelGGL((k_seg_decode<1, S, false>), grid, block, 0, st, a);                  \
     break;
   switch (steps) {
     WQ_SEG_CASE(1)

@@ -287,6 +287,8 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   if (!al16(d->a) || !al16(d->b) || !al16(d->y) || !al16(d->acc_out) || d->lda % 16 != 0 || (d->ldy * ysz) % 16 != 0)
     return WQ_ERR_ALIGN;
   if (d->seg_offsets == nullptr && d->batch != 1) return WQ_ERR_UNSUPPORTED;
+  // fragment-order weights: expert segments here (dense calls: wq_fused_quant_matmul_packed)
+  if (d->b_layout == WQ_LAYOUT_FRAGMENT && (d->seg_offsets == nullptr || K % 64 != 0)) return WQ_ERR_UNSUPPORTED;
   if (d->seg_offsets != nullptr) {
     // expert segments: persistent 128x128 tiles over the non-empty (expert, row tile) pairs
     if (!wq::tile_fits((int)K) || d->acc_out) return WQ_ERR_UNSUPPORTED;
@@ -309,6 +311,7 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
     t.ldy = d->ldy;
     t.seg_offsets = d->seg_offsets;
     t.batch = (int)d->batch;
+    t.b_frag = d->b_layout == WQ_LAYOUT_FRAGMENT ? 1 : 0;
     // experts with few rows stream their weights through the 16-column kernel; the tiled
     // kernel takes the rest (both read the offsets on the device and skip the other set)
     const bool small = c->seg_small && wq::seg_decode_fits((int)N, (int)K, d->epilogue, d->batch);
@@ -458,6 +461,8 @@ int wq_quant_matmul(wq_ctx* c, const wq_matmul_desc* d, void* stream) {
   if (d->M < 0 || d->N <= 0 || d->K <= 0 || d->batch < 1) return WQ_ERR_SHAPE;
   if (d->M > (int64_t)1 << 30 || d->N > (int64_t)1 << 30) return WQ_ERR_SHAPE;
   if (d->epilogue != WQ_EPI_BF16 && d->epilogue != WQ_EPI_SWIGLU_F32) return WQ_ERR_SHAPE;
+  if (d->b_layout != WQ_LAYOUT_PLAIN && d->b_layout != WQ_LAYOUT_FRAGMENT) return WQ_ERR_SHAPE;
+  if (d->b_layout == WQ_LAYOUT_FRAGMENT && d->payload != WQ_PAYLOAD_INT8) return WQ_ERR_UNSUPPORTED;
   if (d->M == 0) return WQ_OK;
   DeviceGuard g(c->device);
   hipStream_t st = static_cast<hipStream_t>(stream);

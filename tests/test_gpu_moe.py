@@ -48,23 +48,28 @@ def test_rmsnorm_quant_gather(T, H):
     assert np.array_equal(host(q), q_ref)
 
 
-def _run_block_gpu(d, E):
+def _run_block_gpu(d, E, frag=False):
     ids_d = dev(d["ids"])
     perm, row_token, offsets = wq.wq_moe_sort(ids_d, E)
     q1, s1 = wq.wq_dynamic_quant(bf16_dev(d["h"]), rms_gamma=bf16_dev(d["gamma"]), row_index=row_token)
     w13, sw13, w2, sw2 = d["w13_d"], d["sw13_d"], d["w2_d"], d["sw2_d"]
-    hmid = wq.wq_quant_matmul(q1, s1, w13, sw13, seg_offsets=offsets, epilogue=wq.WQ_EPI_SWIGLU_F32)
+    if frag:
+        w13, w2 = wq.wq_pack_weight_i8(w13), wq.wq_pack_weight_i8(w2)
+    hmid = wq.wq_quant_matmul(q1, s1, w13, sw13, seg_offsets=offsets, epilogue=wq.WQ_EPI_SWIGLU_F32,
+                              b_fragment=frag)
     q2, s2 = wq.wq_dynamic_quant(hmid)
-    y = wq.wq_quant_matmul(q2, s2, w2, sw2, seg_offsets=offsets)
+    y = wq.wq_quant_matmul(q2, s2, w2, sw2, seg_offsets=offsets, b_fragment=frag)
     torch.cuda.synchronize()
     return dict(perm=perm, offsets=offsets, q1=q1, s1=s1, h=hmid, q2=q2, s2=s2, y=y)
 
 
-@pytest.mark.parametrize("T,H,I,E,topk", [(32, 256, 128, 8, 2), (64, 1024, 512, 32, 8), (300, 512, 256, 4, 2)])
-def test_moe_block_against_oracle(T, H, I, E, topk):
+@pytest.mark.parametrize("T,H,I,E,topk,frag", [(32, 256, 128, 8, 2, False), (64, 1024, 512, 32, 8, False),
+                                              (300, 512, 256, 4, 2, False), (64, 1024, 512, 32, 8, True),
+                                              (300, 512, 256, 4, 2, True)])
+def test_moe_block_against_oracle(T, H, I, E, topk, frag):
     d = syn.moe_inputs(seed=T, T=T, H=H, I=I, E=E, TOPK=topk)
     d.update(w13_d=dev(d["w13"]), sw13_d=dev(d["sw13"]), w2_d=dev(d["w2"]), sw2_d=dev(d["sw2"]))
-    g = _run_block_gpu(d, E)
+    g = _run_block_gpu(d, E, frag)
     r = moe.moe_block(d["h"], d["gamma"], d["ids"], d["w13"], d["sw13"], d["w2"], d["sw2"], keep=True)
     assert_same("perm", host(g["perm"]), r["perm"])
     assert_same("offsets", host(g["offsets"]), r["offsets"])
@@ -116,11 +121,13 @@ def test_moe_block_full_size_sampled_experts():
         assert nm.bf16_ulp_distance(host_bf16_bits(g["y"][lo:hi]), y).max() <= 1
 
 
+@pytest.mark.parametrize("frag", [False, True])
 @pytest.mark.parametrize("epi", ["bf16", "swiglu"])
-def test_segments_across_the_small_expert_boundary(epi):
+def test_segments_across_the_small_expert_boundary(epi, frag):
     """Expert row counts on both sides of the 16-row split between the weight-streaming
     kernel and the tiled one (0, 1, 15, 16, 17, 31, 32, 33, 129 rows), K = 1024 so both
-    kernels take part; every expert's rows against the oracle's dense per-expert product."""
+    kernels take part; every expert's rows against the oracle's dense per-expert product.
+    frag: the expert weights cast to fragment order (both kernels read that layout)."""
     counts = np.array([0, 1, 15, 16, 17, 31, 32, 33, 129], np.int64)
     E, K, N = counts.size, 1024, 512
     M = int(counts.sum())
@@ -131,10 +138,12 @@ def test_segments_across_the_small_expert_boundary(epi):
     sw = np.empty((E, N), np.float32)
     for e in range(E):
         w[e], sw[e] = syn.int8_weights((63, e), N, K)
+    wd = wq.wq_pack_weight_i8(dev(w)) if frag else dev(w)
     if epi == "bf16":
-        y = wq.wq_quant_matmul(dev(q), dev(s), dev(w), dev(sw), seg_offsets=dev(offsets))
+        y = wq.wq_quant_matmul(dev(q), dev(s), wd, dev(sw), seg_offsets=dev(offsets), b_fragment=frag)
     else:
-        y = wq.wq_quant_matmul(dev(q), dev(s), dev(w), dev(sw), seg_offsets=dev(offsets), epilogue=wq.WQ_EPI_SWIGLU_F32)
+        y = wq.wq_quant_matmul(dev(q), dev(s), wd, dev(sw), seg_offsets=dev(offsets), epilogue=wq.WQ_EPI_SWIGLU_F32,
+                               b_fragment=frag)
     torch.cuda.synchronize()
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
