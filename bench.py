@@ -327,9 +327,10 @@ def main():
     xsc = {M: [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(R)] for M in SWEEP}
 
     def standalone_step(r, Ms=SWEEP):
+        # the two-launch form on the same fragment-order weights as the headline
         for M in Ms:
             wq.wq_dynamic_quant(xs[M][r], x_q=xq[M][r], x_scale=xsc[M][r])
-            wq.wq_quant_matmul(xq[M][r], xsc[M][r], ws[r], sws[r], y=ys[M][r])
+            wq.wq_quant_matmul(xq[M][r], xsc[M][r], wps[r], sws[r], y=ys[M][r], b_fragment=True, n=N_A)
 
     sweep, us_fused = [], {}
     for M in SWEEP:

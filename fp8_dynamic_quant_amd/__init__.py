@@ -211,13 +211,14 @@ def wq_group_quant_fp8_ue8m0(x: torch.Tensor, x_q: torch.Tensor | None = None, s
 
 
 def wq_quant_matmul(a, a_scale, b, b_scale, *, y=None, acc_out=None, seg_offsets=None,
-                    epilogue=WQ_EPI_BF16, fp8_groups=None, a_scale_tokens=0, b_fragment=False):
+                    epilogue=WQ_EPI_BF16, fp8_groups=None, a_scale_tokens=0, b_fragment=False, n=None):
     """INT8: a int8 [M, K] (row stride a.stride(0)), a_scale f32 [M], b int8 [N, K] (or
     [E, N, K] with seg_offsets int64 [E+1]), b_scale f32 [N] (or [E, N]) -> y.
     FP8 (fp8_groups=G): a uint8 [M, G, K], a_scale = packed storage [G, PH, TA],
     b uint8 [G, N, K], b_scale f32 [G, N/128, K/128] -> y bf16 [M, G, N].
-    b_fragment: INT8 expert weights [E, N, K] cast per expert by wq_pack_weight_i8 (same
-    shape and strides; segments only)."""
+    b_fragment: INT8 weights cast by wq_pack_weight_i8: expert weights [E, N, K] (same shape
+    and strides) with seg_offsets, or a dense [N, K] cast (flat N*K bytes; give n = N) at
+    M <= 64."""
     d = MatmulDesc()
     d.b_layout = WQ_LAYOUT_FRAGMENT if b_fragment else WQ_LAYOUT_PLAIN
     dev = a.device
@@ -235,7 +236,12 @@ def wq_quant_matmul(a, a_scale, b, b_scale, *, y=None, acc_out=None, seg_offsets
         d.y, d.ldy, d.y_batch_stride = _ptr(y), y.stride(0), y.stride(1)
     else:
         M, K = a.shape
-        N = b.shape[-2]
+        if b.dim() == 1:
+            if not b_fragment or n is None:
+                raise ValueError("a flat b is a fragment-order cast: pass b_fragment=True and n")
+            N = n
+        else:
+            N = b.shape[-2]
         batch = b.shape[0] if b.dim() == 3 else 1
         ncols = N // 2 if epilogue == WQ_EPI_SWIGLU_F32 else N
         if y is None:

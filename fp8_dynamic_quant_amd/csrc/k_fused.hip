@@ -298,6 +298,8 @@ hipError_t launch_fused_rt(const DecodeArgs& a, int nt, hipStream_t st) {
 
 template <int R>
 hipError_t launch_fused_r(const DecodeArgs& a, int nt, bool packed, hipStream_t st) {
+  if (a.x == nullptr && packed)
+    return nt > 16 ? launch_fused_rt<R, 2, true, true>(a, nt, st) : launch_fused_rt<R, 1, true, true>(a, nt, st);
   if (a.x == nullptr)
     return nt > 16 ? launch_fused_rt<R, 2, true, false>(a, nt, st) : launch_fused_rt<R, 1, true, false>(a, nt, st);
   if (packed)
@@ -329,7 +331,7 @@ bool fused_decode_fits(int M, int K) {
 
 hipError_t launch_fused_decode(const DecodeArgs& a, int nt, int rows_per_wg, hipStream_t st, bool packed) {
   if (!fused_decode_fits(a.M, a.K) || (a.x == nullptr && (a.a == nullptr || a.a_scale == nullptr)) ||
-      !(nt == 4 || nt == 8 || nt == 16 || nt == 32) || (packed && (a.x == nullptr || a.N % 4 != 0)))
+      !(nt == 4 || nt == 8 || nt == 16 || nt == 32) || (packed && a.N % 4 != 0))
     return hipErrorInvalidValue;
   switch (rows_per_wg) {
     case 1: return launch_fused_r<1>(a, nt, packed, st);

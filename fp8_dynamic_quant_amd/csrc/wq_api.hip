@@ -287,8 +287,14 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   if (!al16(d->a) || !al16(d->b) || !al16(d->y) || !al16(d->acc_out) || d->lda % 16 != 0 || (d->ldy * ysz) % 16 != 0)
     return WQ_ERR_ALIGN;
   if (d->seg_offsets == nullptr && d->batch != 1) return WQ_ERR_UNSUPPORTED;
-  // fragment-order weights: expert segments here (dense calls: wq_fused_quant_matmul_packed)
-  if (d->b_layout == WQ_LAYOUT_FRAGMENT && (d->seg_offsets == nullptr || K % 64 != 0)) return WQ_ERR_UNSUPPORTED;
+  // fragment-order weights: expert segments, or the decode kernel on given codes (dense
+  // M <= 64, K % 512 == 0, K <= 4096)
+  if (d->b_layout == WQ_LAYOUT_FRAGMENT) {
+    if (K % 64 != 0) return WQ_ERR_UNSUPPORTED;
+    if (d->seg_offsets == nullptr && (M > 64 || !wq::fused_decode_fits((int)std::max<int64_t>(M, 1), (int)K) ||
+                                      d->epilogue != WQ_EPI_BF16))
+      return WQ_ERR_UNSUPPORTED;
+  }
   if (d->seg_offsets != nullptr) {
     // expert segments: persistent 128x128 tiles over the non-empty (expert, row tile) pairs
     if (!wq::tile_fits((int)K) || d->acc_out) return WQ_ERR_UNSUPPORTED;
@@ -342,12 +348,14 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
     // M > 2: the fused decode kernel without its quantisation, the given codes and scales
     // going straight to its tiles (row tiles x column slices; at M <= 2 the dot4 GEMV below
     // measured faster)
-    if (M > 2 && wq::fused_decode_fits((int)M, (int)K) && c->decode_nt == 0 && c->decode_mt == 0) {
+    const bool frag = d->b_layout == WQ_LAYOUT_FRAGMENT;
+    if ((M > 2 || frag) && wq::fused_decode_fits((int)M, (int)K) && ((c->decode_nt == 0 && c->decode_mt == 0) || frag)) {
       // shape: the fused call's model up to M = 16; above, a row without quantisation
-      // costs about a column (both measured fastest at K = 4096, N = 1024)
+      // costs about a column (both measured fastest at K = 4096, N = 1024).  Fragment-order
+      // weights (any M <= 64) always take this kernel: it is the decode kernel that reads them
       int nt = 16, rr = 16;
       fused_shape(c, M, N, &nt, &rr, M > 16 ? 1 : 4);
-      hipError_t e = wq::launch_fused_decode(a, nt, rr, st);
+      hipError_t e = wq::launch_fused_decode(a, nt, rr, st, frag);
       if (c->log)
         std::fprintf(stderr, "[wq] quant_matmul int8 decode (fused kernel, given codes) M=%lld N=%lld K=%lld cols/wg=%d "
                      "rows/wg=%d\n", (long long)M, (long long)N, (long long)K, nt, rr);

@@ -35,7 +35,7 @@ hipError_t launch_decode(const DecodeArgs& a, int nt, int mt, hipStream_t st);
 // One-launch fused quant + GEMM for M <= 64, K % 512 == 0, K <= 4096 (k_fused.hip);
 // nt output columns (4, 8, 16 or 32) and rows_per_wg rows (1, 2, 4, 8 or 16) per
 // workgroup, ceil(N / nt) * ceil(M / rows_per_wg) workgroups
-// packed: a.w holds the weights in fragment order (launch_pack_weight_i8), x given, N % 4 == 0
+// packed: a.w holds the weights in fragment order (launch_pack_weight_i8), N % 4 == 0
 hipError_t launch_fused_decode(const DecodeArgs& a, int nt, int rows_per_wg, hipStream_t st, bool packed = false);
 // weights int8 [N, K] (row stride ldw) -> fragment order: byte (n, k) at
 // ((k/64 * N/4 + n/4) * 4 + (k%64)/16) * 64 + (n%4) * 16 + k%16; N % 4 == 0, K % 64 == 0

@@ -107,6 +107,35 @@ def test_packed_every_column_width(R, NT):
         wq.set_fused_shape(DEV, 0, 0)
 
 
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 1024), (2, 512, 64), (7, 4096, 1024), (33, 1536, 272), (64, 4096, 1024)])
+def test_quant_matmul_on_packed_weights(M, K, N):
+    """The standalone GEMM on given codes (wq_quant_matmul, decode M) on fragment-order
+    weights: the same bytes as on the plain ones, the oracle's accumulators and outputs."""
+    x = syn.activations((14, M, K), M, K, outlier_frac=0.01, outlier_mul=25.0)
+    w, sw = syn.int8_weights((14, N, K), N, K)
+    ref = il.linear_w8a8(x, w, sw)
+    xq, xs = wq.wq_dynamic_quant(bf16_dev(x))
+    wd, swd = dev(w), dev(sw)
+    wp = wq.wq_pack_weight_i8(wd)
+    acc_p, acc_f = poison((M, N), torch.int32), poison((M, N), torch.int32)
+    y_plain = wq.wq_quant_matmul(xq, xs, wd, swd, acc_out=acc_p)
+    y_frag = wq.wq_quant_matmul(xq, xs, wp, swd, acc_out=acc_f, b_fragment=True, n=N)
+    torch.cuda.synchronize()
+    assert_same("y", host_bf16_bits(y_frag), host_bf16_bits(y_plain))
+    assert_same("acc", host(acc_f), ref["acc"])
+    assert nm.bf16_ulp_distance(host_bf16_bits(y_frag), ref["y"]).max() <= 1
+
+
+def test_quant_matmul_packed_unsupported_sizes():
+    K, N = 512, 64
+    w, sw = syn.int8_weights((15, N, K), N, K)
+    wp = wq.wq_pack_weight_i8(dev(w))
+    for M in (65, 300):
+        q = torch.zeros((M, K), dtype=torch.int8, device=DEV)
+        with pytest.raises(wq.WqError):
+            wq.wq_quant_matmul(q, torch.ones(M, device=DEV), wp, dev(sw), b_fragment=True, n=N)
+
+
 def test_packed_errors():
     N, K = 64, 512
     w, sw = syn.int8_weights((13, N, K), N, K)
