@@ -392,6 +392,66 @@ def main():
 
     rows = {}
     if not args.no_rows:
+        # ---- more decode shapes of the same projection family: wkv (K=4096, N=512) over the
+        # sweep's M values, and wq_a at M=128 (above the one-launch limit: quant + GEMM) ------
+        Nk = 512
+        Rk = max(2, ROTATE_BYTES // (K_A * Nk))
+        wk_h, swk_h = syn.int8_weights((2, 22, 1), Nk, K_A)
+        wk0 = torch.from_numpy(wk_h).to(dev)
+        wkp = [wq.wq_pack_weight_i8(wk0) for _ in range(Rk)]
+        swk = torch.from_numpy(swk_h).to(dev)
+        wkv = {}
+        for M in (1, 8, 64):
+            xk = [xs[M][r % R] for r in range(Rk)]
+            yk = torch.empty((M, Nk), dtype=torch.bfloat16, device=dev)
+            us = time_in_graph(lambda r, M=M: wq.wq_fused_quant_matmul_packed(xk[r], wkp[r], swk, Nk, y=yk), Rk)
+            b = fused_bytes(M, K_A, Nk)
+            wkv[str(M)] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1), "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+        rows["wkv_decode"] = {"workload": "wkv-shaped fused decode linear: X bf16 [M,4096] x W int8 [4096->512], "
+                                          "fragment-order weights, cold (rotating copies)",
+                              "kernel": "k_fused_decode<R, CT, false, true>", "by_M": wkv}
+        del wkp
+        x128 = [torch.from_numpy(syn.wq_a_linear(128)[0].view(np.int16)).to(dev).view(torch.bfloat16) for _ in range(R)]
+        y128 = torch.empty((128, N_A), dtype=torch.bfloat16, device=dev)
+        q128 = torch.empty((128, K_A), dtype=torch.int8, device=dev)
+        s128 = torch.empty((128,), dtype=torch.float32, device=dev)
+        us128 = time_in_graph(lambda r: wq.wq_fused_quant_matmul(x128[r], ws[r], sws[r], y=y128, x_q_out=q128,
+                                                                 x_scale_out=s128), R)
+        b128 = standalone_bytes(128)
+        rows["wq_a_m128"] = {"workload": "wq_a linear at M=128 (above the one-launch limit): quant kernel + INT8 GEMM, "
+                                         "plain [N,K] weights, cold", "path": wq.FUSED_PATHS[wq.wq_fused_path(128, K_A, N_A)],
+                             "us": round(us128, 3), "GBps": round(b128 / us128 / 1e3, 1),
+                             "frac_hbm": round(b128 / us128 / 1e3 / HBM_PEAK_GBS, 4)}
+        del x128
+
+        # ---- expert-local row-count sweep of the segmented gate/up GEMM (SwiGLU epilogue):
+        # 32 experts of W13 [4096 -> 2 x 2048] (512 MiB, fragment order), each with M_e rows;
+        # M_e <= 16 goes to the weight-streaming kernel, larger M_e to the tiled one ----------
+        Ee, He, Ie = 32, 4096, 2048
+        gen_e = torch.Generator(device=dev)
+        gen_e.manual_seed(7070)
+        w13e = wq.wq_pack_weight_i8(torch.randint(-127, 128, (Ee, 2 * Ie, He), generator=gen_e, device=dev,
+                                                  dtype=torch.int8))
+        sw13e = torch.rand((Ee, 2 * Ie), generator=gen_e, device=dev) * 9e-3 + 1e-3
+        me_rows = {}
+        for Me in (1, 2, 4, 8, 16, 17, 32, 64, 96, 127, 128, 129, 160, 192, 256):
+            Mt = Ee * Me
+            qe = torch.randint(-127, 128, (Mt, He), generator=gen_e, device=dev, dtype=torch.int8)
+            se = torch.rand((Mt,), generator=gen_e, device=dev) * 0.05 + 0.01
+            offe = torch.arange(0, Ee + 1, device=dev, dtype=torch.int64) * Me
+            he = torch.empty((Mt, Ie), dtype=torch.float32, device=dev)
+            us = time_events(lambda: wq.wq_quant_matmul(qe, se, w13e, sw13e, seg_offsets=offe, y=he,
+                                                        epilogue=wq.WQ_EPI_SWIGLU_F32, b_fragment=True), 5, warm=2)
+            wb = Ee * 2 * Ie * He
+            me_rows[str(Me)] = {"us": round(us, 1), "us_per_expert": round(us / Ee, 2),
+                                "weight_GBps": round(wb / us / 1e3, 1), "TOPS": round(2 * Mt * 2 * Ie * He / us / 1e6, 1),
+                                "kernel": "k_seg_decode<2, 8, true>" if Me <= 16 else "k_gemm_seg<2>"}
+            del qe, se, he
+        rows["moe_expert_rows_sweep"] = {
+            "workload": "segmented gate/up GEMM + SwiGLU, 32 experts x W13 int8 [4096 -> 2x2048] (fragment order), "
+                        "M_e rows per expert", "by_M_e": me_rows}
+        del w13e
+
         # ---- prefill GEMM: wq_b-shaped M=8192, K=1024, N=32768 -----------------------------
         Mp, Kp, Np = 8192, 1024, 32768
         xp = torch.from_numpy(syn.wq_b_x(Mp).view(np.int16)).to(dev).view(torch.bfloat16)

@@ -218,7 +218,7 @@ def wq_quant_matmul(a, a_scale, b, b_scale, *, y=None, acc_out=None, seg_offsets
     b uint8 [G, N, K], b_scale f32 [G, N/128, K/128] -> y bf16 [M, G, N].
     b_fragment: INT8 weights cast by wq_pack_weight_i8: expert weights [E, N, K] (same shape
     and strides) with seg_offsets, or a dense [N, K] cast (flat N*K bytes; give n = N) at
-    M <= 64."""
+    M < 256 (K % 512 == 0, K <= 4096)."""
     d = MatmulDesc()
     d.b_layout = WQ_LAYOUT_FRAGMENT if b_fragment else WQ_LAYOUT_PLAIN
     dev = a.device

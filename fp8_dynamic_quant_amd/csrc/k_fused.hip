@@ -329,8 +329,13 @@ bool fused_decode_fits(int M, int K) {
   return M >= 1 && M <= 64 && K % (kFW * 64) == 0 && K / kFW <= kFMaxKW;
 }
 
+bool given_decode_fits(int M, int K) {
+  return M >= 1 && M < 256 && K % (kFW * 64) == 0 && K / kFW <= kFMaxKW;
+}
+
 hipError_t launch_fused_decode(const DecodeArgs& a, int nt, int rows_per_wg, hipStream_t st, bool packed) {
-  if (!fused_decode_fits(a.M, a.K) || (a.x == nullptr && (a.a == nullptr || a.a_scale == nullptr)) ||
+  if (!(a.x != nullptr ? fused_decode_fits(a.M, a.K) : given_decode_fits(a.M, a.K)) ||
+      (a.x == nullptr && (a.a == nullptr || a.a_scale == nullptr)) ||
       !(nt == 4 || nt == 8 || nt == 16 || nt == 32) || (packed && a.N % 4 != 0))
     return hipErrorInvalidValue;
   switch (rows_per_wg) {

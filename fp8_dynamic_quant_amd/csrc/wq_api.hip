@@ -291,7 +291,7 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   // M <= 64, K % 512 == 0, K <= 4096)
   if (d->b_layout == WQ_LAYOUT_FRAGMENT) {
     if (K % 64 != 0) return WQ_ERR_UNSUPPORTED;
-    if (d->seg_offsets == nullptr && (M > 64 || !wq::fused_decode_fits((int)std::max<int64_t>(M, 1), (int)K) ||
+    if (d->seg_offsets == nullptr && (M >= 256 || !wq::given_decode_fits((int)std::max<int64_t>(M, 1), (int)K) ||
                                       d->epilogue != WQ_EPI_BF16))
       return WQ_ERR_UNSUPPORTED;
   }
@@ -334,21 +334,33 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
     return status_of(e);
   }
   if (d->epilogue != WQ_EPI_BF16) return WQ_ERR_UNSUPPORTED;
+  const bool frag = d->b_layout == WQ_LAYOUT_FRAGMENT;
+  wq::DecodeArgs a{};
+  a.a = static_cast<const int8_t*>(d->a);
+  a.lda = d->lda;
+  a.a_scale = static_cast<const float*>(d->a_scale);
+  a.w = static_cast<const int8_t*>(d->b);
+  a.w_scale = d->b_scale;
+  a.M = (int)M; a.N = (int)N; a.K = (int)K;
+  a.y = static_cast<uint16_t*>(d->y);
+  a.ldy = d->ldy;
+  a.acc_out = d->acc_out;
+  if (M > 64 && M < 256 && wq::given_decode_fits((int)M, (int)K) && c->decode_nt == 0 && c->decode_mt == 0) {
+    // between the decode sizes and the 256-row prefill tiles: the decode kernel on the given
+    // codes with row tiles of up to 16 rows (at M = 128, N = 1024 the 128 x 128 tiles gave
+    // only 8 workgroups: 41.6 us with the quant)
+    int nt = 16, rr = 16;
+    fused_shape(c, M, N, &nt, &rr, 1);
+    hipError_t e = wq::launch_fused_decode(a, nt, rr, st, frag);
+    if (c->log)
+      std::fprintf(stderr, "[wq] quant_matmul int8 mid-M (decode kernel, given codes) M=%lld N=%lld K=%lld cols/wg=%d "
+                   "rows/wg=%d\n", (long long)M, (long long)N, (long long)K, nt, rr);
+    return status_of(e);
+  }
   if (M <= 64) {
-    wq::DecodeArgs a{};
-    a.a = static_cast<const int8_t*>(d->a);
-    a.lda = d->lda;
-    a.a_scale = static_cast<const float*>(d->a_scale);
-    a.w = static_cast<const int8_t*>(d->b);
-    a.w_scale = d->b_scale;
-    a.M = (int)M; a.N = (int)N; a.K = (int)K;
-    a.y = static_cast<uint16_t*>(d->y);
-    a.ldy = d->ldy;
-    a.acc_out = d->acc_out;
     // M > 2: the fused decode kernel without its quantisation, the given codes and scales
     // going straight to its tiles (row tiles x column slices; at M <= 2 the dot4 GEMV below
     // measured faster)
-    const bool frag = d->b_layout == WQ_LAYOUT_FRAGMENT;
     if ((M > 2 || frag) && wq::fused_decode_fits((int)M, (int)K) && ((c->decode_nt == 0 && c->decode_mt == 0) || frag)) {
       // shape: the fused call's model up to M = 16; above, a row without quantisation
       // costs about a column (both measured fastest at K = 4096, N = 1024).  Fragment-order

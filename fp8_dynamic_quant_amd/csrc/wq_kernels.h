@@ -41,6 +41,8 @@ hipError_t launch_fused_decode(const DecodeArgs& a, int nt, int rows_per_wg, hip
 // ((k/64 * N/4 + n/4) * 4 + (k%64)/16) * 64 + (n%4) * 16 + k%16; N % 4 == 0, K % 64 == 0
 hipError_t launch_pack_weight_i8(const int8_t* w, int64_t ldw, int N, int K, int8_t* wp, hipStream_t st);
 bool fused_decode_fits(int M, int K);
+// the same kernel on given INT8 codes (x null): M < 256 (row tiles of up to 16 rows)
+bool given_decode_fits(int M, int K);
 // GEMV-style kernel for M <= 8 (k_decode.hip); fused needs M <= 4 and K <= 8192
 hipError_t launch_gemv(const DecodeArgs& a, hipStream_t st);
 bool gemv_fits(int M, int K, bool fused);

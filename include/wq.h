@@ -54,7 +54,7 @@ enum { WQ_PAYLOAD_INT8 = 1, WQ_PAYLOAD_FP8_E4M3 = 2 };
 /* GEMM epilogues */
 enum { WQ_EPI_BF16 = 1, WQ_EPI_SWIGLU_F32 = 2 };
 /* weight layout of wq_matmul_desc.b: plain [batch][N][K], or the fragment order of
- * wq_pack_weight_i8 applied to each batch (INT8: segments, or dense decode M) */
+ * wq_pack_weight_i8 applied to each batch (INT8: segments, or dense M < 256) */
 enum { WQ_LAYOUT_PLAIN = 0, WQ_LAYOUT_FRAGMENT = 1 };
 
 /* Human-readable text for a status code (static storage). */
@@ -186,7 +186,7 @@ typedef struct {
   int32_t* acc_out;        /* optional raw INT8 accumulators [M, N]                       */
   int32_t b_layout;        /* WQ_LAYOUT_PLAIN, or WQ_LAYOUT_FRAGMENT: the [N][K] weights (of
                               every expert) cast by wq_pack_weight_i8, same b_batch_stride.
-                              INT8 only, with seg_offsets, or dense with M <= 64,
+                              INT8 only, with seg_offsets, or dense with M < 256,
                               K % 512 == 0, K <= 4096 and WQ_EPI_BF16; other combinations
                               give WQ_ERR_UNSUPPORTED.  Outputs are the same bytes as with
                               the plain layout.                                             */

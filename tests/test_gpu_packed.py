@@ -89,6 +89,14 @@ def test_packed_wq_a_decode(M):
     _check_packed(x, w, sw)
 
 
+@pytest.mark.parametrize("M", [1, 8, 64])
+def test_packed_wkv_decode(M):
+    """The wkv-shaped projection (K = 4096, N = 512) of the same family."""
+    x = syn.activations((16, M, 4096), M, 4096, outlier_frac=0.005, outlier_mul=30.0)
+    w, sw = syn.int8_weights((16, 512, 4096), 512, 4096)
+    _check_packed(x, w, sw)
+
+
 @pytest.mark.parametrize("M,K,N", [(3, 512, 528), (33, 1536, 272), (64, 2048, 48), (17, 4096, 1040), (5, 1024, 16)])
 def test_packed_ragged_shapes(M, K, N):
     x = syn.activations((12, M, K), M, K, outlier_frac=0.01, outlier_mul=40.0)
@@ -126,11 +134,30 @@ def test_quant_matmul_on_packed_weights(M, K, N):
     assert nm.bf16_ulp_distance(host_bf16_bits(y_frag), ref["y"]).max() <= 1
 
 
+@pytest.mark.parametrize("M,K,N", [(65, 4096, 1024), (128, 4096, 1024), (200, 2048, 272), (255, 512, 48)])
+def test_quant_matmul_mid_m(M, K, N):
+    """64 < M < 256: the decode kernel on the given codes with row tiles of 16, on plain and
+    on fragment-order weights: the oracle's accumulators and outputs, the same bytes."""
+    x = syn.activations((17, M, K), M, K, outlier_frac=0.01, outlier_mul=25.0)
+    w, sw = syn.int8_weights((17, N, K), N, K)
+    ref = il.linear_w8a8(x, w, sw)
+    xq, xs = wq.wq_dynamic_quant(bf16_dev(x))
+    wd, swd = dev(w), dev(sw)
+    acc_p, acc_f = poison((M, N), torch.int32), poison((M, N), torch.int32)
+    y_plain = wq.wq_quant_matmul(xq, xs, wd, swd, acc_out=acc_p)
+    y_frag = wq.wq_quant_matmul(xq, xs, wq.wq_pack_weight_i8(wd), swd, acc_out=acc_f, b_fragment=True, n=N)
+    torch.cuda.synchronize()
+    assert_same("acc", host(acc_p), ref["acc"])
+    assert_same("acc (fragment order)", host(acc_f), ref["acc"])
+    assert_same("y", host_bf16_bits(y_frag), host_bf16_bits(y_plain))
+    assert nm.bf16_ulp_distance(host_bf16_bits(y_plain), ref["y"]).max() <= 1
+
+
 def test_quant_matmul_packed_unsupported_sizes():
     K, N = 512, 64
     w, sw = syn.int8_weights((15, N, K), N, K)
     wp = wq.wq_pack_weight_i8(dev(w))
-    for M in (65, 300):
+    for M in (256, 300):
         q = torch.zeros((M, K), dtype=torch.int8, device=DEV)
         with pytest.raises(wq.WqError):
             wq.wq_quant_matmul(q, torch.ones(M, device=DEV), wp, dev(sw), b_fragment=True, n=N)
