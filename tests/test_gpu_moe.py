@@ -125,10 +125,11 @@ def test_moe_block_full_size_sampled_experts():
 @pytest.mark.parametrize("epi", ["bf16", "swiglu"])
 def test_segments_across_the_small_expert_boundary(epi, frag):
     """Expert row counts on both sides of the 16-row split between the weight-streaming
-    kernel and the tiled one (0, 1, 15, 16, 17, 31, 32, 33, 129 rows), K = 1024 so both
-    kernels take part; every expert's rows against the oracle's dense per-expert product.
+    kernel and the tiled one, and of the tiled kernel's 64- and 128-row marks (0, 1, 15,
+    16, 17, 31, 32, 33, 63, 64, 65, 129 rows), K = 1024 so both kernels take part; every
+    expert's rows against the oracle's dense per-expert product.
     frag: the expert weights cast to fragment order (both kernels read that layout)."""
-    counts = np.array([0, 1, 15, 16, 17, 31, 32, 33, 129], np.int64)
+    counts = np.array([0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 129], np.int64)
     E, K, N = counts.size, 1024, 512
     M = int(counts.sum())
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
