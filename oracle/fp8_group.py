@@ -29,6 +29,13 @@ Readings where the page is silent (listed in the design doc):
 * the contraction out[t, g, n] = sum_k x[t, g, k] * W_g[n, k] uses per-(t, g, 128-k
   block) activation scales and per-(g, 128-n block, 128-k block) power-of-two
   weight scales, accumulates in float and rounds once to bf16.
+
+The MX-like variant follows "重塑大模型推理数据流：DeepSeek V4 950 低精度优化全复盘",
+section 2.1: every 32 consecutive elements share one 8-bit (UE8M0) scale, with E4M3
+values.  Readings (listed in the design doc): the per-block exponent is the same rule as
+above with 32-element groups; the bytes use the same packed layout (hidden groups
+D / 32); the weights carry one power-of-two scale per (output column, 32-deep K
+block); the contraction scales each 32-term block sum by both scales.
 """
 
 from __future__ import annotations
@@ -37,26 +44,28 @@ import numpy as np
 
 from .numerics import bf16_to_f32, e4m3_decode, e4m3_encode_rn, f64_to_bf16_rn, ue8m0_exponent
 
-GROUP = 128  # elements sharing one UE8M0 exponent
+GROUP = 128  # elements sharing one UE8M0 exponent (the wo_a quant of the PR)
+MX_GROUP = 32  # elements sharing one scale in the MX-like block scaling
 PER_PACK = 4  # UE8M0 bytes per int32 word
 
 
-def layout_dims(T: int, D: int):
+def layout_dims(T: int, D: int, group: int = GROUP):
     """(HG, PH, TA): hidden groups, packed hidden words, 4-aligned token count."""
-    if D % GROUP:
-        raise ValueError("D must be a multiple of 128")
-    HG = D // GROUP
+    if D % group:
+        raise ValueError(f"D must be a multiple of {group}")
+    HG = D // group
     PH = (HG + PER_PACK - 1) // PER_PACK
     TA = (T + PER_PACK - 1) // PER_PACK * PER_PACK
     return HG, PH, TA
 
 
-def group_quant_fp8(x_bits: np.ndarray):
-    """x [T, G, D] bf16 bits -> (payload uint8 E4M3FN [T, G, D], exponent bytes uint8 [T, G, HG])."""
+def group_quant_fp8(x_bits: np.ndarray, group: int = GROUP):
+    """x [T, G, D] bf16 bits -> (payload uint8 E4M3FN [T, G, D], exponent bytes uint8 [T, G, HG]),
+    one exponent per `group` consecutive elements (128, or 32 for the MX-like blocks)."""
     x_bits = np.asarray(x_bits)
     T, G, D = x_bits.shape
-    HG, _, _ = layout_dims(T, D)
-    xf = bf16_to_f32(x_bits).astype(np.float64).reshape(T, G, HG, GROUP)
+    HG, _, _ = layout_dims(T, D, group)
+    xf = bf16_to_f32(x_bits).astype(np.float64).reshape(T, G, HG, group)
     a = np.max(np.abs(xf), axis=-1) if T > 0 else np.zeros((0, G, HG))
     e = ue8m0_exponent(a)  # [T, G, HG]
     scaled = np.ldexp(xf, -e[..., None])  # exact power-of-two scaling in float64
@@ -97,9 +106,9 @@ def unpack_ue8m0(storage: np.ndarray, T: int, HG: int) -> np.ndarray:
     return out
 
 
-def group_quant_fp8_packed(x_bits: np.ndarray):
+def group_quant_fp8_packed(x_bits: np.ndarray, group: int = GROUP):
     """The whole producer: payload [T, G, D] and packed int32 storage [G, PH, TA]."""
-    payload, ebyte = group_quant_fp8(x_bits)
+    payload, ebyte = group_quant_fp8(x_bits, group)
     return payload, pack_ue8m0(ebyte), ebyte
 
 
@@ -147,3 +156,34 @@ def contraction_from_packed(xq, storage, T, wq, w_scale, **kw):
     """Contraction reading the activation scales from the packed int32 storage."""
     HG = xq.shape[2] // GROUP
     return fp8_grouped_contraction(xq, ebyte_to_scale(unpack_ue8m0(storage, T, HG)), wq, w_scale, **kw)
+
+
+def mx_contraction(xq: np.ndarray, x_scale_f: np.ndarray, wq: np.ndarray, w_scale: np.ndarray,
+                   *, return_abs: bool = False):
+    """The contraction with MX-like 32-element blocks on both operands:
+         out[t, g, n] = sum over 32-deep k blocks kb of
+             x_scale_f[t, g, kb] * w_scale[g, n, kb] * sum_{k in kb} x[t, g, k] * W_g[n, k]
+
+    xq: E4M3FN codes [T, G, D]; x_scale_f: powers of two [T, G, D/32]; wq: E4M3FN codes
+    [G, N, D]; w_scale: powers of two [G, N, D/32].  Each 32-term block sum is exact in
+    float64, the scaled block sums are added in float64 in block order and rounded once
+    to bf16; with return_abs also S = sum of |scaled products| per output.
+    """
+    T, G, D = xq.shape
+    Gw, N, Dw = wq.shape
+    assert Gw == G and Dw == D and D % MX_GROUP == 0
+    HG = D // MX_GROUP
+    xv = e4m3_decode(xq).reshape(T, G, HG, MX_GROUP)
+    wv = e4m3_decode(wq).reshape(G, N, HG, MX_GROUP)
+    xs = np.asarray(x_scale_f, np.float64)
+    ws = np.asarray(w_scale, np.float64)
+    out = np.zeros((T, G, N), dtype=np.float64)
+    sabs = np.zeros((T, G, N), dtype=np.float64)
+    for g in range(G):
+        for kb in range(HG):
+            sc = xs[:, g, kb][:, None] * ws[g, :, kb][None, :]
+            out[:, g, :] += (xv[:, g, kb, :] @ wv[g, :, kb, :].T) * sc  # block sum exact
+            if return_abs:
+                sabs[:, g, :] += (np.abs(xv[:, g, kb, :]) @ np.abs(wv[g, :, kb, :]).T) * sc
+    y = f64_to_bf16_rn(out)
+    return (y, sabs) if return_abs else y

@@ -157,3 +157,104 @@ def test_packed_and_f32_scales_give_identical_bytes():
     y_f32 = fg.fp8_grouped_contraction(payload, fg.ebyte_to_scale(eb), wq, ws)
     y_pk = fg.contraction_from_packed(payload, storage, T, wq, ws)
     assert np.array_equal(y_f32, y_pk)
+
+
+# ---- MX-like 32-element blocks ("DeepSeek V4 950" section 2.1) ---------------------------
+
+def _mx_golden():
+    lines = list(_golden_lines("mx_blocks.txt"))
+    row = {int(k): float(v) for k, v in (e.split("=") for e in lines[0].split("|")[1].split())}
+    out = {}
+    for line in lines[1:]:
+        name, bs, cs = [p.strip() for p in line.split("|")]
+        out[name] = ([int(b, 16) for b in bs.split()], {int(k): int(v, 16) for k, v in (e.split("=") for e in cs.split())})
+    return row, out
+
+
+@pytest.mark.parametrize("group", [128, 32])
+def test_mx_hand_row(group):
+    row, want = _mx_golden()
+    x = np.zeros((1, 1, 128), np.uint16)
+    for i, v in row.items():
+        x[0, 0, i] = bf16_bits_of(v)
+    payload, eb = fg.group_quant_fp8(x, group)
+    bytes_want, codes_want = want[f"group{group}"]
+    assert eb[0, 0].tolist() == bytes_want
+    for i, c in codes_want.items():
+        assert int(payload[0, 0, i]) == c, (i, hex(int(payload[0, 0, i])), hex(c))
+    zero = [i for i in range(128) if i not in row]
+    assert not payload[0, 0, zero].any()
+
+
+def test_mx_blocks_invariants():
+    x = syn.fp8_group_x(9, G=2, D=512, layout_variant=True)
+    payload, eb = fg.group_quant_fp8(x, 32)
+    a = np.abs(nm.bf16_to_f32(x).astype(np.float64)).reshape(9, 2, 16, 32).max(axis=-1)
+    e = eb.astype(np.int64) - 127
+    live = e > -127
+    assert np.all(np.ldexp(448.0, e[live]) >= a[live])          # 2^e covers absmax / 448
+    assert np.all(np.ldexp(448.0, e[live] - 1) < a[live])       # and is the smallest power that does
+    dec = nm.e4m3_decode(payload).reshape(9, 2, 16, 32)
+    assert np.all(np.abs(dec) <= 448)                           # never saturates
+
+
+def test_mx_blocks_equal_groups_of_128_when_every_block_holds_the_max():
+    """If each 32-element block holds an element equal to its 128-group's absmax, both
+    block sizes pick the same exponent, so the bytes repeat 4 times and the codes agree."""
+    x = syn.fp8_group_x(5, G=3, D=384)
+    T, G, D = x.shape
+    xf = nm.bf16_to_f32(x).astype(np.float32).reshape(T, G, D // 128, 4, 32)
+    m = np.abs(xf).max(axis=(-1, -2))                           # [T, G, HG]
+    xf[:, :, :, :, 0] = m[:, :, :, None]                        # the group's absmax in every block
+    # every value is still a bf16 value, so its bits are the high half of the f32 bits
+    xb = (np.ascontiguousarray(xf.reshape(T, G, D)).view(np.uint32) >> 16).astype(np.uint16)
+    p128, e128 = fg.group_quant_fp8(xb, 128)
+    p32, e32 = fg.group_quant_fp8(xb, 32)
+    assert np.array_equal(p32, p128)
+    assert np.array_equal(e32, np.repeat(e128, 4, axis=-1))
+
+
+def _exact_mx(xq, xs_f, wq, ws):
+    xv, wv = nm.e4m3_decode(xq), nm.e4m3_decode(wq)
+    T, G, D = xq.shape
+    N = wq.shape[1]
+    out = np.zeros((T, G, N), np.uint16)
+    for t in range(T):
+        for g in range(G):
+            for n in range(N):
+                tot = F(0)
+                for k in range(D):
+                    kb = k // 32
+                    tot += F(float(xv[t, g, k])) * F(float(wv[g, n, k])) * F(float(xs_f[t, g, kb])) * F(float(ws[g, n, kb]))
+                r = rn_bf16(tot)
+                out[t, g, n] = 0 if r == 0 else f32_bits(float(r)) >> 16
+    return out
+
+
+def test_mx_contraction_against_exact_fractions():
+    g = np.random.default_rng(33)
+    T, G, D, N = 2, 2, 128, 6
+    xq = syn.random_e4m3_codes(g, (T, G, D))
+    xs_f = np.ldexp(1.0, g.integers(-6, 6, (T, G, D // 32)))
+    wq = syn.random_e4m3_codes(g, (G, N, D))
+    ws = np.ldexp(1.0, g.integers(-3, 4, (G, N, D // 32)))
+    y = fg.mx_contraction(xq, xs_f, wq, ws)
+    want = _exact_mx(xq, xs_f, wq, ws)
+    assert nm.bf16_ulp_distance(y, want).max() <= 1
+    assert (nm.bf16_ulp_distance(y, want) == 0).mean() > 0.99
+
+
+def test_mx_contraction_equals_128_blocks_when_scales_repeat():
+    """Scales constant over each 128-deep block (and, for the weights, over 128 columns):
+    the MX contraction is the 128-block contraction, byte for byte."""
+    g = np.random.default_rng(34)
+    T, G, D, N = 3, 2, 256, 128
+    xq = syn.random_e4m3_codes(g, (T, G, D))
+    wq = syn.random_e4m3_codes(g, (G, N, D))
+    xs128 = np.ldexp(1.0, g.integers(-5, 5, (T, G, D // 128)))
+    ws128 = np.ldexp(np.float32(1.0), g.integers(-3, 4, (G, N // 128, D // 128))).astype(np.float32)
+    y128 = fg.fp8_grouped_contraction(xq, xs128, wq, ws128)
+    xs32 = np.repeat(xs128, 4, axis=-1)
+    ws32 = np.repeat(np.repeat(ws128.astype(np.float64), 128, axis=1), 4, axis=-1)
+    y32 = fg.mx_contraction(xq, xs32, wq, ws32)
+    assert np.array_equal(y32, y128)
