@@ -490,6 +490,12 @@ def main():
             q8 = [torch.empty((T, G8, D8), dtype=torch.uint8, device=dev) for _ in range(R8)]
             st8 = [torch.empty((G8, PH, TA), dtype=torch.int32, device=dev) for _ in range(R8)]
             us_gq = time_in_graph(lambda r: wq.wq_group_quant_fp8_ue8m0(x8[r], x_q=q8[r], storage=st8[r]), R8)
+            # the MX-like 32-element blocks: same payload size, 4x the scale bytes
+            _, PHm, TAm = wq.packed_scale_dims(T, D8, 32)
+            stm = [torch.empty((G8, PHm, TAm), dtype=torch.int32, device=dev) for _ in range(R8)]
+            us_mx = time_in_graph(lambda r: wq.wq_group_quant_fp8_ue8m0(x8[r], x_q=q8[r], storage=stm[r], group=32), R8)
+            mx_bytes = 2 * T * G8 * D8 + T * G8 * D8 + 4 * G8 * PHm * TAm
+            del stm
             y8 = torch.empty((T, G8, N8), dtype=torch.bfloat16, device=dev)
             us_c = time_in_graph(lambda r: wq.wq_quant_matmul(q8[r], st8[r], wq8[r], ws8, y=y8, fp8_groups=G8), R8)
             del x8, q8, st8
@@ -497,12 +503,13 @@ def main():
             c_bytes = T * G8 * D8 + 4 * G8 * PH * TA + G8 * N8 * D8 + 4 * G8 * (N8 // 128) * (D8 // 128) + 2 * T * G8 * N8
             c_ops = 2 * T * G8 * N8 * D8
             fp8[str(T)] = {"group_quant_us": round(us_gq, 3), "group_quant_GBps": round(gq_bytes / us_gq / 1e3, 1),
+                           "mx32_group_quant_us": round(us_mx, 3), "mx32_group_quant_GBps": round(mx_bytes / us_mx / 1e3, 1),
                            "contraction_us": round(us_c, 3), "contraction_GBps": round(c_bytes / us_c / 1e3, 1),
                            "contraction_frac_hbm": round(c_bytes / us_c / 1e3 / HBM_PEAK_GBS, 4),
                            "contraction_TOPS": round(c_ops / us_c / 1e6, 2)}
         rows["fp8_wo_a"] = {"workload": "X bf16 [T, 8, 4096] -> E4M3 + packed UE8M0 [8, 8, align4(T)]; "
                                         "out[T,g,:] = x_q[T,g,:] W_g^T, W_g E4M3 [1024, 4096], 128x128 pow2 scales",
-                            "kernels": "k_group_quant_fp8; k_fp8_decode (T <= 16), k_fp8_decode32 (16 < T <= 64), k_gemm_tile<FP8> (T > 64)", "by_T": fp8}
+                            "kernels": "k_group_quant_fp8 (k_group_quant_mx for 32-element blocks); k_fp8_decode (T <= 16), k_fp8_decode32 (16 < T <= 64), k_gemm_tile<FP8> (T > 64)", "by_T": fp8}
         del wq8
 
         # ---- MoE block: T=256, hidden 4096, 256 experts of 2x2048, top-8 Zipf(1.1) ----------

@@ -72,6 +72,8 @@ EXPORTS = {
     "wq_moe_sort": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                    _c_void_p]),
     "wq_fused_path": (ctypes.c_int, [_c_void_p, _i64, _i64, _i64]),
+    "wq_group_quant_mxfp8": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p,
+                                            _c_void_p]),
     "wq_pack_weight_i8": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p]),
     "wq_fused_quant_matmul_packed": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p,
                                                     _i64, _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p,
@@ -181,19 +183,23 @@ def wq_dynamic_quant(x: torch.Tensor, rms_gamma: torch.Tensor | None = None, rms
     return x_q, x_scale
 
 
-def packed_scale_dims(T: int, D: int):
-    HG = D // 128
+def packed_scale_dims(T: int, D: int, group: int = 128):
+    HG = D // group
     return HG, (HG + 3) // 4, (T + 3) // 4 * 4
 
 
-def wq_group_quant_fp8_ue8m0(x: torch.Tensor, x_q: torch.Tensor | None = None, storage: torch.Tensor | None = None):
+def wq_group_quant_fp8_ue8m0(x: torch.Tensor, x_q: torch.Tensor | None = None, storage: torch.Tensor | None = None,
+                             group: int = 128):
     """x bf16 [T, G, D] contiguous -> (x_q uint8 [T, G, D] E4M3FN codes,
     x_s int32 logical view [T, G, PH] with strides (1, PH*TA, TA), storage [G, PH, TA]).
-    x_q / storage may be passed in (contiguous, those shapes) instead of allocated."""
+    x_q / storage may be passed in (contiguous, those shapes) instead of allocated.
+    group=32: the MX-like 32-element blocks (wq_group_quant_mxfp8)."""
     if x.dim() != 3 or not x.is_contiguous() or x.dtype != torch.bfloat16:
         raise ValueError("x must be a contiguous bf16 [T, G, D] tensor")
+    if group not in (128, 32):
+        raise ValueError("group must be 128 or 32")
     T, G, D = x.shape
-    _, PH, TA = packed_scale_dims(T, D)
+    _, PH, TA = packed_scale_dims(T, D, group)
     ctx = context(x.device)
     if x_q is None:
         x_q = torch.empty((T, G, D), dtype=torch.uint8, device=x.device)
@@ -203,9 +209,9 @@ def wq_group_quant_fp8_ue8m0(x: torch.Tensor, x_q: torch.Tensor | None = None, s
             or not storage.is_contiguous() or storage.dtype != torch.int32:
         raise ValueError("x_q must be uint8 [T, G, D] and storage int32 [G, PH, TA], both contiguous")
     if x.numel() > 0:
-        st = lib().wq_group_quant_fp8_ue8m0(ctx.handle, _ptr(x), T, G, D, _ptr(x_q), _ptr(storage),
-                                            _stream(x.device))
-        _check("wq_group_quant_fp8_ue8m0", st)
+        fn = "wq_group_quant_fp8_ue8m0" if group == 128 else "wq_group_quant_mxfp8"
+        st = getattr(lib(), fn)(ctx.handle, _ptr(x), T, G, D, _ptr(x_q), _ptr(storage), _stream(x.device))
+        _check(fn, st)
     x_s = storage.transpose(-1, -2)[:, :T, :].transpose(0, 1)
     return x_q, x_s, storage
 

@@ -88,6 +88,73 @@ __global__ __launch_bounds__(256) void k_group_quant_fp8(const uint16_t* __restr
   }
 }
 
+// MX-like 32-element blocks ("DeepSeek V4 950 低精度优化全复盘", section 2.1: every 32
+// elements share one 8-bit scale), same exponent rule and packed layout with HG = D / 32.
+// One wave64 per (token t, outer group g, 4 consecutive packs): its 16-lane row r takes
+// pack p = 4 * pw + r, i.e. blocks 4p .. 4p+3 (128 bf16 contiguous, 16 bytes per lane),
+// and each 4-lane quad of the row one block; the quad's absmax comes from two quad
+// permutes, and lane 0 of the row writes the pack's word.
+__global__ __launch_bounds__(256) void k_group_quant_mx(const uint16_t* __restrict__ x, int64_t T, int G, int D,
+                                                        uint8_t* __restrict__ xq, int32_t* __restrict__ xs) {
+  const int lane = threadIdx.x & 63;
+  const int HG = D / 32, PH = (HG + 3) / 4, PW = (PH + 3) / 4;
+  const int64_t TA = (T + 3) / 4 * 4;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= TA * G * PW) return;
+  const int pw = (int)(wid % PW);
+  const int64_t tg = wid / PW;
+  const int g = (int)(tg % G);
+  const int64_t t = tg / G;
+  const int r = lane >> 4, q = (lane >> 2) & 3;
+  const int p = 4 * pw + r;  // this row's pack
+  const int h = 4 * p + q;   // this quad's block
+  int byte = 0;
+  if (t < T && p < PH && h < HG) {
+    const int64_t off = (t * G + g) * (int64_t)D + (int64_t)h * 32 + (lane & 3) * 8;
+    const uint4 u = *reinterpret_cast<const uint4*>(x + off);
+    float v[8];
+    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w4[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+    // max over the quad: swap neighbours, then pairs (exec covers whole quads here)
+    a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, false)));
+    a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, false)));
+    const int e = ue8m0_exp(a);
+    const float sc = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-127, 126]
+    uint32_t lo = 0, hi = 0;
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[0], sc), __fmul_rn(v[1], sc), lo, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[2], sc), __fmul_rn(v[3], sc), lo, true);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[4], sc), __fmul_rn(v[5], sc), hi, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[6], sc), __fmul_rn(v[7], sc), hi, true);
+    *reinterpret_cast<uint2*>(xq + off) = uint2{lo, hi};
+    byte = e + 127;
+  }
+  // the row's four quad bytes (0 for blocks past HG) form the pack word; lane 16 r writes it
+  const int base = lane & ~15;
+  const int b1 = __shfl(byte, base + 4, 64), b2 = __shfl(byte, base + 8, 64), b3 = __shfl(byte, base + 12, 64);
+  if ((lane & 15) == 0 && p < PH) {
+    const uint32_t word = (uint32_t)byte | ((uint32_t)b1 << 8) | ((uint32_t)b2 << 16) | ((uint32_t)b3 << 24);
+    xs[((int64_t)g * PH + p) * TA + t] = (int32_t)word;
+  }
+}
+
+hipError_t launch_group_quant_mx(const uint16_t* x, int64_t T, int G, int D, uint8_t* xq, int32_t* xs,
+                                 hipStream_t st) {
+  const int HG = D / 32, PH = (HG + 3) / 4, PW = (PH + 3) / 4;
+  const int64_t TA = (T + 3) / 4 * 4;
+  const int64_t waves = TA * G * PW;
+  if (waves == 0) return hipSuccess;
+  dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  hipLaunchKernelGGL(k_group_quant_mx, grid, block, 0, st, x, T, G, D, xq, xs);
+  return hipGetLastError();
+}
+
 hipError_t launch_group_quant_fp8(const uint16_t* x, int64_t T, int G, int D, uint8_t* xq, int32_t* xs,
                                   hipStream_t st) {
   const int HG = D / 128, PH = (HG + 3) / 4;

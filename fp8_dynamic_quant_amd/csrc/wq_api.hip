@@ -278,6 +278,21 @@ int wq_group_quant_fp8_ue8m0(wq_ctx* c, const void* x, int64_t T, int64_t G, int
   return status_of(e);
 }
 
+int wq_group_quant_mxfp8(wq_ctx* c, const void* x, int64_t T, int64_t G, int64_t D, uint8_t* x_q, int32_t* x_s,
+                         void* stream) {
+  if (!c) return WQ_ERR_NULL;
+  if (T < 0 || G <= 0 || D <= 0 || D % 32 != 0 || G > 65535 || D > (1 << 20)) return WQ_ERR_SHAPE;
+  if (T == 0) return WQ_OK;
+  if (!x || !x_q || !x_s) return WQ_ERR_NULL;
+  if (!al16(x) || !al16(x_q) || !al16(x_s)) return WQ_ERR_ALIGN;
+  DeviceGuard g(c->device);
+  hipError_t e = wq::launch_group_quant_mx(static_cast<const uint16_t*>(x), T, (int)G, (int)D, x_q, x_s,
+                                           static_cast<hipStream_t>(stream));
+  if (c->log)
+    std::fprintf(stderr, "[wq] group_quant_mxfp8 T=%lld G=%lld D=%lld\n", (long long)T, (long long)G, (long long)D);
+  return status_of(e);
+}
+
 static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   const int64_t M = d->M, N = d->N, K = d->K;
   if (N % 16 != 0 || K % 16 != 0 || K > 131072 || d->lda < K || d->ldy < (d->epilogue == WQ_EPI_SWIGLU_F32 ? N / 2 : N))

@@ -98,6 +98,9 @@ bool fp8_decode32_fits(int T, int N, int K);
 // FP8 group quant with packed UE8M0 scales (k_fp8.hip).
 hipError_t launch_group_quant_fp8(const uint16_t* x, int64_t T, int G, int D, uint8_t* xq, int32_t* xs,
                                   hipStream_t st);
+// the same with MX-like 32-element blocks (D % 32 == 0; HG = D / 32)
+hipError_t launch_group_quant_mx(const uint16_t* x, int64_t T, int G, int D, uint8_t* xq, int32_t* xs,
+                                 hipStream_t st);
 
 // Expert sort (k_moe.hip).
 hipError_t launch_moe_sort(const int32_t* ids, int64_t T, int topk, int E, int32_t* perm, int32_t* row_token,

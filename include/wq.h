@@ -143,6 +143,16 @@ int wq_dynamic_quant(wq_ctx* ctx, const void* x, int x_dtype, int64_t M, int64_t
 int wq_group_quant_fp8_ue8m0(wq_ctx* ctx, const void* x, int64_t T, int64_t G, int64_t D,
                              uint8_t* x_q, int32_t* x_s, void* stream);
 
+/* The MX-like variant of "DeepSeek V4 950 低精度优化全复盘", section 2.1: every 32
+ * elements share one 8-bit scale, E4M3 values.  Same contract as wq_group_quant_fp8_ue8m0
+ * with 32-element groups: D % 32 == 0, HG = D / 32 (so PH = ceil(D / 128)),
+ *   a = max |x[t, g, 32h .. 32h+31]|, e = max(-127, smallest e with 2^e >= a / 448),
+ *   x_q = E4M3FN(x * 2^-e), byte e + 127 at byte (h % 4) of word (g * PH + h / 4) * TA + t,
+ * every other byte of x_s [G, PH, TA] zero.  One pack word holds the four 32-element
+ * scales of one 128-deep K block. */
+int wq_group_quant_mxfp8(wq_ctx* ctx, const void* x, int64_t T, int64_t G, int64_t D,
+                         uint8_t* x_q, int32_t* x_s, void* stream);
+
 /* ---- quantised matmul ---------------------------------------------------------------
  * INT8 (section 一 of the W8A8 article; npu_quant_matmul, and the tuple-reuse path where
  * an upstream producer already gave (x_q, x_scale)):

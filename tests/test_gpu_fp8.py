@@ -198,3 +198,53 @@ def test_fp8_contraction_subnormal_and_extreme_codes():
     want = nm.e4m3_decode(codes)
     bad = np.flatnonzero(got != want)
     assert bad.size == 0, f"codes {[hex(int(c)) for c in codes[bad][:8]]}: got {got[bad][:8]} want {want[bad][:8]}"
+
+
+# ---- MX-like 32-element blocks (wq_group_quant_mxfp8) ------------------------------------
+
+def _check_mx(x_bits, poison_storage=True):
+    T, G, D = x_bits.shape
+    payload, storage, _ = fg.group_quant_fp8_packed(x_bits, 32)
+    HG, PH, TA = wq.packed_scale_dims(T, D, 32)
+    st = torch.full((G, PH, TA), -0x5A5A5A5B, dtype=torch.int32, device=DEV)  # 0xA5A5A5A5: unwritten words show
+    xq = torch.full((T, G, D), 0xA5, dtype=torch.uint8, device=DEV)
+    xq, xs, st = wq.wq_group_quant_fp8_ue8m0(bf16_dev(x_bits), x_q=xq, storage=st if poison_storage else None,
+                                             group=32)
+    torch.cuda.synchronize()
+    assert xs.shape == (T, G, PH)
+    assert np.array_equal(host(xq), payload)
+    assert np.array_equal(host(st), storage)
+
+
+@pytest.mark.parametrize("T", [1, 7, 64, 512])
+def test_mx_group_quant_dsv4_wo_a(T):
+    _check_mx(syn.fp8_group_x(T))
+
+
+@pytest.mark.parametrize("T,G,D", [(5, 3, 96), (9, 2, 160), (6, 1, 544), (3, 2, 32), (4, 8, 4096), (2, 1, 4160)])
+def test_mx_group_quant_pack_tails(T, G, D):
+    """Blocks per row 3, 5, 17, 1, 128, 130: partial last packs (zero tail bytes) and
+    partial last groups of four packs in a wave, with token padding."""
+    _check_mx(syn.fp8_group_x(T, G=G, D=D, layout_variant=True))
+
+
+def test_mx_group_quant_hand_row_and_special_values():
+    """The hand-worked row of tests/golden/mx_blocks.txt, and special values per block."""
+    x = np.zeros((2, 1, 128), np.uint16)
+    x[0, 0, 0], x[0, 0, 40], x[0, 0, 100] = 0x3F80, 0x43E1, 0xBE9A  # 1.0, 450, -0.30078125
+    x[1, 0, 32] = 0x43E0  # 448 alone in block 1
+    x[1, 0, 64] = 0x3A80  # 2^-10 -> tie to 0
+    x[1, 0, 65] = 0x3AC0  # 3*2^-11
+    x[1, 0, 66] = 0x8000  # -0
+    _check_mx(x)
+    q, _, st = wq.wq_group_quant_fp8_ue8m0(bf16_dev(x), group=32)
+    torch.cuda.synchronize()
+    assert host(st)[0, 0, 0] == 0x75008077  # bytes 0x77, 0x80, 0x00, 0x75 (little-endian)
+    assert [int(host(q)[0, 0, i]) for i in (0, 40, 100)] == [0x78, 0x76, 0xFA]
+
+
+def test_mx_group_quant_empty_and_errors():
+    xq, xs, st = wq.wq_group_quant_fp8_ue8m0(torch.empty((0, 2, 64), dtype=torch.bfloat16, device=DEV), group=32)
+    assert tuple(xs.shape) == (0, 2, 1)
+    rc = wq.lib().wq_group_quant_mxfp8(wq.context(DEV).handle, 0, 1, 1, 48, 0, 0, 0)
+    assert rc == 2  # WQ_ERR_SHAPE: D not a multiple of 32
