@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libwq.so")
 
 WQ_OK = 0
 WQ_IN_BF16, WQ_IN_F32 = 1, 2
-WQ_PAYLOAD_INT8, WQ_PAYLOAD_FP8_E4M3 = 1, 2
+WQ_PAYLOAD_INT8, WQ_PAYLOAD_FP8_E4M3, WQ_PAYLOAD_MXFP8 = 1, 2, 3
 WQ_EPI_BF16, WQ_EPI_SWIGLU_F32 = 1, 2
 WQ_LAYOUT_PLAIN, WQ_LAYOUT_FRAGMENT = 0, 1
 
@@ -217,11 +217,14 @@ def wq_group_quant_fp8_ue8m0(x: torch.Tensor, x_q: torch.Tensor | None = None, s
 
 
 def wq_quant_matmul(a, a_scale, b, b_scale, *, y=None, acc_out=None, seg_offsets=None,
-                    epilogue=WQ_EPI_BF16, fp8_groups=None, a_scale_tokens=0, b_fragment=False, n=None):
+                    epilogue=WQ_EPI_BF16, fp8_groups=None, a_scale_tokens=0, b_fragment=False, n=None,
+                    mx=False):
     """INT8: a int8 [M, K] (row stride a.stride(0)), a_scale f32 [M], b int8 [N, K] (or
     [E, N, K] with seg_offsets int64 [E+1]), b_scale f32 [N] (or [E, N]) -> y.
     FP8 (fp8_groups=G): a uint8 [M, G, K], a_scale = packed storage [G, PH, TA],
     b uint8 [G, N, K], b_scale f32 [G, N/128, K/128] -> y bf16 [M, G, N].
+    mx (with fp8_groups): the MX-like 32-element blocks: a_scale = storage of
+    wq_group_quant_mxfp8 [G, K/128, TA], b_scale = UE8M0 bytes uint8 [G, N, K/32].
     b_fragment: INT8 weights cast by wq_pack_weight_i8: expert weights [E, N, K] (same shape
     and strides) with seg_offsets, or a dense [N, K] cast (flat N*K bytes; give n = N) at
     M < 256 (K % 512 == 0, K <= 4096)."""
@@ -234,7 +237,7 @@ def wq_quant_matmul(a, a_scale, b, b_scale, *, y=None, acc_out=None, seg_offsets
         N = b.shape[1]
         if y is None:
             y = torch.empty((M, G, N), dtype=torch.bfloat16, device=dev)
-        d.payload, d.epilogue = WQ_PAYLOAD_FP8_E4M3, WQ_EPI_BF16
+        d.payload, d.epilogue = (WQ_PAYLOAD_MXFP8 if mx else WQ_PAYLOAD_FP8_E4M3), WQ_EPI_BF16
         d.M, d.N, d.K, d.batch = M, N, K, G
         d.a, d.lda, d.a_batch_stride = _ptr(a), a.stride(0), a.stride(1)
         d.a_scale, d.a_scale_tokens = _ptr(a_scale), a_scale.shape[2]

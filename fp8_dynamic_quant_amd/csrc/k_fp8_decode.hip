@@ -32,8 +32,15 @@ constexpr int kF8MaxSteps = 8;  // 128-deep K steps per wave: K <= 4096
 constexpr int kF8MaxRT = 4;     // 16-token row tiles: T <= 64
 }  // namespace
 
-template <int TPW>
+// MX: the MX-like 32-element blocks ("DeepSeek V4 950 低精度优化全复盘", section 2.1) on
+// both operands: the activation words hold the four 32-element scales of one 128-deep
+// block (storage [G, K/128, TA] from wq_group_quant_mxfp8) and p.w_scale holds UE8M0
+// bytes [G][N][K/32].  The MFMA applies the scale operand of lane group kq to K bytes
+// 32 kq .. 32 kq + 31 of the block (its operand layout is stated at the loads below), so
+// lane group kq passes byte kq of the activation word and of the column's scale word.
+template <int TPW, bool MX>
 __global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
+  constexpr int NW = MX ? kF8MaxSteps : 3;  // packed activation words per token tile
   __shared__ float red[4][TPW][4][64];
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: the weight-scale loads go scalar
@@ -44,9 +51,13 @@ __global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
   const int kb0 = wv * steps;
   const int cl = lane & 15, kq = lane >> 4;  // column (B) / row (A) in the tile; 32-byte quarter of the step
   const int n = n0 + cl;
-  const int PH = (KT + 3) >> 2;
+  const int PH = MX ? KT : (KT + 3) >> 2;
   const int32_t* xs_g = p.a_scale_packed + (int64_t)g * PH * p.a_scale_tokens;
-  const int8_t* A = p.a + (int64_t)g * p.a_batch_stride + kq * 32;
+  // operand layout of v_mfma_scale_f32_16x16x128_f8f6f4 (measured on gfx950 with one-hot
+  // inputs and distinct 32-element block scales): lane group q (lanes 16q .. 16q+15) holds
+  // K bytes 16q .. 16q+15 in its first four registers and 64+16q .. 64+16q+15 in the last
+  // four, and the scale operand of lane group s applies to K bytes 32s .. 32s+31
+  const int8_t* A = p.a + (int64_t)g * p.a_batch_stride + kq * 16;
   const int rt_lo = blockIdx.z * TPW;    // this workgroup's 16-token tiles [rt_lo, rt_lo + TPW)
 
   // Every load is issued before the first wait and none sits under a branch (K steps and
@@ -57,49 +68,58 @@ __global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
   // this wave's K blocks [kb0, kb0 + steps) touch at most 3 packed activation-scale words
   const int w0 = kb0 >> 2;
   // ---- weights, 32 bytes per lane per 128-deep step, straight into the B layout ----------
-  const int8_t* W = p.w + (int64_t)g * p.w_batch_stride + (int64_t)n * K + kq * 32;
+  const int8_t* W = p.w + (int64_t)g * p.w_batch_stride + (int64_t)n * K + kq * 16;
   v8i b[kF8MaxSteps];
 #pragma unroll
   for (int j = 0; j < kF8MaxSteps; ++j) {
     const int8_t* src = W + (int64_t)(kb0 + min(j, steps - 1)) * 128;
     const v4i lo = *reinterpret_cast<const v4i*>(src);
-    const v4i hi = *reinterpret_cast<const v4i*>(src + 16);
+    const v4i hi = *reinterpret_cast<const v4i*>(src + 64);
     b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   // ---- token tiles (fragments and packed scale words): the next tile loads while the
   // current one multiplies -------------------------------------------------------------------
-  auto load_tile = [&](int rt, v8i (&a)[kF8MaxSteps], int32_t (&wd)[3]) {
+  auto load_tile = [&](int rt, v8i (&a)[kF8MaxSteps], int32_t (&wd)[NW]) {
     // rows past T read row T-1: they only feed output rows that are not stored
     const int row = min((rt_lo + rt) * 16 + cl, T - 1);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) wd[q] = xs_g[(int64_t)min(w0 + q, PH - 1) * p.a_scale_tokens + row];
+    for (int q = 0; q < NW; ++q)
+      wd[q] = MX ? xs_g[(int64_t)(kb0 + min(q, steps - 1)) * p.a_scale_tokens + row]
+                 : xs_g[(int64_t)min(w0 + q, PH - 1) * p.a_scale_tokens + row];
     const int8_t* arow = A + (int64_t)row * p.lda;
 #pragma unroll
     for (int j = 0; j < kF8MaxSteps; ++j) {
       const int8_t* src = arow + (int64_t)(kb0 + min(j, steps - 1)) * 128;
       const v4i lo = *reinterpret_cast<const v4i*>(src);
-      const v4i hi = *reinterpret_cast<const v4i*>(src + 16);
+      const v4i hi = *reinterpret_cast<const v4i*>(src + 64);
       a[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
   v8i abuf[2][kF8MaxSteps];
-  int32_t words[2][3];
+  int32_t words[2][NW];
   load_tile(0, abuf[0], words[0]);
   if (TPW > 1) load_tile(1, abuf[1], words[1]);
   // keep the issue order: a load the scheduler sinks next to its use is waited for at once
   __builtin_amdgcn_sched_barrier(0);
   // ---- the weight block-scale exponents (wave-uniform scalar loads, while the vector loads
   // are in flight; the empty asm pins each value here, so no load is sunk next to its MFMA)
-  const float* wsc = p.w_scale + ((int64_t)g * (N >> 7) + (n0 >> 7)) * KT + kb0;
-  uint32_t wsb[kF8MaxSteps];
-#pragma unroll
-  for (int j = 0; j < kF8MaxSteps; ++j) wsb[j] = __float_as_uint(wsc[min(j, steps - 1)]);
-  static_assert(kF8MaxSteps == 8, "one pin for the eight scales");
-  asm volatile("" : "+s"(wsb[0]), "+s"(wsb[1]), "+s"(wsb[2]), "+s"(wsb[3]), "+s"(wsb[4]), "+s"(wsb[5]), "+s"(wsb[6]),
-               "+s"(wsb[7]));
   int sbx[kF8MaxSteps];
+  if constexpr (MX) {
+    // per lane: the column's word of four 32-element scales for block kb0 + j, byte kq
+    const uint32_t* wsw = reinterpret_cast<const uint32_t*>(p.w_scale) + ((int64_t)g * N + n) * KT + kb0;
 #pragma unroll
-  for (int j = 0; j < kF8MaxSteps; ++j) sbx[j] = (int)((wsb[j] >> 23) & 0xFF);
+    for (int j = 0; j < kF8MaxSteps; ++j) sbx[j] = (int)((wsw[min(j, steps - 1)] >> (8 * kq)) & 0xFF);
+  } else {
+    const float* wsc = p.w_scale + ((int64_t)g * (N >> 7) + (n0 >> 7)) * KT + kb0;
+    uint32_t wsb[kF8MaxSteps];
+#pragma unroll
+    for (int j = 0; j < kF8MaxSteps; ++j) wsb[j] = __float_as_uint(wsc[min(j, steps - 1)]);
+    static_assert(kF8MaxSteps == 8, "one pin for the eight scales");
+    asm volatile("" : "+s"(wsb[0]), "+s"(wsb[1]), "+s"(wsb[2]), "+s"(wsb[3]), "+s"(wsb[4]), "+s"(wsb[5]),
+                 "+s"(wsb[6]), "+s"(wsb[7]));
+#pragma unroll
+    for (int j = 0; j < kF8MaxSteps; ++j) sbx[j] = (int)((wsb[j] >> 23) & 0xFF);
+  }
   v4f acc[TPW];
 #pragma unroll
   for (int rt = 0; rt < TPW; ++rt) {
@@ -112,9 +132,14 @@ __global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
     for (int j = 0; j < kF8MaxSteps; ++j) {
       if (j < steps) {  // uniform
         const int kb = kb0 + j;
-        const int q = (kb >> 2) - w0;  // 0, 1 or 2
-        const int32_t w = q == 0 ? words[rt & 1][0] : (q == 1 ? words[rt & 1][1] : words[rt & 1][2]);
-        const int sa = (w >> (8 * (kb & 3))) & 0xFF;
+        int sa;
+        if constexpr (MX) {
+          sa = (words[rt & 1][j] >> (8 * kq)) & 0xFF;  // this lane's 32-element block of block kb
+        } else {
+          const int q = (kb >> 2) - w0;  // 0, 1 or 2
+          const int32_t w = q == 0 ? words[rt & 1][0] : (q == 1 ? words[rt & 1][1] : words[rt & 1][2]);
+          sa = (w >> (8 * (kb & 3))) & 0xFF;
+        }
         // sbx[j]: the exponent field of the power-of-two weight block scale
         acc[rt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(abuf[rt & 1][j], b[j], acc[rt], 0, 0, 0, sa, 0, sbx[j]);
       }
@@ -264,17 +289,23 @@ bool fp8_decode_fits(int T, int N, int K) {
          K / (128 * kF8Waves) <= kF8MaxSteps;
 }
 
-hipError_t launch_fp8_decode(const TileArgs& a, int rt_per_wg, hipStream_t st) {
+hipError_t launch_fp8_decode(const TileArgs& a, int rt_per_wg, hipStream_t st, bool mx) {
   if (!fp8_decode_fits(a.M, a.N, a.K) || rt_per_wg < 1 || rt_per_wg > kF8MaxRT) return hipErrorInvalidValue;
   const int rt = (a.M + 15) / 16;
   const int tpw = min(rt_per_wg, rt);  // token tiles per workgroup
   const dim3 grid((unsigned)(a.N / kF8NT), (unsigned)a.batch, (unsigned)((rt + tpw - 1) / tpw));
+#define WQ_F8D(TP)                                                            \
+  if (mx)                                                                     \
+    hipLaunchKernelGGL((k_fp8_decode<TP, true>), grid, dim3(256), 0, st, a);  \
+  else                                                                        \
+    hipLaunchKernelGGL((k_fp8_decode<TP, false>), grid, dim3(256), 0, st, a);
   switch (tpw) {
-    case 1: hipLaunchKernelGGL(k_fp8_decode<1>, grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(k_fp8_decode<2>, grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL(k_fp8_decode<3>, grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL(k_fp8_decode<4>, grid, dim3(256), 0, st, a); break;
+    case 1: WQ_F8D(1) break;
+    case 2: WQ_F8D(2) break;
+    case 3: WQ_F8D(3) break;
+    default: WQ_F8D(4) break;
   }
+#undef WQ_F8D
   return hipGetLastError();
 }
 

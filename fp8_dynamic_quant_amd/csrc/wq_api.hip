@@ -443,6 +443,7 @@ static int fp8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   if (d->lda < K || d->ldy < N || d->a_batch_stride < 0 || d->y_batch_stride < 0) return WQ_ERR_SHAPE;
   const int64_t TA = (M + 3) / 4 * 4;
   if (d->a_scale_tokens < TA) return WQ_ERR_SHAPE;
+  const bool mx = d->payload == WQ_PAYLOAD_MXFP8;
   if (!d->a || !d->a_scale || !d->b || !d->b_scale || !d->y) return WQ_ERR_NULL;
   if (!al16(d->a) || !al16(d->b) || !al16(d->y) || !al16(d->a_scale) || d->lda % 16 != 0 ||
       d->a_batch_stride % 16 != 0 || (d->ldy * 2) % 16 != 0 || (d->y_batch_stride * 2) % 16 != 0 ||
@@ -463,6 +464,15 @@ static int fp8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   t.ldy = d->ldy;
   t.y_batch_stride = d->y_batch_stride;
   t.batch = (int)G;
+  if (mx) {
+    // MX-like 32-element blocks: the 16-column decode kernel, decode-sized T only
+    if (!wq::fp8_decode_fits((int)M, (int)N, (int)K)) return WQ_ERR_UNSUPPORTED;
+    hipError_t e = wq::launch_fp8_decode(t, c->fp8_rt > 0 ? c->fp8_rt : 4, st, true);
+    if (c->log)
+      std::fprintf(stderr, "[wq] quant_matmul mxfp8 decode M=%lld N=%lld K=%lld groups=%lld\n", (long long)M,
+                   (long long)N, (long long)K, (long long)G);
+    return status_of(e);
+  }
   if (c->fp8_cols == 32 && wq::fp8_decode32_fits((int)M, (int)N, (int)K)) {
     // 17..64 tokens: weight streaming, 32 columns x whole K per workgroup of 8 waves, every
     // token tile in flight at once (T = 64: 22.4 us with 16 columns, 17.3 us with 32)
@@ -502,7 +512,7 @@ int wq_quant_matmul(wq_ctx* c, const wq_matmul_desc* d, void* stream) {
   DeviceGuard g(c->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (d->payload == WQ_PAYLOAD_INT8) return int8_matmul(c, d, st);
-  if (d->payload == WQ_PAYLOAD_FP8_E4M3) return fp8_matmul(c, d, st);
+  if (d->payload == WQ_PAYLOAD_FP8_E4M3 || d->payload == WQ_PAYLOAD_MXFP8) return fp8_matmul(c, d, st);
   return WQ_ERR_SHAPE;
 }
 

@@ -87,7 +87,8 @@ bool big_fits(int M, int N, int K, int64_t lda, int64_t ldy);
 // FP8 grouped contraction for T <= 64, K % 512 == 0, K <= 4096 (k_fp8_decode.hip):
 // 16 output columns of one group and min(rt_per_wg, ceil(T / 16)) 16-token tiles per
 // workgroup, grid (N / 16, G, ceil(ceil(T / 16) / that))
-hipError_t launch_fp8_decode(const TileArgs& a, int rt_per_wg, hipStream_t st);
+// mx: 32-element blocks (activation storage [G, K/128, TA]; w_scale UE8M0 bytes [G][N][K/32])
+hipError_t launch_fp8_decode(const TileArgs& a, int rt_per_wg, hipStream_t st, bool mx = false);
 bool fp8_decode_fits(int T, int N, int K);
 // 32 output columns of one group per workgroup of 8 waves, all token tiles (16 < T <= 64,
 // K % 1024 == 0, K <= 4096, N % 32 == 0), grid (N / 32, G); at T <= 16 the 16-column

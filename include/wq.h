@@ -50,7 +50,7 @@ enum {
 /* input element types */
 enum { WQ_IN_BF16 = 1, WQ_IN_F32 = 2 };
 /* GEMM payload types */
-enum { WQ_PAYLOAD_INT8 = 1, WQ_PAYLOAD_FP8_E4M3 = 2 };
+enum { WQ_PAYLOAD_INT8 = 1, WQ_PAYLOAD_FP8_E4M3 = 2, WQ_PAYLOAD_MXFP8 = 3 };
 /* GEMM epilogues */
 enum { WQ_EPI_BF16 = 1, WQ_EPI_SWIGLU_F32 = 2 };
 /* weight layout of wq_matmul_desc.b: plain [batch][N][K], or the fragment order of
@@ -175,9 +175,15 @@ int wq_group_quant_mxfp8(wq_ctx* ctx, const void* x, int64_t T, int64_t G, int64
  *   [G][N][K]; b_scale = f32 powers of two [G][N/128][K/128];
  *   y[m, g, n] = bf16_RN( sum_kb 2^(e_a(m,g,kb)) * b_scale[g, n/128, kb]
  *                         * sum_{k in block kb} a[m, g, k] * b[g, n, k] )   (f32 accumulate)
+ * MX-like 32-element blocks ("DeepSeek V4 950 低精度优化全复盘", section 2.1): payload
+ *   WQ_PAYLOAD_MXFP8, as the FP8 payload but a_scale = the storage of wq_group_quant_mxfp8
+ *   ([G, K/128, TA]) and b_scale pointing at UE8M0 bytes [G][N][K/32] (not floats);
+ *   y[m, g, n] = bf16_RN( sum over 32-deep blocks kb of 2^(e_a(m,g,kb))
+ *                         * 2^(b_scale[g, n, kb] - 127) * sum_{k in kb} a[m,g,k] * b[g,n,k] );
+ *   decode-sized M only (M <= 64, K % 512 == 0, K <= 4096; else WQ_ERR_UNSUPPORTED).
  * acc_out (INT8 dense only, may be NULL): the raw int32 accumulators [M, N], row stride N. */
 typedef struct {
-  int32_t payload;         /* WQ_PAYLOAD_INT8 or WQ_PAYLOAD_FP8_E4M3                      */
+  int32_t payload;         /* WQ_PAYLOAD_INT8, WQ_PAYLOAD_FP8_E4M3 or WQ_PAYLOAD_MXFP8    */
   int32_t epilogue;        /* WQ_EPI_BF16 or WQ_EPI_SWIGLU_F32                            */
   int64_t M, N, K;         /* rows (per batch for strided batches), columns, depth        */
   int64_t batch;           /* 1 = dense; G for FP8 groups; E for segments                 */

@@ -124,6 +124,18 @@ def fp8_weights(seed=42, G=8, N=1024, D=4096, exp_range=4, normalish=True):
     return wq, ws
 
 
+def mx_weights(seed=43, G=8, N=1024, D=4096, exp_range=4):
+    """FP8 weights [G, N, D] (normal-like codes, as fp8_weights) with one UE8M0 scale byte
+    per (column, 32-deep block) [G, N, D/32], 127 + j with j uniform in [-exp_range, exp_range]."""
+    g = rng(5, seed, G, N, D, 1)
+    ef = g.integers(4, 10, size=(G, N, D), dtype=np.int64)
+    fr = g.integers(0, 8, size=(G, N, D), dtype=np.int64)
+    sg = g.integers(0, 2, size=(G, N, D), dtype=np.int64)
+    wq = ((sg << 7) | (ef << 3) | fr).astype(np.uint8)
+    wb = (127 + g.integers(-exp_range, exp_range + 1, size=(G, N, D // 32))).astype(np.uint8)
+    return wq, wb
+
+
 def zipf_topk_ids(key, T, E, TOPK, a=1.1):
     """[T, TOPK] distinct expert ids per token from a truncated Zipf(a) law over
     ranks 1..E (rank k -> expert k-1), drawn slot by slot without replacement."""

@@ -248,3 +248,88 @@ def test_mx_group_quant_empty_and_errors():
     assert tuple(xs.shape) == (0, 2, 1)
     rc = wq.lib().wq_group_quant_mxfp8(wq.context(DEV).handle, 0, 1, 1, 48, 0, 0, 0)
     assert rc == 2  # WQ_ERR_SHAPE: D not a multiple of 32
+
+
+# ---- MX-like contraction (payload WQ_PAYLOAD_MXFP8) ---------------------------------------
+
+def _check_mx_contraction(payload, eb, wq_codes, wb, y, bound_mult=1.0):
+    """eb: activation bytes [T, G, D/32]; wb: weight bytes [G, N, D/32]; same tolerance as
+    the 128-block contraction (A25): 1 bf16 ulp, or the f32 accumulation bound K 2^-24 S."""
+    y_ref, sabs = fg.mx_contraction(payload, fg.ebyte_to_scale(eb), wq_codes, fg.ebyte_to_scale(wb), return_abs=True)
+    got = host(y.view(torch.int16)).view(np.uint16)
+    d = nm.bf16_ulp_distance(got, y_ref)
+    diff = np.abs(nm.bf16_to_f32(got).astype(np.float64) - nm.bf16_to_f32(y_ref).astype(np.float64))
+    K = payload.shape[2]
+    ok = (d <= 1) | (diff <= bound_mult * K * 2.0 ** -24 * sabs)
+    assert ok.all(), f"{(~ok).sum()} outputs outside tolerance, max ulp {d.max()}"
+    assert (d <= 1).mean() >= 0.995
+    return d
+
+
+@pytest.mark.parametrize("T", [1, 7, 16, 33, 64])
+def test_mx_contraction_dsv4_wo_a(T):
+    G, D, N = 8, 4096, 1024
+    x = syn.fp8_group_x(T, G=G, D=D)
+    payload, storage, eb = fg.group_quant_fp8_packed(x, 32)
+    wq_codes, wb = syn.mx_weights(44, G=G, N=N, D=D)
+    y = wq.wq_quant_matmul(dev(payload), dev(storage), dev(wq_codes), dev(wb), fp8_groups=G, mx=True)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (T, G, N)
+    _check_mx_contraction(payload, eb, wq_codes, wb, y)
+
+
+@pytest.mark.parametrize("T,G,D,N", [(3, 2, 512, 128), (17, 1, 1536, 256), (64, 3, 2048, 384), (5, 1, 4096, 128)])
+def test_mx_contraction_small_shapes(T, G, D, N):
+    x = syn.fp8_group_x(T, G=G, D=D, layout_variant=True)
+    payload, storage, eb = fg.group_quant_fp8_packed(x, 32)
+    wq_codes, wb = syn.mx_weights(45, G=G, N=N, D=D)
+    y = wq.wq_quant_matmul(dev(payload), dev(storage), dev(wq_codes), dev(wb), fp8_groups=G, mx=True)
+    torch.cuda.synchronize()
+    _check_mx_contraction(payload, eb, wq_codes, wb, y)
+
+
+def test_mx_chain_gpu_quant_then_contraction():
+    T, G, D, N = 64, 8, 4096, 1024
+    x = syn.fp8_group_x(T, G=G, D=D)
+    xq, xs, st = wq.wq_group_quant_fp8_ue8m0(bf16_dev(x), group=32)
+    wq_codes, wb = syn.mx_weights(46, G=G, N=N, D=D)
+    y = wq.wq_quant_matmul(xq, st, dev(wq_codes), dev(wb), fp8_groups=G, mx=True)
+    torch.cuda.synchronize()
+    payload, storage, eb = fg.group_quant_fp8_packed(x, 32)
+    assert np.array_equal(host(xq), payload) and np.array_equal(host(st), storage)
+    _check_mx_contraction(payload, eb, wq_codes, wb, y)
+
+
+def test_mx_scales_are_per_32_element_block():
+    """One nonzero product per 32-element block of the first 128, each block with its own
+    activation and weight exponents: every output is the bf16 rounding of an exact sum of
+    four powers of two (exact in f32), so a scale applied to the wrong block, lane or byte
+    shows.  (K = 512, the smallest the decode kernel takes; blocks 4..15 are zero.)"""
+    T, G, D, N = 4, 1, 512, 128
+    xq = np.zeros((T, G, D), np.uint8)
+    wqc = np.zeros((G, N, D), np.uint8)
+    xq[:, 0, [0, 32, 64, 96]] = 0x38          # 1.0 in each of the first four blocks
+    wqc[0, :, [0, 32, 64, 96]] = 0x38
+    eb = np.full((T, G, D // 32), 127, np.uint8)
+    for t in range(T):
+        eb[t, 0, :4] = [127 + t, 127 - 2, 127 + 3, 127 - 5]
+    wb = np.full((G, N, D // 32), 127, np.uint8)
+    for n in range(N):
+        wb[0, n, :4] = [127, 127 + (n % 3), 127 - (n % 5), 127 + 1]
+    storage = fg.pack_ue8m0(eb)
+    y = wq.wq_quant_matmul(dev(xq), dev(storage), dev(wqc), dev(wb), fp8_groups=G, mx=True)
+    torch.cuda.synchronize()
+    got = nm.bf16_to_f32(host(y.view(torch.int16)).view(np.uint16)[:, 0, :]).astype(np.float64)
+    exact = np.array([[sum(2.0 ** (int(eb[t, 0, b]) - 127 + int(wb[0, n, b]) - 127) for b in range(4))
+                       for n in range(N)] for t in range(T)])
+    want = nm.bf16_to_f32(nm.f64_to_bf16_rn(exact)).astype(np.float64)  # one rounding of the exact sum
+    assert np.array_equal(got, want)
+
+
+def test_mx_contraction_unsupported_sizes():
+    G, D, N, T = 1, 4096, 128, 65
+    with pytest.raises(wq.WqError):
+        wq.wq_quant_matmul(torch.zeros((T, G, D), dtype=torch.uint8, device=DEV),
+                           torch.zeros((G, D // 128, 68), dtype=torch.int32, device=DEV),
+                           torch.zeros((G, N, D), dtype=torch.uint8, device=DEV),
+                           torch.zeros((G, N, D // 32), dtype=torch.uint8, device=DEV), fp8_groups=G, mx=True)
