@@ -507,6 +507,22 @@ def main():
                            "contraction_us": round(us_c, 3), "contraction_GBps": round(c_bytes / us_c / 1e3, 1),
                            "contraction_frac_hbm": round(c_bytes / us_c / 1e3 / HBM_PEAK_GBS, 4),
                            "contraction_TOPS": round(c_ops / us_c / 1e6, 2)}
+        # the MX-like 32-element blocks on both operands (decode-sized T)
+        wmx_h, wbx_h = syn.mx_weights(44, G=G8, N=N8, D=D8)
+        wmx = [torch.from_numpy(wmx_h).to(dev) for _ in range(R8)]
+        wbx = torch.from_numpy(wbx_h).to(dev)
+        mxc = {}
+        for T in (1, 64):
+            x8h = torch.from_numpy(syn.fp8_group_x(T, G=G8, D=D8).view(np.int16)).to(dev).view(torch.bfloat16)
+            qm, _, stmx = wq.wq_group_quant_fp8_ue8m0(x8h, group=32)
+            ym = torch.empty((T, G8, N8), dtype=torch.bfloat16, device=dev)
+            us = time_in_graph(lambda r: wq.wq_quant_matmul(qm, stmx, wmx[r], wbx, y=ym, fp8_groups=G8, mx=True), R8)
+            b = T * G8 * D8 + 4 * stmx.numel() + G8 * N8 * D8 + G8 * N8 * (D8 // 32) + 2 * T * G8 * N8
+            mxc[str(T)] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1), "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del wmx
+        rows["mx32_contraction"] = {"workload": "MX-like FP8: X E4M3 [T, 8, 4096] with 32-element UE8M0 scales (packed) x "
+                                                "W_g E4M3 [1024, 4096] with 32-element UE8M0 scales, bf16 out",
+                                    "kernel": "k_fp8_decode<TPW, true>", "by_T": mxc}
         rows["fp8_wo_a"] = {"workload": "X bf16 [T, 8, 4096] -> E4M3 + packed UE8M0 [8, 8, align4(T)]; "
                                         "out[T,g,:] = x_q[T,g,:] W_g^T, W_g E4M3 [1024, 4096], 128x128 pow2 scales",
                             "kernels": "k_group_quant_fp8 (k_group_quant_mx for 32-element blocks); k_fp8_decode (T <= 16), k_fp8_decode32 (16 < T <= 64), k_gemm_tile<FP8> (T > 64)", "by_T": fp8}
