@@ -512,7 +512,7 @@ def main():
         wmx = [torch.from_numpy(wmx_h).to(dev) for _ in range(R8)]
         wbx = torch.from_numpy(wbx_h).to(dev)
         mxc = {}
-        for T in (1, 64):
+        for T in (1, 64, 512):
             x8h = torch.from_numpy(syn.fp8_group_x(T, G=G8, D=D8).view(np.int16)).to(dev).view(torch.bfloat16)
             qm, _, stmx = wq.wq_group_quant_fp8_ue8m0(x8h, group=32)
             ym = torch.empty((T, G8, N8), dtype=torch.bfloat16, device=dev)
@@ -522,7 +522,8 @@ def main():
         del wmx
         rows["mx32_contraction"] = {"workload": "MX-like FP8: X E4M3 [T, 8, 4096] with 32-element UE8M0 scales (packed) x "
                                                 "W_g E4M3 [1024, 4096] with 32-element UE8M0 scales, bf16 out",
-                                    "kernel": "k_fp8_decode<TPW, true>", "by_T": mxc}
+                                    "kernels": "k_fp8_decode<TPW, true> (T <= 64), k_gemm_tile<true> with MX scales (T > 64)",
+                                    "by_T": mxc}
         rows["fp8_wo_a"] = {"workload": "X bf16 [T, 8, 4096] -> E4M3 + packed UE8M0 [8, 8, align4(T)]; "
                                         "out[T,g,:] = x_q[T,g,:] W_g^T, W_g E4M3 [1024, 4096], 128x128 pow2 scales",
                             "kernels": "k_group_quant_fp8 (k_group_quant_mx for 32-element blocks); k_fp8_decode (T <= 16), k_fp8_decode32 (16 < T <= 64), k_gemm_tile<FP8> (T > 64)", "by_T": fp8}

@@ -109,9 +109,13 @@ __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, c
         acc[i][j][e] = 0;
         acc2[i][j][e] = 0;
       }
-  const int PH = (KT + 3) >> 2;
+  // MX (FP8 only): one activation word per 128-deep block holds its four 32-element scales,
+  // and the weights have one such word per (column, block)
+  const bool mx = FP8 && p.mx != 0;
+  const int PH = mx ? KT : (KT + 3) >> 2;
   const int32_t* xs_g = FP8 ? p.a_scale_packed + (int64_t)g * PH * p.a_scale_tokens : nullptr;
-  const float* ws_g = FP8 ? p.w_scale + ((int64_t)g * (N / 128) + (n0 >> 7)) * KT : nullptr;
+  const float* ws_g = FP8 && !mx ? p.w_scale + ((int64_t)g * (N / 128) + (n0 >> 7)) * KT : nullptr;
+  const uint32_t* wsw_g = mx ? reinterpret_cast<const uint32_t*>(p.w_scale) + (int64_t)g * N * KT : nullptr;
 
   // issue slice kt into its ring stage: A, B (, B2) and, for FP8, the 128 rows' packed
   // scale words (wave w: rows m0 + 32w .. +31, one 4-byte word per lane 0..31) and the
@@ -125,9 +129,14 @@ __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, c
     dma_slice(B, K, n0, N, kt * kBK, st + kSlice, wv, lane, frag_n);
     if constexpr (DUAL) dma_slice(B, K, n0 + dual_off, N, kt * kBK, st + 2 * kSlice, wv, lane, frag_n);
     if constexpr (FP8) {
+      // MX: lanes 0..31 the rows' words for block kt, lanes 32..63 the words of columns
+      // n0 + 32w .. n0 + 32w + 31
       const int r = min(m0 + wv * 32 + (lane & 31), row_hi - 1);
-      const void* src = lane == 32 ? reinterpret_cast<const void*>(ws_g + kt)
-                                   : reinterpret_cast<const void*>(xs_g + (int64_t)(kt >> 2) * p.a_scale_tokens + r);
+      const void* src =
+          mx ? (lane < 32 ? reinterpret_cast<const void*>(xs_g + (int64_t)kt * p.a_scale_tokens + r)
+                          : reinterpret_cast<const void*>(wsw_g + (int64_t)min(n0 + wv * 32 + (lane & 31), N - 1) * KT + kt))
+             : lane == 32 ? reinterpret_cast<const void*>(ws_g + kt)
+                          : reinterpret_cast<const void*>(xs_g + (int64_t)(kt >> 2) * p.a_scale_tokens + r);
       __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(st + (DUAL ? 3 : 2) * kSlice + wv * 256), 4, 0, 0);
     }
   };
@@ -155,32 +164,44 @@ __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, c
     const int kh = lane >> 5;  // which half of the K step this lane carries
     if constexpr (FP8) {
       const int32_t* scw = reinterpret_cast<const int32_t*>(sa + 2 * kSlice);
-      int sca[2];
+      int rw[2], cw[2];  // the rows' and (MX) the columns' scale words of this slice
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = ar + i * 32;  // row in the tile; its word sits at (r / 32) * 64 + r % 32
-        sca[i] = (scw[(r >> 5) * 64 + (r & 31)] >> (8 * (kt & 3))) & 0xFF;
+        rw[i] = scw[(r >> 5) * 64 + (r & 31)];
+        const int c = br + i * 32;  // column in the tile (MX): at (c / 32) * 64 + 32 + c % 32
+        cw[i] = mx ? scw[(c >> 5) * 64 + 32 + (c & 31)] : 0;
       }
-      const int scb = (scw[32] >> 23) & 0xFF;  // exponent field of the f32 power-of-two block scale
-      // two K=64 MFMAs per slice; a lane carries 32 bytes = chunks 4*ks + 2*kh, +1
+      const int scb128 = (scw[32] >> 23) & 0xFF;  // exponent field of the f32 power-of-two block scale
+      // two K=64 MFMAs per slice.  Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4: lane
+      // group h (lanes 32h .. 32h+31) holds K bytes 16h .. 16h+15 of the step in its first
+      // four registers and 32+16h .. 32+16h+15 in the last four, and the scale operand of
+      // lane group h applies to K bytes 32h .. 32h+31 of the step.  With one scale per
+      // 128-deep block any K order shared by both operands gives the same sum, so the
+      // 128-block path keeps its contiguous 32 bytes per lane.
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
+        const int c0 = mx ? 4 * ks + kh : 4 * ks + 2 * kh, c1 = mx ? 4 * ks + 2 + kh : 4 * ks + 2 * kh + 1;
         v8i af[2], bf[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const v4i lo = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 32, 4 * ks + 2 * kh));
-          const v4i hi = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 32, 4 * ks + 2 * kh + 1));
+          const v4i lo = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 32, c0));
+          const v4i hi = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 32, c1));
           af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const v4i blo = *reinterpret_cast<const v4i*>(sb + tswz(br + i * 32, 4 * ks + 2 * kh));
-          const v4i bhi = *reinterpret_cast<const v4i*>(sb + tswz(br + i * 32, 4 * ks + 2 * kh + 1));
+          const v4i blo = *reinterpret_cast<const v4i*>(sb + tswz(br + i * 32, c0));
+          const v4i bhi = *reinterpret_cast<const v4i*>(sb + tswz(br + i * 32, c1));
           bf[i] = v8i{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
         }
+        const int sub = 2 * ks + kh;  // MX: this lane group's 32-element block of the slice
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i) {
+          const int sca = mx ? (rw[i] >> (8 * sub)) & 0xFF : (rw[i] >> (8 * (kt & 3))) & 0xFF;
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, sca[i], 0,
-                                                                         scb);
+          for (int j = 0; j < 2; ++j) {
+            const int scb = mx ? (cw[j] >> (8 * sub)) & 0xFF : scb128;
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, sca, 0, scb);
+          }
+        }
       }
     } else {
       // four K=32 MFMAs per slice; a lane carries 16 bytes = chunk 2*ks + kh

@@ -464,16 +464,17 @@ static int fp8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   t.ldy = d->ldy;
   t.y_batch_stride = d->y_batch_stride;
   t.batch = (int)G;
-  if (mx) {
-    // MX-like 32-element blocks: the 16-column decode kernel, decode-sized T only
-    if (!wq::fp8_decode_fits((int)M, (int)N, (int)K)) return WQ_ERR_UNSUPPORTED;
+  t.mx = mx ? 1 : 0;
+  if (mx && wq::fp8_decode_fits((int)M, (int)N, (int)K)) {
+    // MX-like 32-element blocks at decode-sized T: the 16-column decode kernel (larger T:
+    // the tiled kernel below)
     hipError_t e = wq::launch_fp8_decode(t, c->fp8_rt > 0 ? c->fp8_rt : 4, st, true);
     if (c->log)
       std::fprintf(stderr, "[wq] quant_matmul mxfp8 decode M=%lld N=%lld K=%lld groups=%lld\n", (long long)M,
                    (long long)N, (long long)K, (long long)G);
     return status_of(e);
   }
-  if (c->fp8_cols == 32 && wq::fp8_decode32_fits((int)M, (int)N, (int)K)) {
+  if (!mx && c->fp8_cols == 32 && wq::fp8_decode32_fits((int)M, (int)N, (int)K)) {
     // 17..64 tokens: weight streaming, 32 columns x whole K per workgroup of 8 waves, every
     // token tile in flight at once (T = 64: 22.4 us with 16 columns, 17.3 us with 32)
     hipError_t e = wq::launch_fp8_decode32(t, st);
@@ -482,7 +483,7 @@ static int fp8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
                    (long long)M, (long long)N, (long long)K, (long long)G, (long long)(N / 32), (long long)G);
     return status_of(e);
   }
-  if (wq::fp8_decode_fits((int)M, (int)N, (int)K)) {
+  if (!mx && wq::fp8_decode_fits((int)M, (int)N, (int)K)) {
     // up to 16 tokens (or K not a multiple of 1024): weight streaming, 16 columns x whole K
     // per workgroup (T = 1: 9.1 us, against 10.1 us with 32 columns)
     // all token tiles in one workgroup: splitting them over more workgroups re-reads the

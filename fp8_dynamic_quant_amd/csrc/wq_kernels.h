@@ -68,6 +68,7 @@ struct TileArgs {
   int64_t y_batch_stride;      // strided groups: elements between groups of y
   int seg_min_rows;            // segments: experts with fewer rows are left to another kernel
   int b_frag;                  // INT8 segments: each expert's w in the fragment order of launch_pack_weight_i8
+  int mx;                      // FP8: MX-like 32-element blocks (storage [G, K/128, TA]; w_scale bytes [G][N][K/32])
 };
 hipError_t launch_gemm_i8_tile(const TileArgs& a, hipStream_t st);
 // 128x128 tiles with DMA-fed LDS (k_gemm_tile.hip); K % 128 == 0

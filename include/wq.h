@@ -180,7 +180,7 @@ int wq_group_quant_mxfp8(wq_ctx* ctx, const void* x, int64_t T, int64_t G, int64
  *   ([G, K/128, TA]) and b_scale pointing at UE8M0 bytes [G][N][K/32] (not floats);
  *   y[m, g, n] = bf16_RN( sum over 32-deep blocks kb of 2^(e_a(m,g,kb))
  *                         * 2^(b_scale[g, n, kb] - 127) * sum_{k in kb} a[m,g,k] * b[g,n,k] );
- *   decode-sized M only (M <= 64, K % 512 == 0, K <= 4096; else WQ_ERR_UNSUPPORTED).
+ *   any M (decode-sized M on the weight-streaming kernel, larger M on the tiled one).
  * acc_out (INT8 dense only, may be NULL): the raw int32 accumulators [M, N], row stride N. */
 typedef struct {
   int32_t payload;         /* WQ_PAYLOAD_INT8, WQ_PAYLOAD_FP8_E4M3 or WQ_PAYLOAD_MXFP8    */

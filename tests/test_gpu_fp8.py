@@ -266,7 +266,7 @@ def _check_mx_contraction(payload, eb, wq_codes, wb, y, bound_mult=1.0):
     return d
 
 
-@pytest.mark.parametrize("T", [1, 7, 16, 33, 64])
+@pytest.mark.parametrize("T", [1, 7, 16, 33, 64, 65, 512])
 def test_mx_contraction_dsv4_wo_a(T):
     G, D, N = 8, 4096, 1024
     x = syn.fp8_group_x(T, G=G, D=D)
@@ -278,7 +278,8 @@ def test_mx_contraction_dsv4_wo_a(T):
     _check_mx_contraction(payload, eb, wq_codes, wb, y)
 
 
-@pytest.mark.parametrize("T,G,D,N", [(3, 2, 512, 128), (17, 1, 1536, 256), (64, 3, 2048, 384), (5, 1, 4096, 128)])
+@pytest.mark.parametrize("T,G,D,N", [(3, 2, 512, 128), (17, 1, 1536, 256), (64, 3, 2048, 384), (5, 1, 4096, 128),
+                                     (130, 2, 256, 256), (3, 3, 384, 128), (200, 1, 1152, 384)])
 def test_mx_contraction_small_shapes(T, G, D, N):
     x = syn.fp8_group_x(T, G=G, D=D, layout_variant=True)
     payload, storage, eb = fg.group_quant_fp8_packed(x, 32)
@@ -300,19 +301,21 @@ def test_mx_chain_gpu_quant_then_contraction():
     _check_mx_contraction(payload, eb, wq_codes, wb, y)
 
 
-def test_mx_scales_are_per_32_element_block():
+@pytest.mark.parametrize("T", [4, 70])
+def test_mx_scales_are_per_32_element_block(T):
     """One nonzero product per 32-element block of the first 128, each block with its own
     activation and weight exponents: every output is the bf16 rounding of an exact sum of
     four powers of two (exact in f32), so a scale applied to the wrong block, lane or byte
-    shows.  (K = 512, the smallest the decode kernel takes; blocks 4..15 are zero.)"""
-    T, G, D, N = 4, 1, 512, 128
+    shows.  (K = 512, the smallest the decode kernel takes; blocks 4..15 are zero.)  T = 4
+    runs the weight-streaming kernel, T = 70 the tiled one."""
+    G, D, N = 1, 512, 128
     xq = np.zeros((T, G, D), np.uint8)
     wqc = np.zeros((G, N, D), np.uint8)
     xq[:, 0, [0, 32, 64, 96]] = 0x38          # 1.0 in each of the first four blocks
     wqc[0, :, [0, 32, 64, 96]] = 0x38
     eb = np.full((T, G, D // 32), 127, np.uint8)
     for t in range(T):
-        eb[t, 0, :4] = [127 + t, 127 - 2, 127 + 3, 127 - 5]
+        eb[t, 0, :4] = [127 + t % 7, 127 - 2, 127 + 3, 127 - 5]
     wb = np.full((G, N, D // 32), 127, np.uint8)
     for n in range(N):
         wb[0, n, :4] = [127, 127 + (n % 3), 127 - (n % 5), 127 + 1]
@@ -324,12 +327,3 @@ def test_mx_scales_are_per_32_element_block():
                        for n in range(N)] for t in range(T)])
     want = nm.bf16_to_f32(nm.f64_to_bf16_rn(exact)).astype(np.float64)  # one rounding of the exact sum
     assert np.array_equal(got, want)
-
-
-def test_mx_contraction_unsupported_sizes():
-    G, D, N, T = 1, 4096, 128, 65
-    with pytest.raises(wq.WqError):
-        wq.wq_quant_matmul(torch.zeros((T, G, D), dtype=torch.uint8, device=DEV),
-                           torch.zeros((G, D // 128, 68), dtype=torch.int32, device=DEV),
-                           torch.zeros((G, N, D), dtype=torch.uint8, device=DEV),
-                           torch.zeros((G, N, D // 32), dtype=torch.uint8, device=DEV), fp8_groups=G, mx=True)
