@@ -169,8 +169,11 @@ __global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
 // tiles.  Half as many workgroups read each token tile from L2 as with 16 columns, and all
 // token tiles are in flight at once (at most 56 vector loads per wave: 16 for the weights,
 // 8 per token tile for the fragments and 2 for its packed scale words).
-template <int TPW>
+// MX: the MX-like 32-element blocks, as in k_fp8_decode<TPW, true> (operands in the MFMA's
+// own K layout, per-lane scale bytes of the activation and column words)
+template <int TPW, bool MX>
 __global__ __launch_bounds__(512) void k_fp8_decode32(TileArgs p) {
+  constexpr int NWD = MX ? 4 : 2;  // packed activation words per token tile
   __shared__ float red[8][TPW][2][4][64];
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -180,9 +183,11 @@ __global__ __launch_bounds__(512) void k_fp8_decode32(TileArgs p) {
   const int steps = KT >> 3;             // 128-deep blocks per wave (1..4)
   const int kb0 = wv * steps;
   const int cl = lane & 15, kq = lane >> 4;
-  const int PH = (KT + 3) >> 2;
+  const int PH = MX ? KT : (KT + 3) >> 2;
   const int32_t* xs_g = p.a_scale_packed + (int64_t)g * PH * p.a_scale_tokens;
-  const int8_t* A = p.a + (int64_t)g * p.a_batch_stride + kq * 32;
+  // plain: a lane's 32 bytes of a block at 32 kq (halves 16 apart); MX: at 16 kq and 64 + 16 kq
+  const int koff = MX ? kq * 16 : kq * 32, khalf = MX ? 64 : 16;
+  const int8_t* A = p.a + (int64_t)g * p.a_batch_stride + koff;
   const int rt_lo = blockIdx.z * TPW;
   const int w0 = kb0 >> 2;               // the wave's blocks touch packed words w0 and w0 + 1 at most
 
@@ -190,43 +195,55 @@ __global__ __launch_bounds__(512) void k_fp8_decode32(TileArgs p) {
   v8i b[2][4];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
-    const int8_t* W = p.w + (int64_t)g * p.w_batch_stride + (int64_t)(n0 + ct * 16 + cl) * K + kq * 32;
+    const int8_t* W = p.w + (int64_t)g * p.w_batch_stride + (int64_t)(n0 + ct * 16 + cl) * K + koff;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int8_t* src = W + (int64_t)(kb0 + min(j, steps - 1)) * 128;
       const v4i lo = *reinterpret_cast<const v4i*>(src);
-      const v4i hi = *reinterpret_cast<const v4i*>(src + 16);
+      const v4i hi = *reinterpret_cast<const v4i*>(src + khalf);
       b[ct][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   }
   // ---- every token tile's fragments and packed scale words --------------------------------
   v8i a[TPW][4];
-  int32_t wd[TPW][2];
+  int32_t wd[TPW][NWD];
 #pragma unroll
   for (int rt = 0; rt < TPW; ++rt) {
     // rows past T read row T-1: they only feed output rows that are not stored
     const int row = min((rt_lo + rt) * 16 + cl, T - 1);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) wd[rt][q] = xs_g[(int64_t)min(w0 + q, PH - 1) * p.a_scale_tokens + row];
+    for (int q = 0; q < NWD; ++q)
+      wd[rt][q] = MX ? xs_g[(int64_t)(kb0 + min(q, steps - 1)) * p.a_scale_tokens + row]
+                     : xs_g[(int64_t)min(w0 + q, PH - 1) * p.a_scale_tokens + row];
     const int8_t* arow = A + (int64_t)row * p.lda;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int8_t* src = arow + (int64_t)(kb0 + min(j, steps - 1)) * 128;
       const v4i lo = *reinterpret_cast<const v4i*>(src);
-      const v4i hi = *reinterpret_cast<const v4i*>(src + 16);
+      const v4i hi = *reinterpret_cast<const v4i*>(src + khalf);
       a[rt][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   }
   __builtin_amdgcn_sched_barrier(0);
   // ---- weight block-scale exponents: both column tiles lie in one 128-column block --------
-  const float* wsc = p.w_scale + ((int64_t)g * (N >> 7) + (n0 >> 7)) * KT + kb0;
-  uint32_t wsb[4];
+  int sbx[2][4];  // [column tile][step]
+  if constexpr (MX) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) wsb[j] = __float_as_uint(wsc[min(j, steps - 1)]);
-  asm volatile("" : "+s"(wsb[0]), "+s"(wsb[1]), "+s"(wsb[2]), "+s"(wsb[3]));
-  int sbx[4];
+    for (int ct = 0; ct < 2; ++ct) {
+      const uint32_t* wsw =
+          reinterpret_cast<const uint32_t*>(p.w_scale) + ((int64_t)g * N + n0 + ct * 16 + cl) * KT + kb0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) sbx[j] = (int)((wsb[j] >> 23) & 0xFF);
+      for (int j = 0; j < 4; ++j) sbx[ct][j] = (int)((wsw[min(j, steps - 1)] >> (8 * kq)) & 0xFF);
+    }
+  } else {
+    const float* wsc = p.w_scale + ((int64_t)g * (N >> 7) + (n0 >> 7)) * KT + kb0;
+    uint32_t wsb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wsb[j] = __float_as_uint(wsc[min(j, steps - 1)]);
+    asm volatile("" : "+s"(wsb[0]), "+s"(wsb[1]), "+s"(wsb[2]), "+s"(wsb[3]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sbx[0][j] = sbx[1][j] = (int)((wsb[j] >> 23) & 0xFF);
+  }
 
   v4f acc[TPW][2];
 #pragma unroll
@@ -237,12 +254,17 @@ __global__ __launch_bounds__(512) void k_fp8_decode32(TileArgs p) {
     for (int j = 0; j < 4; ++j) {
       if (j < steps) {  // uniform
         const int kb = kb0 + j;
-        const int32_t w = (kb >> 2) == w0 ? wd[rt][0] : wd[rt][1];
-        const int sa = (w >> (8 * (kb & 3))) & 0xFF;
+        int sa;
+        if constexpr (MX) {
+          sa = (wd[rt][j] >> (8 * kq)) & 0xFF;
+        } else {
+          const int32_t w = (kb >> 2) == w0 ? wd[rt][0] : wd[rt][1];
+          sa = (w >> (8 * (kb & 3))) & 0xFF;
+        }
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
           acc[rt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[rt][j], b[ct][j], acc[rt][ct], 0, 0, 0, sa,
-                                                                         0, sbx[j]);
+                                                                         0, sbx[ct][j]);
       }
     }
   }
@@ -272,15 +294,21 @@ bool fp8_decode32_fits(int T, int N, int K) {
   return T > 16 && T <= 16 * kF8MaxRT && N % 32 == 0 && K % 1024 == 0 && K <= 4096;
 }
 
-hipError_t launch_fp8_decode32(const TileArgs& a, hipStream_t st) {
+hipError_t launch_fp8_decode32(const TileArgs& a, hipStream_t st, bool mx) {
   if (!fp8_decode32_fits(a.M, a.N, a.K)) return hipErrorInvalidValue;
   const int rt = (a.M + 15) / 16;
   const dim3 grid((unsigned)(a.N / 32), (unsigned)a.batch, 1);
+#define WQ_F8D32(TP)                                                             \
+  if (mx)                                                                        \
+    hipLaunchKernelGGL((k_fp8_decode32<TP, true>), grid, dim3(512), 0, st, a);   \
+  else                                                                           \
+    hipLaunchKernelGGL((k_fp8_decode32<TP, false>), grid, dim3(512), 0, st, a);
   switch (rt) {
-    case 2: hipLaunchKernelGGL(k_fp8_decode32<2>, grid, dim3(512), 0, st, a); break;
-    case 3: hipLaunchKernelGGL(k_fp8_decode32<3>, grid, dim3(512), 0, st, a); break;
-    default: hipLaunchKernelGGL(k_fp8_decode32<4>, grid, dim3(512), 0, st, a); break;
+    case 2: WQ_F8D32(2) break;
+    case 3: WQ_F8D32(3) break;
+    default: WQ_F8D32(4) break;
   }
+#undef WQ_F8D32
   return hipGetLastError();
 }
 

@@ -465,6 +465,14 @@ static int fp8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   t.y_batch_stride = d->y_batch_stride;
   t.batch = (int)G;
   t.mx = mx ? 1 : 0;
+  if (mx && c->fp8_cols == 32 && wq::fp8_decode32_fits((int)M, (int)N, (int)K)) {
+    // MX-like 32-element blocks at 17..64 tokens: the 32-column decode kernel
+    hipError_t e = wq::launch_fp8_decode32(t, st, true);
+    if (c->log)
+      std::fprintf(stderr, "[wq] quant_matmul mxfp8 decode32 M=%lld N=%lld K=%lld groups=%lld\n", (long long)M,
+                   (long long)N, (long long)K, (long long)G);
+    return status_of(e);
+  }
   if (mx && wq::fp8_decode_fits((int)M, (int)N, (int)K)) {
     // MX-like 32-element blocks at decode-sized T: the 16-column decode kernel (larger T:
     // the tiled kernel below)

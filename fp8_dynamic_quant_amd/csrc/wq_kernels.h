@@ -94,7 +94,7 @@ bool fp8_decode_fits(int T, int N, int K);
 // 32 output columns of one group per workgroup of 8 waves, all token tiles (16 < T <= 64,
 // K % 1024 == 0, K <= 4096, N % 32 == 0), grid (N / 32, G); at T <= 16 the 16-column
 // kernel is faster (one token tile: the activation re-reads it saves are few)
-hipError_t launch_fp8_decode32(const TileArgs& a, hipStream_t st);
+hipError_t launch_fp8_decode32(const TileArgs& a, hipStream_t st, bool mx = false);
 bool fp8_decode32_fits(int T, int N, int K);
 
 // FP8 group quant with packed UE8M0 scales (k_fp8.hip).
