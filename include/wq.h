@@ -89,10 +89,14 @@ size_t wq_workspace_bytes(void);
  *                     workgroup of that MFMA kernel (0 = auto; see wq_ctx_set_fused_shape);
  *   WQ_SEG_SMALL=0    expert segments: run every expert on the tiled kernel instead of
  *                     sending the experts with at most 16 rows to the streaming kernel;
- *   WQ_FP8_RT=r       grouped FP8 contraction at T <= 64: 16-token tiles per workgroup
- *                     (1..4; 0 = auto, all of them).
+ *   WQ_FP8_RT=r       grouped FP8 contraction at T <= 16: 16-token tiles per workgroup
+ *                     (1..4; 0 = auto, all of them);
+ *   WQ_FP8_COLS=16    grouped FP8 contraction at 16 < T <= 64: keep the 16-column kernel
+ *                     instead of the 32-column one (default 32).
  * Values out of range fall back to the default.  Every setting gives bit-identical
- * results; the knobs exist for tests and measurement. */
+ * results except WQ_FP8_COLS, which changes the order of the FP8 contraction's f32 sums
+ * (4 or 8 partial sums per output; both within the contraction's stated tolerance).  The
+ * knobs exist for tests and measurement. */
 int wq_ctx_create(int device, void* workspace, size_t workspace_bytes, wq_ctx** out);
 void wq_ctx_destroy(wq_ctx* ctx);
 
