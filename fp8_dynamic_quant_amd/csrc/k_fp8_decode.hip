@@ -20,6 +20,9 @@
 //    a fixed order and written as bf16.
 // Above 16 tokens every workgroup re-reads each token tile from L2, 64 times per group at
 // N = 1024; k_fp8_decode32 below halves that with 32 columns per workgroup.
+// Both kernels also take the MX-like 32-element blocks of "重塑大模型推理数据流：DeepSeek
+// V4 950 低精度优化全复盘", section 2.1 (template flag MX): then every lane group passes
+// the scale bytes of its own 32-element block of activations and weights.
 #include "wq_device.h"
 #include "wq_kernels.h"
 
@@ -66,6 +69,7 @@ __global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
   // had cost a memory round trip per MFMA.  (At most 63 vector loads can be counted in
   // flight; the weight block scales are wave-uniform scalar loads outside that count.)
   // this wave's K blocks [kb0, kb0 + steps) touch at most 3 packed activation-scale words
+  // (with MX, one word per block: up to 8)
   const int w0 = kb0 >> 2;
   // ---- weights, 32 bytes per lane per 128-deep step, straight into the B layout ----------
   const int8_t* W = p.w + (int64_t)g * p.w_batch_stride + (int64_t)n * K + kq * 16;
