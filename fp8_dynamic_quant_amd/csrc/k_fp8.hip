@@ -39,52 +39,64 @@ __device__ __forceinline__ int ue8m0_exp(float a) {
   return e < -127 ? -127 : e;
 }
 
+// PPW packs per wave (consecutive packs of one (t, g)); their loads are issued first
+template <int PPW>
 __global__ __launch_bounds__(256) void k_group_quant_fp8(const uint16_t* __restrict__ x, int64_t T, int G,
                                                          int D, uint8_t* __restrict__ xq,
                                                          int32_t* __restrict__ xs) {
   const int lane = threadIdx.x & 63;
-  const int HG = D / 128, PH = (HG + 3) / 4;
+  const int HG = D / 128, PH = (HG + 3) / 4, PW = (PH + PPW - 1) / PPW;
   const int64_t TA = (T + 3) / 4 * 4;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t total = TA * G * PH;
+  const int64_t total = TA * G * PW;
   if (wid >= total) return;
-  const int p = (int)(wid % PH);
-  const int64_t tg = wid / PH;
+  const int pw = (int)(wid % PW);
+  const int64_t tg = wid / PW;
   const int g = (int)(tg % G);
   const int64_t t = tg / G;
-  const int q = lane >> 4;            // quarter: hidden group 4p + q
-  const int h = 4 * p + q;
-  int byte = 0;
-  if (t < T && h < HG) {
-    const int64_t off = (t * G + g) * (int64_t)D + (int64_t)h * 128 + (lane & 15) * 8;
-    const uint4 u = *reinterpret_cast<const uint4*>(x + off);
-    float v[8];
-    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+  const int q = lane >> 4;  // quarter: hidden group 4p + q
+  uint4 u[PPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w4[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
-    }
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-    const int e = ue8m0_exp(a);
-    const float sc = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-127, 126]
-    uint32_t lo = 0, hi = 0;
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[0], sc), __fmul_rn(v[1], sc), lo, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[2], sc), __fmul_rn(v[3], sc), lo, true);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[4], sc), __fmul_rn(v[5], sc), hi, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[6], sc), __fmul_rn(v[7], sc), hi, true);
-    *reinterpret_cast<uint2*>(xq + off) = uint2{lo, hi};
-    byte = e + 127;
+  for (int i = 0; i < PPW; ++i) {  // clamped in-range loads, all before the first use
+    const int h = min(4 * (pw * PPW + i) + q, HG - 1);
+    u[i] = *reinterpret_cast<const uint4*>(x + (min(t, T - 1) * G + g) * (int64_t)D + (int64_t)h * 128 + (lane & 15) * 8);
   }
-  // gather the four quarter bytes into lane 0 (quarters whose h >= HG contribute 0)
-  const int b1 = __shfl(byte, 16, 64), b2 = __shfl(byte, 32, 64), b3 = __shfl(byte, 48, 64);
-  if (lane == 0) {
-    const uint32_t word = (uint32_t)byte | ((uint32_t)b1 << 8) | ((uint32_t)b2 << 16) | ((uint32_t)b3 << 24);
-    xs[((int64_t)g * PH + p) * TA + t] = (int32_t)word;
+#pragma unroll
+  for (int i = 0; i < PPW; ++i) {
+    const int p = pw * PPW + i;
+    if (p >= PH) break;  // uniform
+    const int h = 4 * p + q;
+    int byte = 0;
+    if (t < T && h < HG) {
+      const int64_t off = (t * G + g) * (int64_t)D + (int64_t)h * 128 + (lane & 15) * 8;
+      float v[8];
+      const uint32_t w4[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(w4[j] << 16);
+        v[2 * j + 1] = __uint_as_float(w4[j] & 0xFFFF0000u);
+      }
+      float a = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(v[j]));
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+      const int e = ue8m0_exp(a);
+      const float sc = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-127, 126]
+      uint32_t lo = 0, hi = 0;
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[0], sc), __fmul_rn(v[1], sc), lo, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[2], sc), __fmul_rn(v[3], sc), lo, true);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[4], sc), __fmul_rn(v[5], sc), hi, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[6], sc), __fmul_rn(v[7], sc), hi, true);
+      *reinterpret_cast<uint2*>(xq + off) = uint2{lo, hi};
+      byte = e + 127;
+    }
+    // gather the four quarter bytes into lane 0 (quarters whose h >= HG contribute 0)
+    const int b1 = __shfl(byte, 16, 64), b2 = __shfl(byte, 32, 64), b3 = __shfl(byte, 48, 64);
+    if (lane == 0) {
+      const uint32_t word = (uint32_t)byte | ((uint32_t)b1 << 8) | ((uint32_t)b2 << 16) | ((uint32_t)b3 << 24);
+      xs[((int64_t)g * PH + p) * TA + t] = (int32_t)word;
+    }
   }
 }
 
@@ -159,10 +171,17 @@ hipError_t launch_group_quant_fp8(const uint16_t* x, int64_t T, int G, int D, ui
                                   hipStream_t st) {
   const int HG = D / 128, PH = (HG + 3) / 4;
   const int64_t TA = (T + 3) / 4 * 4;
-  const int64_t waves = TA * G * PH;
+  // two packs per wave once the grid is large (>= 64 waves per CU at one pack per
+  // wave): fewer, longer waves with both loads in flight measured faster there and
+  // slower on small grids
+  const int ppw = TA * G * PH >= 16384 ? 2 : 1;
+  const int64_t waves = TA * G * ((PH + ppw - 1) / ppw);
   if (waves == 0) return hipSuccess;
   dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-  hipLaunchKernelGGL(k_group_quant_fp8, grid, block, 0, st, x, T, G, D, xq, xs);
+  if (ppw == 2)
+    hipLaunchKernelGGL(k_group_quant_fp8<2>, grid, block, 0, st, x, T, G, D, xq, xs);
+  else
+    hipLaunchKernelGGL(k_group_quant_fp8<1>, grid, block, 0, st, x, T, G, D, xq, xs);
   return hipGetLastError();
 }
 

@@ -46,6 +46,13 @@ def test_group_quant_pack_tails(T, G, D):
     _check(syn.fp8_group_x(T, G=G, D=D, layout_variant=True))
 
 
+@pytest.mark.parametrize("T,G,D", [(1023, 6, 1152), (2048, 4, 1024)])
+def test_group_quant_large_grid(T, G, D):
+    # TA * G * PH >= 16384: the kernel takes two packs per wave; PH = 3 leaves the
+    # second pack of the last wave per (t, g) empty
+    _check(syn.fp8_group_x(T, G=G, D=D, layout_variant=True))
+
+
 def test_group_quant_poisoned_storage_fully_written():
     T, G, D = 6, 3, 640
     x = syn.fp8_group_x(T, G=G, D=D, layout_variant=True)
