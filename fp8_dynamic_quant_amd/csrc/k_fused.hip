@@ -188,7 +188,7 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
     const uint32_t a = r < rows ? wave_umax(bf16x8_absmax_bits(xr[r])) : 0u;  // uniform
     if (lane == 0) wmax[r * kFW + wv] = a;
   }
-  __syncthreads();
+  lds_barrier();  // the weight loads stay in flight through the quantisation
   // lane r < R combines row r's 8 wave maxima and derives s = RN(a/127), inv = RN(1/s)
   float s_l = 0.0f, inv_l = 0.0f;
   if (lane < R) {

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
       const int later = min(kStages - 2, total - 1 - s);
       wait_vm_slices(later);
     }
-    __syncthreads();  // slice s is in LDS everywhere; the stage of slice s-1 is free
+    lds_barrier();  // slice s is in LDS everywhere; the stage of slice s-1 is free
     if (KT > 1 && s % KT == 1) scl[(s / KT) & 1][t] = scale_v;  // loaded with slice s - 1, now waited for
     if (s % KT == 0) load_scale(s);
     if (s + kStages - 1 < total) issue(s + kStages - 1);

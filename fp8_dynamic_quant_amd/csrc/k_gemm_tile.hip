@@ -155,7 +155,7 @@ __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, c
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    __syncthreads();  // slice kt is in LDS for everyone; the stage of slice kt-1 is free
+    lds_barrier();  // slice kt is in LDS for everyone; the stage of slice kt-1 is free
     if (kt + Ring::kStages - 1 < KT) issue(kt + Ring::kStages - 1);
     int8_t* sa = smem + (kt % Ring::kStages) * Ring::kStageB;
     int8_t* sb = sa + kSlice;

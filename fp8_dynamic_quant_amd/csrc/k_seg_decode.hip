@@ -155,7 +155,7 @@ __global__ __launch_bounds__(512) void k_seg_decode(TileArgs p) {
       red[wv][0][i][lane] = accg[i];
       red[wv][1][i][lane] = accu[i];
     }
-    __syncthreads();
+    lds_barrier();  // the next item's loads stay in flight through the epilogue
     if (EPI == 2 ? t < 256 : true) {
       const Item it = item_of(item);
       if (orow < it.rows) {
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(512) void k_seg_decode(TileArgs p) {
         }
       }
     }
-    __syncthreads();  // red is reused by the next item
+    lds_barrier();  // red is reused by the next item
   };
 
   int item = blockIdx.x;

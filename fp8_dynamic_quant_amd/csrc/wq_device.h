@@ -14,6 +14,15 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 
+// Workgroup barrier for hand-offs through LDS.  __syncthreads() also carries a workgroup
+// release fence, which the compiler implements by waiting for every outstanding global
+// load first (s_waitcnt vmcnt(0)): loads issued ahead on purpose (the later slices of an
+// LDS-DMA ring, the next item's operands) then land before anyone passes the barrier.
+// This barrier waits only for the wave's own LDS operations; a wave that needs its LDS-DMA
+// data waits for it with an explicit vmcnt first.  The memory clobber keeps the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // bf16 bits -> f32: the bf16 pattern is the high half of the binary32 pattern.
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
