@@ -106,7 +106,8 @@ def traffic_summary(fetch_dir, write_dir, probe_log):
             "--traffic-probe > gpurun_out/tr_fetch.log",
             "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/tr_write -o run --output-format csv -- python bench.py "
             "--traffic-probe > gpurun_out/tr_write.log",
-            "python bench.py --traffic-summary gpurun_out/tr_fetch gpurun_out/tr_write gpurun_out/tr_fetch.log",
+            "python bench.py --traffic-summary gpurun_out/tr_fetch gpurun_out/tr_write gpurun_out/tr_fetch.log "
+            "> profiles/traffic_k_fused_decode_wq_a.json",
         ],
         "calibration": {"kernel": "__amd_rocclr_copyBuffer (torch copy_ of 64 MiB)", "bytes_read": nbytes,
                         "bytes_written": nbytes, "fetch_size_kib_read": fetch_cal, "write_size_kib_read": write_cal,
