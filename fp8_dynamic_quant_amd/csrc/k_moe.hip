@@ -8,9 +8,10 @@
 // One workgroup of 16 waves does a stable counting sort.  Wave w owns a contiguous chunk
 // of the pairs.  Pass 1: per-wave histograms in LDS.  Pass 2: an exclusive scan over
 // (expert, wave) in expert-major order gives each wave the first output slot of each
-// expert.  Pass 3: each wave walks its chunk 64 pairs at a time in order; lanes holding
-// the same id find each other with one ballot per id bit, so a lane's rank among equal
-// ids is the popcount of the lower matching lanes - the pair order is kept.
+// expert (each wave scans a block of it, then adds the earlier blocks' totals).  Pass 3:
+// each wave walks its chunk 64 pairs at a time in order; lanes holding the same id find
+// each other with one ballot per id bit, so a lane's rank among equal ids is the popcount
+// of the lower matching lanes - the pair order is kept.
 #include "wq_device.h"
 #include "wq_kernels.h"
 
@@ -23,6 +24,7 @@ __global__ __launch_bounds__(1024) void k_moe_sort(const int32_t* __restrict__ i
                                                    int32_t* __restrict__ perm, int32_t* __restrict__ row_token,
                                                    int64_t* __restrict__ offsets) {
   __shared__ int cnt[kSortMaxE * kSortWaves];  // [e][w]
+  __shared__ int blk_total[kSortWaves];         // the scan's per-wave block totals
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   for (int i = t; i < E * kSortWaves; i += 1024) cnt[i] = 0;
   __syncthreads();
@@ -33,22 +35,31 @@ __global__ __launch_bounds__(1024) void k_moe_sort(const int32_t* __restrict__ i
     if (id >= 0 && id < E) atomicAdd(&cnt[id * kSortWaves + w], 1);
   }
   __syncthreads();
-  // exclusive scan over cnt in (e, w) order, single wave
-  if (w == 0) {
+  // exclusive scan over cnt in (e, w) order, in two levels: each wave scans its own
+  // contiguous block of whole 64-entry chunks (a serial chain of total / 1024 chunks rather
+  // than total / 64), then adds the totals of the blocks before it
+  {
     const int total = E * kSortWaves;
+    const int per = ((total + kSortWaves - 1) / kSortWaves + 63) & ~63;
+    const int b0 = w * per, b1 = min(total, b0 + per);
     int carry = 0;
-    for (int base = 0; base < total; base += 64) {
+    for (int base = b0; base < b1; base += 64) {
       const int i = base + lane;
-      const int v = (i < total) ? cnt[i] : 0;
+      const int v = (i < b1) ? cnt[i] : 0;
       int incl = v;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int u = __shfl_up(incl, o, 64);
         if (lane >= o) incl += u;
       }
-      if (i < total) cnt[i] = carry + incl - v;
+      if (i < b1) cnt[i] = carry + incl - v;
       carry += __shfl(incl, 63, 64);
     }
+    if (lane == 0) blk_total[w] = carry;
+    __syncthreads();
+    int off = 0;
+    for (int j = 0; j < w; ++j) off += blk_total[j];
+    for (int i = b0 + lane; i < b1; i += 64) cnt[i] += off;
   }
   __syncthreads();
   for (int e = t; e <= E; e += 1024) offsets[e] = (e < E) ? (int64_t)cnt[e * kSortWaves] : (int64_t)n;
