@@ -15,7 +15,9 @@
 // from v_cvt_pk_fp8_f32 (OCP E4M3FN, round to nearest even) applied to x * 2^-e, an exact
 // power-of-two scaling.  The four exponent bytes meet in lane 0, which writes the whole
 // packed word - no byte-granular read-modify-write and no dependence on prior contents.
-// Waves with t in [T, TA) write the zero padding words.
+// Waves with t in [T, TA) write the zero padding words.  On large grids (16384 waves or
+// more at one pack per wave) a wave takes two consecutive packs of its (t, g), with both
+// packs' loads issued before the first is quantised.
 #include "wq_device.h"
 #include "wq_kernels.h"
 
