@@ -52,7 +52,7 @@ struct TileRing {
 };
 constexpr int kDenseStages = 4;
 template <int EPI>
-constexpr int seg_stages() { return EPI == 2 ? 2 : 3; }
+constexpr int seg_stages() { return EPI == 2 ? 3 : 4; }
 constexpr int kGroupM = 8;         // tile rows per group in the L2-friendly tile order
 constexpr int kMaxSegTiles = kSegMaxPairs;  // (expert, row tile) pairs a persistent workgroup lists
 
@@ -342,9 +342,9 @@ __global__ __launch_bounds__(256) void k_gemm_tile(TileArgs p, int tiles_m, int 
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-  __shared__ int pair_e[kMaxSegTiles];
-  __shared__ int pair_m[kMaxSegTiles];
-  __shared__ int npairs;
+  // one word per (expert, row tile) pair: expert << 16 | tile index within the expert
+  // (16 KiB, so that with three SwiGLU stages of 48 KiB the workgroup holds 160 KiB)
+  __shared__ int pair_list[kMaxSegTiles];
   const int t = threadIdx.x;
   // list the non-empty (expert, row tile) pairs, in expert order (one wave, scan by shuffles)
   if (t < 64) {
@@ -365,24 +365,23 @@ __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
         if (t >= o) incl += u;
       }
       const int start = base + incl - cnt;
-      for (int j = 0; j < cnt; ++j) {
-        if (start + j < kMaxSegTiles) {
-          pair_e[start + j] = e;
-          pair_m[start + j] = (int)lo + j * kBM;
-        }
-      }
+      for (int j = 0; j < cnt; ++j)
+        if (start + j < kMaxSegTiles) pair_list[start + j] = (e << 16) | j;
       base += __shfl(incl, 63, 64);
     }
-    if (t == 0) npairs = base < kMaxSegTiles ? base : kMaxSegTiles;
+    // the count goes through the ring's first word, which no DMA touches before the
+    // mainloop's opening barrier
+    if (t == 0) *reinterpret_cast<int*>(smem) = base < kMaxSegTiles ? base : kMaxSegTiles;
   }
   __syncthreads();
-  const int npair = npairs;
+  const int npair = *reinterpret_cast<const int*>(smem);
   const int nn = (EPI == 2) ? (p.N / 2 + kBN - 1) / kBN : tiles_n;
   const int total = npair * nn;
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int pi = item / nn, tn = item - pi * nn;
-    const int e = pair_e[pi];
-    const int m0 = pair_m[pi];
+    const int pw = pair_list[pi];
+    const int e = pw >> 16;
+    const int m0 = (int)p.seg_offsets[e] + (pw & 0xFFFF) * kBM;
     const int row_hi = (int)p.seg_offsets[e + 1];
     const int8_t* B = p.w + (int64_t)e * p.w_batch_stride;
     const float* wsc = p.w_scale + (int64_t)e * p.N;
