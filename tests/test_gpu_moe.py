@@ -121,15 +121,23 @@ def test_moe_block_full_size_sampled_experts():
         assert nm.bf16_ulp_distance(host_bf16_bits(g["y"][lo:hi]), y).max() <= 1
 
 
+BOUNDARY_COUNTS = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 129]
+# experts of three to five 128-row tiles between small ones: the tiled kernel's work list
+# names a tile by its index within the expert
+MANY_TILE_COUNTS = [300, 0, 513, 1, 256, 257, 16, 384]
+
+
+@pytest.mark.parametrize("counts", [BOUNDARY_COUNTS, MANY_TILE_COUNTS], ids=["boundary", "many_tiles"])
 @pytest.mark.parametrize("frag", [False, True])
 @pytest.mark.parametrize("epi", ["bf16", "swiglu"])
-def test_segments_across_the_small_expert_boundary(epi, frag):
+def test_segments_across_the_small_expert_boundary(epi, frag, counts):
     """Expert row counts on both sides of the 16-row split between the weight-streaming
     kernel and the tiled one, and of the tiled kernel's 64- and 128-row marks (0, 1, 15,
-    16, 17, 31, 32, 33, 63, 64, 65, 129 rows), K = 1024 so both kernels take part; every
-    expert's rows against the oracle's dense per-expert product.
+    16, 17, 31, 32, 33, 63, 64, 65, 129 rows), and experts of several 128-row tiles;
+    K = 1024 so both kernels take part; every expert's rows against the oracle's dense
+    per-expert product.
     frag: the expert weights cast to fragment order (both kernels read that layout)."""
-    counts = np.array([0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 129], np.int64)
+    counts = np.array(counts, np.int64)
     E, K, N = counts.size, 1024, 512
     M = int(counts.sum())
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
