@@ -57,3 +57,7 @@ def test_host_only_calls():
     assert L.wq_quant_matmul(None, None, None) == 1
     assert L.wq_fused_quant_matmul(None, None, 1, 16, 16, None, None, 16, None, 16, None, None, None, None) == 1
     assert L.wq_moe_sort(None, None, 1, 1, 1, None, None, None, None) == 1
+    assert L.wq_pack_weight_i8(None, None, 16, 64, 64, None, None) == 1
+    assert L.wq_fused_quant_matmul_packed(None, None, 1, 16, 16, None, None, 16, None, 16, None, None, None,
+                                          None) == 1
+    assert L.wq_group_quant_mxfp8(None, None, 1, 1, 32, None, None, None) == 1
