@@ -163,11 +163,17 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
     const int c = CT == 1 ? (cl & (nt - 1)) : ct * 16 + cl;
     const int n = min(n0 + c, N - 1);
     if constexpr (PK) {
-      // fragment j of this wave: K step kbase/64 + j, a (N/4) x 256-byte row of 4-column blocks
+      // fragment j of this wave: K step kbase/64 + j, a (N/4) x 256-byte row of 4-column blocks.
+      // Streaming loads: the weights are read once per call in whole 1 KiB pieces and need
+      // no place in L2, which keeps it for the activation rows every workgroup re-reads
+      // (measured 3.80 -> 3.44 us at M = 1, 9.41 -> 9.13 us at M = 64).  The plain layout
+      // below reads half a 128-byte line per step and the other half one step later, so it
+      // keeps ordinary loads.
       const int8_t* wfr = p.w + ((int64_t)(kbase >> 6) * (N >> 2) + (n >> 2)) * 256 + kg * 64 + (n & 3) * 16;
 #pragma unroll
       for (int j = 0; j < kFMaxSteps; ++j)
-        b[ct][j] = *reinterpret_cast<const v4i*>(wfr + (int64_t)min(j, steps - 1) * (N >> 2) * 256);
+        b[ct][j] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4i*>(wfr + (int64_t)min(j, steps - 1) * (N >> 2) * 256));
     } else {
       const int8_t* wcol = p.w + (int64_t)n * K + kbase + 16 * kg;
 #pragma unroll

@@ -113,10 +113,15 @@ __global__ __launch_bounds__(512) void k_seg_decode(TileArgs p) {
       const int ngt = it.n0 + cl, nup = col2 + it.n0 + cl;
       const int8_t* Wg = We + (ngt >> 2) * 256 + (ngt & 3) * 16;
       const int8_t* Wu = We + (nup >> 2) * 256 + (nup & 3) * 16;
+      // streaming loads: each expert's weights are read once per call, in whole 1 KiB
+      // pieces, so they need no place in L2 (the activation rows, read by every item of the
+      // expert, keep theirs); measured 574 -> 539 us (gate/up) and 299 -> 277 us (down) per
+      // MoE block.  The plain layout below reads 64 of a line's 128 bytes per step and
+      // the other 64 one step later, so it keeps ordinary loads
 #pragma unroll
       for (int j = 0; j < STEPS; ++j) {
-        bg[j] = *reinterpret_cast<const v4i*>(Wg + (int64_t)j * N * 64);
-        bu[j] = *reinterpret_cast<const v4i*>(Wu + (int64_t)j * N * 64);
+        bg[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(Wg + (int64_t)j * N * 64));
+        bu[j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(Wu + (int64_t)j * N * 64));
       }
     } else {
       const int8_t* W = p.w + (int64_t)it.e * p.w_batch_stride + kbase + kg * 16;
