@@ -61,7 +61,15 @@ __global__ __launch_bounds__(256) void k_group_quant_fp8(const uint16_t* __restr
 #pragma unroll
   for (int i = 0; i < PPW; ++i) {  // clamped in-range loads, all before the first use
     const int h = min(4 * (pw * PPW + i) + q, HG - 1);
-    u[i] = *reinterpret_cast<const uint4*>(x + (min(t, T - 1) * G + g) * (int64_t)D + (int64_t)h * 128 + (lane & 15) * 8);
+    const uint16_t* src = x + (min(t, T - 1) * G + g) * (int64_t)D + (int64_t)h * 128 + (lane & 15) * 8;
+    if constexpr (PPW == 2) {
+      // large grids: streaming loads (the rows are read once; measured 14.7 -> 13.7 us at
+      // T = 512, while the small grids measured slower with them)
+      const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src));
+      u[i] = uint4{(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+    } else {
+      u[i] = *reinterpret_cast<const uint4*>(src);
+    }
   }
 #pragma unroll
   for (int i = 0; i < PPW; ++i) {
