@@ -116,6 +116,9 @@ __global__ __launch_bounds__(256) void k_group_quant_fp8(const uint16_t* __restr
 // pack p = 4 * pw + r, i.e. blocks 4p .. 4p+3 (128 bf16 contiguous, 16 bytes per lane),
 // and each 4-lane quad of the row one block; the quad's absmax comes from two quad
 // permutes, and lane 0 of the row writes the pack's word.
+// NT: streaming loads of the rows, chosen on large grids (T = 512 measured 13.6 -> 12.9 us,
+// T = 256 8.0 -> 7.6 us)
+template <bool NT>
 __global__ __launch_bounds__(256) void k_group_quant_mx(const uint16_t* __restrict__ x, int64_t T, int G, int D,
                                                         uint8_t* __restrict__ xq, int32_t* __restrict__ xs) {
   const int lane = threadIdx.x & 63;
@@ -133,7 +136,13 @@ __global__ __launch_bounds__(256) void k_group_quant_mx(const uint16_t* __restri
   int byte = 0;
   if (t < T && p < PH && h < HG) {
     const int64_t off = (t * G + g) * (int64_t)D + (int64_t)h * 32 + (lane & 3) * 8;
-    const uint4 u = *reinterpret_cast<const uint4*>(x + off);
+    uint4 u;
+    if constexpr (NT) {
+      const v4i l = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(x + off));
+      u = uint4{(uint32_t)l[0], (uint32_t)l[1], (uint32_t)l[2], (uint32_t)l[3]};
+    } else {
+      u = *reinterpret_cast<const uint4*>(x + off);
+    }
     float v[8];
     const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -173,7 +182,10 @@ hipError_t launch_group_quant_mx(const uint16_t* x, int64_t T, int G, int D, uin
   const int64_t waves = TA * G * PW;
   if (waves == 0) return hipSuccess;
   dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-  hipLaunchKernelGGL(k_group_quant_mx, grid, block, 0, st, x, T, G, D, xq, xs);
+  if (waves >= 16384)
+    hipLaunchKernelGGL(k_group_quant_mx<true>, grid, block, 0, st, x, T, G, D, xq, xs);
+  else
+    hipLaunchKernelGGL(k_group_quant_mx<false>, grid, block, 0, st, x, T, G, D, xq, xs);
   return hipGetLastError();
 }
 
