@@ -62,7 +62,16 @@ __global__ __launch_bounds__(1024) void k_moe_sort(const int32_t* __restrict__ i
     for (int i = b0 + lane; i < b1; i += 64) cnt[i] += off;
   }
   __syncthreads();
-  for (int e = t; e <= E; e += 1024) offsets[e] = (e < E) ? (int64_t)cnt[e * kSortWaves] : (int64_t)n;
+  // ids outside [0, E) are dropped: offsets[E] counts the kept rows, and the slots past them
+  // get perm = -1 and row_token = 0 (a valid token), so a gather over all T * topk rows reads
+  // only valid memory
+  int kept = 0;
+  for (int j = 0; j < kSortWaves; ++j) kept += blk_total[j];
+  for (int e = t; e <= E; e += 1024) offsets[e] = (e < E) ? (int64_t)cnt[e * kSortWaves] : (int64_t)kept;
+  for (int i = kept + t; i < n; i += 1024) {
+    perm[i] = -1;
+    row_token[i] = 0;
+  }
   __syncthreads();
   // stable scatter
   int nbits = 0;

@@ -103,7 +103,8 @@ void wq_ctx_destroy(wq_ctx* ctx);
 /* Force the K-split factor of later quant calls on this context (the same knob as
  * WQ_FORCE_SPLIT); n = 0 restores the automatic choice.  Results are bit-identical for
  * every split; tests use this to show it.  Returns WQ_ERR_SHAPE for n < 0; a split larger
- * than K / 512 makes later quant calls return WQ_ERR_SHAPE. */
+ * than K / 8 (bf16 input) or K / 4 (f32 input), one 16-byte piece of the row per slice,
+ * makes later quant calls return WQ_ERR_SHAPE. */
 int wq_ctx_set_split(wq_ctx* ctx, int n);
 
 /* Force the shape of the one-launch fused kernel of wq_fused_quant_matmul on this context
@@ -176,7 +177,10 @@ int wq_group_quant_mxfp8(wq_ctx* ctx, const void* x, int64_t T, int64_t G, int64
  *   payload WQ_PAYLOAD_FP8_E4M3, batch = G groups, a = E4M3 codes with row stride lda
  *   bytes and group stride a_batch_stride bytes; a_scale = the int32 packed storage
  *   [G, PH, TA] written by wq_group_quant_fp8_ue8m0 with TA = a_scale_tokens; b = E4M3
- *   [G][N][K]; b_scale = f32 powers of two [G][N/128][K/128];
+ *   [G][N][K]; b_scale = f32 powers of two [G][N/128][K/128] (the kernels pass each scale's
+ *   exponent field to the matrix unit as its E8M0 scale, so a value that is not a normal
+ *   power of two acts as 2^(its biased exponent - 127): its mantissa is ignored, and zero
+ *   or a subnormal acts as 2^-127); K <= 131072 (else WQ_ERR_SHAPE);
  *   y[m, g, n] = bf16_RN( sum_kb 2^(e_a(m,g,kb)) * b_scale[g, n/128, kb]
  *                         * sum_{k in block kb} a[m, g, k] * b[g, n, k] )   (f32 accumulate)
  * MX-like 32-element blocks ("DeepSeek V4 950 低精度优化全复盘", section 2.1): payload
@@ -265,7 +269,9 @@ int wq_fused_quant_matmul_packed(wq_ctx* ctx, const void* x, int64_t M, int64_t 
  * [0, E).  Outputs: perm int32 [T*topk] (flattened pair index t*topk + slot of each sorted
  * row; stable: ties keep pair order), row_token int32 [T*topk] (= perm / topk),
  * offsets int64 [E + 1] (exclusive prefix sum of rows per expert; the group_list of
- * section 五 of the W8A8 article).  Out-of-range ids give undefined output, not a fault. */
+ * section 五 of the W8A8 article).  An id outside [0, E) drops its pair: the kept pairs are
+ * sorted as above, offsets[E] is their count, and the slots from offsets[E] to T*topk get
+ * perm = -1 and row_token = 0, so a gather over all T*topk rows stays in bounds. */
 int wq_moe_sort(wq_ctx* ctx, const int32_t* topk_ids, int64_t T, int64_t topk, int64_t E,
                 int32_t* perm, int32_t* row_token, int64_t* offsets, void* stream);
 

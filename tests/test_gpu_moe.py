@@ -33,6 +33,23 @@ def test_expert_sort(T, E, topk, seed):
     assert np.array_equal(host(offsets), off_ref)
 
 
+def test_expert_sort_drops_out_of_range_ids():
+    """Ids outside [0, E) drop their pairs: the kept pairs sort as the oracle sorts them,
+    offsets[E] counts them, and the slots past them hold perm = -1, row_token = 0."""
+    T, E, topk = 40, 16, 4
+    ids = syn.zipf_topk_ids((9, 7), T, E, topk)
+    ids[3, 1], ids[17, 0], ids[39, 3] = -1, E, 1 << 20
+    perm, row_token, offsets = wq.wq_moe_sort(dev(ids), E)
+    torch.cuda.synchronize()
+    p_ref, off_ref = moe.expert_sort(ids, E, drop_invalid=True)
+    kept = p_ref.size
+    assert kept == T * topk - 3 and off_ref[E] == kept
+    assert np.array_equal(host(offsets), off_ref)
+    assert np.array_equal(host(perm)[:kept], p_ref)
+    assert np.array_equal(host(row_token)[:kept], p_ref // topk)
+    assert (host(perm)[kept:] == -1).all() and (host(row_token)[kept:] == 0).all()
+
+
 @pytest.mark.parametrize("T,H", [(16, 512), (8, 4096), (5, 2064)])
 def test_rmsnorm_quant_gather(T, H):
     h = syn.activations((60, T, H), T, H)
@@ -42,10 +59,22 @@ def test_rmsnorm_quant_gather(T, H):
     tok = p_ref // 4
     q, s = wq.wq_dynamic_quant(bf16_dev(h), rms_gamma=bf16_dev(gamma), row_index=dev(tok.astype(np.int32)))
     torch.cuda.synchronize()
-    v = moe.rmsnorm_f32(h, gamma)
-    q_ref, s_ref = il.quant_int8_per_token(v[tok], is_bf16_bits=False)
+    v, v_alt, flagged = moe.rmsnorm_f32(h, gamma, alternates=True)
+    q_ref, s_ref = _rms_quant_ref(v, v_alt, flagged, tok, host(q), host(s))
     assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
     assert np.array_equal(host(q), q_ref)
+
+
+def _rms_quant_ref(v, v_alt, flagged, tok, q_got, s_got):
+    """The oracle's (q, s) for the RMSNorm rows of tokens `tok`: the primary reading, or for
+    a flagged token (oracle.moe.rmsnorm_mean_squares) whichever of the two readings the kernel's
+    row matches.  Rows that match neither keep the primary, so assert_same reports them."""
+    q_ref, s_ref = il.quant_int8_per_token(v[tok], is_bf16_bits=False)
+    if flagged[tok].any():
+        q_alt, s_alt = il.quant_int8_per_token(v_alt[tok], is_bf16_bits=False)
+        take = flagged[tok] & (s_got.view(np.uint32) == s_alt.view(np.uint32)) & (q_got == q_alt).all(1)
+        q_ref[take], s_ref[take] = q_alt[take], s_alt[take]
+    return q_ref, s_ref
 
 
 def _run_block_gpu(d, E, frag=False):
@@ -70,7 +99,17 @@ def test_moe_block_against_oracle(T, H, I, E, topk, frag):
     d = syn.moe_inputs(seed=T, T=T, H=H, I=I, E=E, TOPK=topk)
     d.update(w13_d=dev(d["w13"]), sw13_d=dev(d["sw13"]), w2_d=dev(d["w2"]), sw2_d=dev(d["sw2"]))
     g = _run_block_gpu(d, E, frag)
-    r = moe.moe_block(d["h"], d["gamma"], d["ids"], d["w13"], d["sw13"], d["w2"], d["sw2"], keep=True)
+    # a token whose RMSNorm row is flagged takes the reading the kernel's rows match
+    v, v_alt, flagged = moe.rmsnorm_f32(d["h"], d["gamma"], alternates=True)
+    perm_ref, _ = moe.expert_sort(d["ids"], E)
+    tok = perm_ref // topk
+    _, s1_ref = _rms_quant_ref(v, v_alt, flagged, tok, host(g["q1"]), host(g["s1"]))
+    _, s1_alt = il.quant_int8_per_token(v_alt[tok], is_bf16_bits=False)
+    for t in np.flatnonzero(flagged):
+        rows = np.flatnonzero(tok == t)
+        if rows.size and (s1_ref[rows].view(np.uint32) == s1_alt[rows].view(np.uint32)).all():
+            v[t] = v_alt[t]
+    r = moe.moe_block(d["h"], d["gamma"], d["ids"], d["w13"], d["sw13"], d["w2"], d["sw2"], keep=True, v_rows=v)
     assert_same("perm", host(g["perm"]), r["perm"])
     assert_same("offsets", host(g["offsets"]), r["offsets"])
     assert_same("s1", host(g["s1"]), r["s1"])
@@ -104,13 +143,13 @@ def test_moe_block_full_size_sampled_experts():
     busiest = int(order[-1])
     one_row = int(np.flatnonzero(counts == 1)[0]) if (counts == 1).any() else int(order[0])
     median = int(order[np.searchsorted(counts[order], np.median(counts[counts > 0]))])
-    v = moe.rmsnorm_f32(d["h"], d["gamma"])
+    v, v_alt, flagged = moe.rmsnorm_f32(d["h"], d["gamma"], alternates=True)
     for e in {busiest, one_row, median}:
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if lo == hi:
             continue
         tok = perm_ref[lo:hi] // topk
-        q1, s1 = il.quant_int8_per_token(v[tok], is_bf16_bits=False)
+        q1, s1 = _rms_quant_ref(v, v_alt, flagged, tok, host(g["q1"][lo:hi]), host(g["s1"][lo:hi]))
         assert_same(f"q1[e={e}]", host(g["q1"][lo:hi]), q1)
         acc13 = il.gemm_int8_int32(q1, host(w13[e]))
         hmid = moe.silu_mul_f32(acc13, s1, np.broadcast_to(host(sw13[e]), (hi - lo, 2 * I)))

@@ -3,6 +3,7 @@
 import math
 
 import numpy as np
+import pytest
 
 import synthetic as syn
 from exact import bf16_bits_of
@@ -84,3 +85,43 @@ def test_block_segments_equal_dense_per_row():
     q1_tok, s1_tok = il.quant_int8_per_token(r["v"], is_bf16_bits=False)
     assert np.array_equal(r["q1"], q1_tok[tok]) and np.array_equal(r["s1"], s1_tok[tok])
     assert r["y"].shape == (32, 256)
+
+
+def test_rmsnorm_boundary_flag():
+    """A18: [1, 1, 2^-12, 2^-12] has sum of squares 2 + 2^-23, so the mean square is exactly
+    halfway between 0.5 and 0.5 + 2^-24: ties to even give 0.5, and a float64 sum in another
+    order could land on either side, so the row is flagged with the other neighbour.  A row
+    of N(0,1) values far from such a boundary is not flagged."""
+    x = np.array([[0x3F80, 0x3F80, 0x3980, 0x3980]], np.uint16)
+    ms, other, flagged = moe.rmsnorm_mean_squares(x)
+    assert ms[0] == np.float32(0.5) and other[0] == np.float32(0.5 + 2.0 ** -24) and flagged[0]
+    v, v_alt, fl = moe.rmsnorm_f32(x, np.full(4, bf16_bits_of(1.0), np.uint16), alternates=True)
+    assert fl[0] and not np.array_equal(v, v_alt)
+    h = syn.activations((78, 2), 32, 4096)
+    ms, other, flagged = moe.rmsnorm_mean_squares(h)
+    assert not flagged.any() and np.array_equal(ms, other)
+
+
+def test_rmsnorm_other_summation_orders_stay_within_the_flag():
+    """Recursive float64 sums in forward, reverse and sorted order all give the oracle's mean
+    square, or the flagged neighbour."""
+    h = syn.activations((78, 3), 64, 2048)
+    ms, other, _ = moe.rmsnorm_mean_squares(h)
+    xf = nm.bf16_to_f32(h).astype(np.float64)
+    for order in (lambda r: r, lambda r: r[::-1], np.sort, lambda r: np.sort(r)[::-1]):
+        for m in range(h.shape[0]):
+            acc = 0.0
+            for v in order(xf[m] * xf[m]):
+                acc += float(v)
+            got = np.float32(acc / h.shape[1])
+            assert got == ms[m] or got == other[m]
+
+
+def test_expert_sort_drop_invalid():
+    """Out-of-range ids: an error by default; with drop_invalid their pairs take no row and
+    the kept pairs keep their stable order."""
+    ids = np.array([[2, -1], [0, 2], [5, 1]], np.int32)
+    with pytest.raises(ValueError):
+        moe.expert_sort(ids, 4)
+    perm, off = moe.expert_sort(ids, 4, drop_invalid=True)
+    assert perm.tolist() == [2, 5, 0, 3] and off.tolist() == [0, 1, 2, 4, 4]
