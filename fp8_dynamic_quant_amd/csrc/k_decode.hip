@@ -384,13 +384,8 @@ template <int MT, int NT>
 static hipError_t decode_launch(const DecodeArgs& a, hipStream_t st) {
   const size_t lds = decode_lds_bytes(MT);
   auto kfn = k_decode<MT, NT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kfn), 160 * 1024);
+  if (e != hipSuccess) return e;
   dim3 grid((unsigned)((a.N + NT - 1) / NT), (unsigned)((a.M + 16 * MT - 1) / (16 * MT))), block(256);
   hipLaunchKernelGGL(kfn, grid, block, lds, st, a);
   return hipGetLastError();

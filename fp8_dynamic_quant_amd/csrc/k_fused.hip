@@ -289,13 +289,8 @@ size_t fused_lds_bytes(int R, int CT, int K) {
 
 template <int R, int CT, bool PREQ, bool PK>
 hipError_t launch_fused_rt(const DecodeArgs& a, int nt, hipStream_t st) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_fused_decode<R, CT, PREQ, PK>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  hipError_t e = set_lds_limit(reinterpret_cast<const void*>(k_fused_decode<R, CT, PREQ, PK>), 160 * 1024);
+  if (e != hipSuccess) return e;
   const int slices = (a.N + nt - 1) / nt, rtiles = (a.M + R - 1) / R;
   hipLaunchKernelGGL((k_fused_decode<R, CT, PREQ, PK>), dim3((unsigned)(slices * rtiles)), dim3(kFW * 64),
                      fused_lds_bytes(R, CT, a.K), st, a, nt, slices, rtiles);

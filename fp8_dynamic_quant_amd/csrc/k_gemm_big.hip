@@ -283,13 +283,8 @@ hipError_t launch_gemm_i8_big(const TileArgs& a, int num_cu, hipStream_t st) {
   bt.per_xcd = (bt.nt + 7) / 8;
   const int wgs_per_xcd = num_cu / 8;
   const size_t lds = kStages * (size_t)kStageB;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_i8_big),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  hipError_t e = set_lds_limit(reinterpret_cast<const void*>(k_gemm_i8_big), (int)lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_gemm_i8_big, dim3((unsigned)(wgs_per_xcd * 8)), dim3(512), lds, st, a, bt, wgs_per_xcd);
   return hipGetLastError();
 }

@@ -2,12 +2,11 @@
 //
 // Operation: "DeepSeek-V4 W8A8 性能分析", section 一 (npu_quant_matmul: INT8 X and
 // per-token scale times pre-quantised weights, BF16 Y) and section 三 (the tiling is
-// derived from the real M, N, K; for small M and N the K dimension is split across
-// cores, the SmallMN / StreamK idea).
+// derived from the real M, N, K).
 //
-// k_gemm_i8_tile - large M.  128x128 workgroup tiles, LDS double buffering, and
-// v_mfma_i32_16x16x64_i8; optionally over expert segments (MoE group_list).  Decode-sized
-// M runs in k_decode.hip instead.
+// k_gemm_i8_tile - the fallback for K not a multiple of 128 above the decode sizes: 128x128
+// workgroup tiles, LDS double buffering, v_mfma_i32_16x16x64_i8.  Decode-sized M runs in
+// k_decode.hip / k_fused.hip, K % 128 == 0 in k_gemm_tile.hip / k_gemm_big.hip.
 #include "wq_device.h"
 #include "wq_kernels.h"
 

@@ -404,13 +404,8 @@ hipError_t launch_gemm_tile(const TileArgs& a, bool fp8, hipStream_t st) {
     const size_t lds = dual ? (size_t)TileRing<false, true, seg_stages<2>()>::kBytes
                             : (size_t)TileRing<false, false, seg_stages<1>()>::kBytes;
     auto kfn = dual ? k_gemm_seg<2> : k_gemm_seg<1>;
-    static bool attr[2] = {false, false};
-    if (!attr[dual]) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      attr[dual] = true;
-    }
+    hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kfn), (int)lds);
+    if (e != hipSuccess) return e;
     int dev = 0, cus = 256;
     (void)hipGetDevice(&dev);
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -424,13 +419,8 @@ hipError_t launch_gemm_tile(const TileArgs& a, bool fp8, hipStream_t st) {
   const size_t lds = fp8 ? (size_t)TileRing<true, false, kDenseStages>::kBytes
                           : (size_t)TileRing<false, false, kDenseStages>::kBytes;
   auto kfn = fp8 ? k_gemm_tile<true> : k_gemm_tile<false>;
-  static bool attr[2] = {false, false};
-  if (!attr[fp8]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    attr[fp8] = true;
-  }
+  hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kfn), (int)lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kfn, grid, block, lds, st, a, tiles_m, tiles_n);
   return hipGetLastError();
 }

@@ -1,21 +1,26 @@
 // Host side of libwq: argument validation, launch-shape selection and the C ABI.
 //
-// Launch-shape rules (the MI355X analogue of the host tiling the W8A8 article reads in
-// sections 二 and 三: launch width derived continuously from the real shape, not from a
-// bucket table):
+// Launch-shape rules (the MI355X counterpart of the host tiling the W8A8 article reads in
+// sections 二 and 三: the launch follows the real shape, not a bucket table):
 //  * quant: one wave per (row, K slice).  Rows alone give M waves; when that leaves most
 //    of the CUs idle (M < CUs / 2, the condition under which the article's arch35 tiling
 //    also splits a row along its tail axis) the row is split into S slices with
 //    M * S <= CUs, each slice at least 512 elements.
-//  * INT8 GEMM, M <= 64: split-K.  A workgroup owns 64 columns and a K slice of
-//    64 * ksteps; the slice shrinks (down to 256) until the grid covers every CU with a
-//    distinct piece of W.
-//  * INT8 GEMM, M > 64: 128x128 tiles.
+//  * INT8 GEMM, M < 256 with K % 512 == 0 and K <= 4096: the 8-wave decode kernel
+//    (k_fused.hip), workgroups of R rows x nt columns, each streaming its columns' whole K,
+//    the shape from a cost model (fused_shape); no workgroup talks to another.  Other K at
+//    M <= 64: the dot4 GEMV (M <= 4) or the 4-wave decode kernel (k_decode.hip).
+//  * INT8 GEMM, M and N >= 256: persistent 256 x 256 tiles (k_gemm_big.hip); other shapes
+//    128 x 128 tiles.
+//  * FP8: the 16- or 32-column weight-streaming kernels at T <= 64, 128 x 128 tiles above.
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <set>
 #include <string>
+#include <utility>
 
 #include "../../include/wq.h"
 #include "wq_kernels.h"
@@ -29,11 +34,9 @@ struct wq_ctx {
   int force_split;
   int decode_nt;  // 0 = automatic; else 4, 8 or 16 (WQ_DECODE_NT)
   int decode_mt;  // 0 = automatic; else 1, 2 or 4 16-row tiles per workgroup (WQ_DECODE_MT)
-  // The fused call quantises inside the GEMM launch up to these M (measured on MI355X at
-  // K = 4096, N = 1024): the dot4 GEMV up to 2 rows, the 8-wave MFMA kernel up to 16.
-  // Every workgroup then quantises all M rows itself (no workgroup may wait for another),
-  // ~0.3 us per row, while a second launch costs a fixed ~6 us; above the limit the call
-  // runs the quant kernel and then the GEMM.
+  // The fused call quantises inside the GEMM launch up to fused_max_m rows (default 64):
+  // every workgroup quantises the rows of its own row tile (no workgroup waits for another);
+  // above the limit the call runs the quant kernel and then the GEMM.
   int seg_small;         // expert segments: small experts on the streaming kernel (WQ_SEG_SMALL=0 turns off)
   int fp8_rt;            // FP8 decode: 16-token tiles per workgroup (WQ_FP8_RT, 1..4; 0 = automatic)
   int fp8_cols;          // FP8 decode: output columns per workgroup (WQ_FP8_COLS, 16 or 32; default 32)
@@ -144,6 +147,21 @@ void fused_shape(const wq_ctx* c, int64_t M, int64_t N, int* nt, int* r, int row
 }
 
 }  // namespace
+
+namespace wq {
+hipError_t set_lds_limit(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;  // (kernel, device) pairs already raised
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({kernel, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({kernel, dev});
+  return e;
+}
+}  // namespace wq
 
 extern "C" {
 
@@ -349,6 +367,8 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
     return status_of(e);
   }
   if (d->epilogue != WQ_EPI_BF16) return WQ_ERR_UNSUPPORTED;
+  // fragment-order weights reach only the decode kernel below (the checks above admit them at
+  // M < 256 with given_decode_fits), whatever the decode knobs say: the other kernels read [N, K]
   const bool frag = d->b_layout == WQ_LAYOUT_FRAGMENT;
   wq::DecodeArgs a{};
   a.a = static_cast<const int8_t*>(d->a);
@@ -360,7 +380,7 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   a.y = static_cast<uint16_t*>(d->y);
   a.ldy = d->ldy;
   a.acc_out = d->acc_out;
-  if (M > 64 && M < 256 && wq::given_decode_fits((int)M, (int)K) && c->decode_nt == 0 && c->decode_mt == 0) {
+  if (M > 64 && M < 256 && wq::given_decode_fits((int)M, (int)K) && ((c->decode_nt == 0 && c->decode_mt == 0) || frag)) {
     // between the decode sizes and the 256-row prefill tiles: the decode kernel on the given
     // codes with row tiles of up to 16 rows (at M = 128, N = 1024 the 128 x 128 tiles gave
     // only 8 workgroups: 41.6 us with the quant)
@@ -406,6 +426,7 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
                    (long long)((M + 16 * mt - 1) / (16 * mt)), c->num_cu);
     return status_of(e);
   }
+  if (frag) return WQ_ERR_UNSUPPORTED;  // not reached: the branches above take every fragment-order call
   wq::TileArgs t{};
   t.a = static_cast<const int8_t*>(d->a);
   t.lda = d->lda;
@@ -439,7 +460,8 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
 
 static int fp8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   const int64_t M = d->M, N = d->N, K = d->K, G = d->batch;
-  if (N % 128 != 0 || K % 128 != 0 || d->seg_offsets != nullptr || d->epilogue != WQ_EPI_BF16) return WQ_ERR_SHAPE;
+  if (N % 128 != 0 || K % 128 != 0 || K > 131072 || d->seg_offsets != nullptr || d->epilogue != WQ_EPI_BF16)
+    return WQ_ERR_SHAPE;
   if (d->lda < K || d->ldy < N || d->a_batch_stride < 0 || d->y_batch_stride < 0) return WQ_ERR_SHAPE;
   const int64_t TA = (M + 3) / 4 * 4;
   if (d->a_scale_tokens < TA) return WQ_ERR_SHAPE;

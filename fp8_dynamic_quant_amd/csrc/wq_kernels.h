@@ -6,6 +6,10 @@
 
 namespace wq {
 
+// Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once per (kernel,
+// device); safe to call from several host threads (wq_api.hip).
+hipError_t set_lds_limit(const void* kernel, int bytes);
+
 // Per-token INT8 quant (k_quant.hip).  S = K-split factor.  *ch_used reports the
 // register-cache depth chosen (0 = streamed rows).
 hipError_t launch_dynamic_quant(const void* x, bool x_f32, int64_t M, int K, int64_t ldx,

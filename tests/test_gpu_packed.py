@@ -7,6 +7,9 @@ packed call must give the same bytes as the plain fused call, which the oracle p
 payloads, scales and accumulators bit-exact, BF16 within 1 ulp of the oracle.
 """
 
+import contextlib
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -151,6 +154,55 @@ def test_quant_matmul_mid_m(M, K, N):
     assert_same("acc (fragment order)", host(acc_f), ref["acc"])
     assert_same("y", host_bf16_bits(y_frag), host_bf16_bits(y_plain))
     assert nm.bf16_ulp_distance(host_bf16_bits(y_plain), ref["y"]).max() <= 1
+
+
+@contextlib.contextmanager
+def _context_with_env(**env):
+    """A fresh library context created with the given knobs in the environment (the context
+    reads it once, at creation), used by the binding's calls on DEV for the with-block."""
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update({k: str(v) for k, v in env.items()})
+    try:
+        ctx = wq.Context(DEV)
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    idx = DEV.index
+    saved = wq._CTX.get(idx)
+    wq._CTX[idx] = ctx
+    try:
+        yield ctx
+    finally:
+        if saved is None:
+            wq._CTX.pop(idx, None)
+        else:
+            wq._CTX[idx] = saved
+
+
+@pytest.mark.parametrize("M", [65, 128, 255])
+@pytest.mark.parametrize("nt,mt", [(8, 0), (0, 2), (16, 4)])
+def test_quant_matmul_mid_m_fragment_order_with_decode_knobs(M, nt, mt):
+    """Fragment-order weights at 64 < M < 256 with the decode knobs set: the call must still
+    read them in fragment order (the knobs only steer the plain-layout kernels), giving the
+    oracle's accumulators and the plain call's bytes."""
+    K, N = 4096, 1024
+    x = syn.activations((18, M, K), M, K, outlier_frac=0.01, outlier_mul=25.0)
+    w, sw = syn.int8_weights((18, N, K), N, K)
+    ref = il.linear_w8a8(x, w, sw)
+    with _context_with_env(WQ_DECODE_NT=nt, WQ_DECODE_MT=mt):
+        xq, xs = wq.wq_dynamic_quant(bf16_dev(x))
+        wd, swd = dev(w), dev(sw)
+        acc_p, acc_f = poison((M, N), torch.int32), poison((M, N), torch.int32)
+        y_plain = wq.wq_quant_matmul(xq, xs, wd, swd, acc_out=acc_p)
+        y_frag = wq.wq_quant_matmul(xq, xs, wq.wq_pack_weight_i8(wd), swd, acc_out=acc_f, b_fragment=True, n=N)
+        torch.cuda.synchronize()
+    assert_same("acc (fragment order)", host(acc_f), ref["acc"])
+    assert_same("acc", host(acc_p), ref["acc"])
+    assert_same("y", host_bf16_bits(y_frag), host_bf16_bits(y_plain))
+    assert nm.bf16_ulp_distance(host_bf16_bits(y_frag), ref["y"]).max() <= 1
 
 
 def test_quant_matmul_packed_unsupported_sizes():
