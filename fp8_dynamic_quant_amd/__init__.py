@@ -78,6 +78,9 @@ EXPORTS = {
     "wq_fused_quant_matmul_packed": (ctypes.c_int, [_c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p,
                                                     _i64, _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p,
                                                     _c_void_p]),
+    "wq_fused_quant_matmul_static": (ctypes.c_int, [ctypes.c_int, _c_void_p, _i64, _i64, _i64, _c_void_p, _c_void_p,
+                                                    _i64, _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                                    _c_void_p]),
 }
 
 _LIB = None
@@ -281,6 +284,23 @@ def wq_fused_quant_matmul(x, w, w_scale, *, y=None, x_q_out=None, x_scale_out=No
                                      y.stride(0), _ptr(x_q_out), _ptr(x_scale_out), _ptr(acc_out),
                                      _stream(x.device))
     _check("wq_fused_quant_matmul", st)
+    return y
+
+
+def wq_fused_quant_matmul_static(x, w, w_scale, *, y=None, x_q_out=None, x_scale_out=None, acc_out=None):
+    """wq_fused_quant_matmul through the allocation-free entry point (no context, the library's
+    static staging buffer); y is allocated here unless given."""
+    if x.dim() != 2 or x.stride(1) != 1 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16 [M, K] with unit stride along K")
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    idx = x.device.index if x.device.index is not None else torch.cuda.current_device()
+    st = lib().wq_fused_quant_matmul_static(idx, _ptr(x), M, K, x.stride(0), _ptr(w), _ptr(w_scale), N, _ptr(y),
+                                            y.stride(0), _ptr(x_q_out), _ptr(x_scale_out), _ptr(acc_out),
+                                            _stream(x.device))
+    _check("wq_fused_quant_matmul_static", st)
     return y
 
 

@@ -18,9 +18,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
-#include <set>
 #include <string>
-#include <utility>
 
 #include "../../include/wq.h"
 #include "wq_kernels.h"
@@ -146,19 +144,65 @@ void fused_shape(const wq_ctx* c, int64_t M, int64_t N, int* nt, int* r, int row
   }
 }
 
+// The knobs a context reads from the environment once, at creation (include/wq.h).
+void read_env_knobs(wq_ctx* c) {
+  const char* lg = std::getenv("WQ_LOG");
+  c->log = lg && lg[0] == '1';
+  const char* fs = std::getenv("WQ_FORCE_SPLIT");
+  c->force_split = fs ? std::atoi(fs) : 0;
+  const char* dn = std::getenv("WQ_DECODE_NT");
+  c->decode_nt = dn ? std::atoi(dn) : 0;
+  if (c->decode_nt != 0 && c->decode_nt != 4 && c->decode_nt != 8 && c->decode_nt != 16) c->decode_nt = 0;
+  const char* dm = std::getenv("WQ_DECODE_MT");
+  c->decode_mt = dm ? std::atoi(dm) : 0;
+  if (c->decode_mt != 0 && c->decode_mt != 1 && c->decode_mt != 2 && c->decode_mt != 4) c->decode_mt = 0;
+  const char* fm = std::getenv("WQ_FUSED_MAX_M");
+  c->fused_max_m = fm ? std::atoi(fm) : 64;
+  if (c->fused_max_m < 0 || c->fused_max_m > 64) c->fused_max_m = 64;
+  const char* fr = std::getenv("WQ_FP8_RT");
+  c->fp8_rt = fr ? std::atoi(fr) : 0;
+  const char* fc = std::getenv("WQ_FP8_COLS");
+  c->fp8_cols = fc ? std::atoi(fc) : 32;
+  if (c->fp8_cols != 16) c->fp8_cols = 32;
+  if (c->fp8_rt < 0 || c->fp8_rt > 4) c->fp8_rt = 0;
+  const char* ss = std::getenv("WQ_SEG_SMALL");
+  c->seg_small = ss ? std::atoi(ss) != 0 : 1;
+  const char* gm = std::getenv("WQ_FUSED_GEMV_MAX_M");
+  c->fused_gemv_max_m = gm ? std::atoi(gm) : 0;
+  if (c->fused_gemv_max_m < 0 || c->fused_gemv_max_m > 4) c->fused_gemv_max_m = 0;
+  const char* fr2 = std::getenv("WQ_FUSED_R");
+  c->fused_r = fr2 ? std::atoi(fr2) : 0;
+  if (c->fused_r != 0 && c->fused_r != 1 && c->fused_r != 2 && c->fused_r != 4 && c->fused_r != 8 && c->fused_r != 16)
+    c->fused_r = 0;
+  const char* fn = std::getenv("WQ_FUSED_NT");
+  c->fused_nt = fn ? std::atoi(fn) : 0;
+  if (c->fused_nt != 0 && c->fused_nt != 4 && c->fused_nt != 8 && c->fused_nt != 16 && c->fused_nt != 32)
+    c->fused_nt = 0;
+}
+
 }  // namespace
 
 namespace wq {
+// (kernel, device) pairs whose limit is raised, in a fixed table (no heap allocation, so the
+// allocation-free entry point may use it); once the table is full the attribute is set on
+// every launch, which is correct, only slower
 hipError_t set_lds_limit(const void* kernel, int bytes) {
+  struct Done {
+    const void* kernel;
+    int device;
+  };
+  constexpr int kMaxDone = 2048;
   static std::mutex mu;
-  static std::set<std::pair<const void*, int>> done;  // (kernel, device) pairs already raised
+  static Done done[kMaxDone];
+  static int n_done = 0;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(mu);
-  if (done.count({kernel, dev})) return hipSuccess;
+  for (int i = 0; i < n_done; ++i)
+    if (done[i].kernel == kernel && done[i].device == dev) return hipSuccess;
   e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess) done.insert({kernel, dev});
+  if (e == hipSuccess && n_done < kMaxDone) done[n_done++] = Done{kernel, dev};
   return e;
 }
 }  // namespace wq
@@ -196,38 +240,7 @@ int wq_ctx_create(int device, void* workspace, size_t workspace_bytes, wq_ctx** 
   c->num_cu = prop.multiProcessorCount;
   c->ws = workspace;
   c->ws_bytes = workspace_bytes;
-  const char* lg = std::getenv("WQ_LOG");
-  c->log = lg && lg[0] == '1';
-  const char* fs = std::getenv("WQ_FORCE_SPLIT");
-  c->force_split = fs ? std::atoi(fs) : 0;
-  const char* dn = std::getenv("WQ_DECODE_NT");
-  c->decode_nt = dn ? std::atoi(dn) : 0;
-  if (c->decode_nt != 0 && c->decode_nt != 4 && c->decode_nt != 8 && c->decode_nt != 16) c->decode_nt = 0;
-  const char* dm = std::getenv("WQ_DECODE_MT");
-  c->decode_mt = dm ? std::atoi(dm) : 0;
-  if (c->decode_mt != 0 && c->decode_mt != 1 && c->decode_mt != 2 && c->decode_mt != 4) c->decode_mt = 0;
-  const char* fm = std::getenv("WQ_FUSED_MAX_M");
-  c->fused_max_m = fm ? std::atoi(fm) : 64;
-  if (c->fused_max_m < 0 || c->fused_max_m > 64) c->fused_max_m = 64;
-  const char* fr = std::getenv("WQ_FP8_RT");
-  c->fp8_rt = fr ? std::atoi(fr) : 0;
-  const char* fc = std::getenv("WQ_FP8_COLS");
-  c->fp8_cols = fc ? std::atoi(fc) : 32;
-  if (c->fp8_cols != 16) c->fp8_cols = 32;
-  if (c->fp8_rt < 0 || c->fp8_rt > 4) c->fp8_rt = 0;
-  const char* ss = std::getenv("WQ_SEG_SMALL");
-  c->seg_small = ss ? std::atoi(ss) != 0 : 1;
-  const char* gm = std::getenv("WQ_FUSED_GEMV_MAX_M");
-  c->fused_gemv_max_m = gm ? std::atoi(gm) : 0;
-  if (c->fused_gemv_max_m < 0 || c->fused_gemv_max_m > 4) c->fused_gemv_max_m = 0;
-  const char* fr2 = std::getenv("WQ_FUSED_R");
-  c->fused_r = fr2 ? std::atoi(fr2) : 0;
-  if (c->fused_r != 0 && c->fused_r != 1 && c->fused_r != 2 && c->fused_r != 4 && c->fused_r != 8 && c->fused_r != 16)
-    c->fused_r = 0;
-  const char* fn = std::getenv("WQ_FUSED_NT");
-  c->fused_nt = fn ? std::atoi(fn) : 0;
-  if (c->fused_nt != 0 && c->fused_nt != 4 && c->fused_nt != 8 && c->fused_nt != 16 && c->fused_nt != 32)
-    c->fused_nt = 0;
+  read_env_knobs(c);
   *out = c;
   return WQ_OK;
 }
@@ -563,10 +576,15 @@ int wq_fused_path(const wq_ctx* c, int64_t M, int64_t K, int64_t N) {
   return fused_path(c, M, K);
 }
 
-int wq_fused_quant_matmul(wq_ctx* c, const void* x, int64_t M, int64_t K, int64_t ldx, const int8_t* w,
-                          const float* w_scale, int64_t N, void* y, int64_t ldy, int8_t* x_q_out,
-                          float* x_scale_out, int32_t* acc_out, void* stream) {
-  if (!c) return WQ_ERR_NULL;
+}  // extern "C"
+
+namespace {
+// The fused call; when M is above the one-launch limit and the caller exported no payload,
+// the payload and its scales are staged in stage_q / stage_s (the context workspace, or the
+// static scratch of wq_fused_quant_matmul_static), of the given capacities.
+int fused_impl(wq_ctx* c, const void* x, int64_t M, int64_t K, int64_t ldx, const int8_t* w, const float* w_scale,
+               int64_t N, void* y, int64_t ldy, int8_t* x_q_out, float* x_scale_out, int32_t* acc_out, void* stream,
+               int8_t* stage_q, size_t stage_q_bytes, float* stage_s, size_t stage_s_bytes) {
   if (M < 0 || K <= 0 || N <= 0 || K % 16 != 0 || N % 16 != 0 || K > 131072 || ldx < K || ldy < N)
     return WQ_ERR_SHAPE;
   if (M == 0) return WQ_OK;
@@ -581,11 +599,11 @@ int wq_fused_quant_matmul(wq_ctx* c, const void* x, int64_t M, int64_t K, int64_
   const bool one_launch_mfma = path == 2;
   if (!one_launch_gemv && !one_launch_mfma) {
     // quantise, then the GEMM (two launches); the INT8 payload goes through the
-    // caller's buffers when given, else through the context workspace
-    if (!x_q_out && (size_t)M * K > kWsQBytes) return WQ_ERR_WORKSPACE;
-    if (!x_scale_out && (size_t)M * 4 > kWsScaleBytes) return WQ_ERR_WORKSPACE;
-    if (!x_q_out) x_q_out = ws_q(c);
-    if (!x_scale_out) x_scale_out = ws_scale(c);
+    // caller's buffers when given, else through the staging buffers
+    if (!x_q_out && (size_t)M * K > stage_q_bytes) return WQ_ERR_WORKSPACE;
+    if (!x_scale_out && (size_t)M * 4 > stage_s_bytes) return WQ_ERR_WORKSPACE;
+    if (!x_q_out) x_q_out = stage_q;
+    if (!x_scale_out) x_scale_out = stage_s;
     int r = wq_dynamic_quant(c, x, WQ_IN_BF16, M, K, ldx, nullptr, 0.0f, nullptr, x_q_out, x_scale_out, stream);
     if (r != WQ_OK) return r;
     wq_matmul_desc d{};
@@ -622,6 +640,73 @@ int wq_fused_quant_matmul(wq_ctx* c, const void* x, int64_t M, int64_t K, int64_
                  (long long)M, (long long)N, (long long)K, nt, rr, (long long)((N + nt - 1) / nt),
                  (long long)((M + rr - 1) / rr), c->num_cu);
   return status_of(e);
+}
+
+// The allocation-free variant's staging buffer: the INT8 payload [M, K] (at most
+// kScratchQBytes), then its f32 scales [M] (at most kScratchScaleBytes).  One copy per device,
+// held until the process ends; host code reaches it only through the address that
+// hipGetSymbolAddress returns for the device (static_device).
+constexpr size_t kScratchQBytes = 16u << 20;
+constexpr size_t kScratchScaleBytes = 64u << 10;
+static __device__ __align__(256) int8_t scratch[kScratchQBytes + kScratchScaleBytes];
+
+struct StaticDevice {
+  bool ready;
+  int num_cu;
+  int8_t* scratch;  // this device's address of `scratch`
+};
+constexpr int kMaxDevices = 64;
+StaticDevice g_static[kMaxDevices];
+std::mutex g_static_mu;
+
+// First call on a device: with the device current, check it is gfx950, read its CU count and
+// the device address of `scratch`; later calls reuse them.
+int static_device(int device, StaticDevice* out) {
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticDevice& d = g_static[device];
+  if (!d.ready) {
+    DeviceGuard g(device);
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return WQ_ERR_DEVICE;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return WQ_ERR_DEVICE;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return WQ_ERR_DEVICE;
+    d.num_cu = prop.multiProcessorCount;
+    d.scratch = static_cast<int8_t*>(p);
+    d.ready = true;
+  }
+  *out = d;
+  return WQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int wq_fused_quant_matmul(wq_ctx* c, const void* x, int64_t M, int64_t K, int64_t ldx, const int8_t* w,
+                          const float* w_scale, int64_t N, void* y, int64_t ldy, int8_t* x_q_out,
+                          float* x_scale_out, int32_t* acc_out, void* stream) {
+  if (!c) return WQ_ERR_NULL;
+  return fused_impl(c, x, M, K, ldx, w, w_scale, N, y, ldy, x_q_out, x_scale_out, acc_out, stream, ws_q(c), kWsQBytes,
+                    ws_scale(c), kWsScaleBytes);
+}
+
+int wq_fused_quant_matmul_static(int device, const void* x, int64_t M, int64_t K, int64_t ldx, const int8_t* w,
+                                 const float* w_scale, int64_t N, void* y, int64_t ldy, int8_t* x_q_out,
+                                 float* x_scale_out, int32_t* acc_out, void* stream) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || device < 0 || device >= count || device >= kMaxDevices)
+    return WQ_ERR_DEVICE;
+  StaticDevice sd;
+  const int r = static_device(device, &sd);
+  if (r != WQ_OK) return r;
+  wq_ctx c{};
+  c.device = device;
+  c.num_cu = sd.num_cu;
+  c.ws = nullptr;
+  c.ws_bytes = 0;
+  read_env_knobs(&c);
+  return fused_impl(&c, x, M, K, ldx, w, w_scale, N, y, ldy, x_q_out, x_scale_out, acc_out, stream, sd.scratch,
+                    kScratchQBytes, reinterpret_cast<float*>(sd.scratch + kScratchQBytes), kScratchScaleBytes);
 }
 
 int wq_pack_weight_i8(wq_ctx* c, const int8_t* w, int64_t N, int64_t K, int64_t ldw, int8_t* wp, void* stream) {

@@ -232,6 +232,24 @@ int wq_fused_quant_matmul(wq_ctx* ctx, const void* x, int64_t M, int64_t K, int6
                           const int8_t* w, const float* w_scale, int64_t N, void* y, int64_t ldy,
                           int8_t* x_q_out, float* x_scale_out, int32_t* acc_out, void* stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph capture, serving
+ * loops that must not allocate, harnesses that forbid it.  wq_fused_quant_matmul with no
+ * context and no workspace: `device` is the HIP device index, every other argument and the
+ * outputs are those of wq_fused_quant_matmul, bit for bit (the knobs come from the same
+ * environment variables, read on every call).  When M is above the one-launch limit and
+ * x_q_out / x_scale_out are NULL, the INT8 payload and its scales are staged in a static
+ * device buffer of the library instead of a context workspace: at most 16 MiB of payload
+ * (M * K bytes) and 16384 scales (M <= 16384); larger calls return WQ_ERR_WORKSPACE and launch
+ * nothing.  Each device the library runs on holds that buffer (16 MiB + 64 KiB) until the
+ * process ends; the first call on a device looks up its address there, later calls only
+ * launch.  The call allocates nothing (no hipMalloc, no hipFree, no host heap).  Calls on one
+ * device share the buffer: two such calls that may overlap in time (on different streams, or
+ * from different host threads) race and must be serialised by the caller.  WQ_ERR_DEVICE for
+ * an invalid or non-gfx950 device. */
+int wq_fused_quant_matmul_static(int device, const void* x, int64_t M, int64_t K, int64_t ldx,
+                                 const int8_t* w, const float* w_scale, int64_t N, void* y, int64_t ldy,
+                                 int8_t* x_q_out, float* x_scale_out, int32_t* acc_out, void* stream);
+
 /* Which launch sequence wq_fused_quant_matmul takes for these sizes on this context:
  * 0 = the quant kernel, then the GEMM (two launches); 1 = one launch of the dot4 GEMV
  * kernel (M <= WQ_FUSED_GEMV_MAX_M, or M <= 4 with a K the MFMA kernel does not take:
