@@ -42,6 +42,7 @@ K_A, N_A = 4096, 1024
 ROTATE_BYTES = 512 << 20
 ROOFLINE_KERNEL = "k_fused_decode"  # the one-launch fused kernel on fragment-order weights, every <R, CT> instance
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_fused_decode_wq_a.json")
+TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace_k_fused_decode_wq_a.json")
 KERNEL_SOURCES = ("k_fused.hip", "wq_device.h", "wq_kernels.h")  # the roofline kernel and the headers it includes
 
 
@@ -119,6 +120,32 @@ def traffic_summary(fetch_dir, write_dir, probe_log):
     }
 
 
+def trace_summary(stats_csv, probe_log):
+    """Per-launch duration of the roofline kernel (fragment-order instances) from a
+    rocprofv3 --kernel-trace --stats run of the headline (bench.py --no-rows --no-cpu-baseline
+    --no-sweep), next to the same run's event-timed figure."""
+    import csv
+
+    line = [ln for ln in open(probe_log) if ln.startswith("{")][-1]
+    run = json.loads(line)
+    rows = [r for r in csv.DictReader(open(stats_csv)) if ROOFLINE_KERNEL in r["Name"] and "true>" in r["Name"]]
+    calls = sum(int(r["Calls"]) for r in rows)
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    return {
+        "kernel": ROOFLINE_KERNEL + "<R, CT, false, true>",
+        "command": "rocprofv3 --kernel-trace --stats -d gpurun_out/kt_head -o run --output-format csv -- python bench.py "
+                   "--no-rows --no-cpu-baseline --no-sweep > gpurun_out/kt_head.log; python bench.py --trace-summary "
+                   "gpurun_out/kt_head/run_kernel_stats.csv gpurun_out/kt_head.log > "
+                   "profiles/kernel_trace_k_fused_decode_wq_a.json",
+        "instances": {r["Name"].split("(")[0].replace("void ", ""): {"calls": int(r["Calls"]),
+                                                                   "mean_us": round(float(r["AverageNs"]) / 1e3, 3)}
+                      for r in rows},
+        "trace_us_per_launch_mean": round(total / calls / 1e3, 3),
+        "event_us_per_call_same_run": run["value"],
+        "kernel_source_hash": kernel_source_hash(),
+    }
+
+
 def cpu_baseline(budget_s=10.0):
     """Time the CPU oracle (as it stands) on the same workload: the full fused chain at
     every M of the sweep, repeated until about budget_s seconds have passed."""
@@ -141,10 +168,19 @@ def cpu_baseline(budget_s=10.0):
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": el / calls * 1e6,
         "unit": "us per fused W8A8 linear call (mean over the M sweep)",
         "cores": int(threads),
+        "cpu": model,
         "kind": "oracle",
         "sample": f"{calls} oracle calls ({calls // len(SWEEP)} passes over M in {list(SWEEP)}, K=4096, N=1024) in "
                   f"{el:.1f} s",
@@ -162,6 +198,8 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true", help="only the roofline kernel's launches, for counters")
     ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_LOG"),
                     help="write the traffic JSON from two --traffic-probe counter runs (no GPU)")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "RUN_LOG"),
+                    help="write the kernel-trace JSON from a rocprofv3 --stats run of the headline (no GPU)")
     ap.add_argument("--prefill-probe", action="store_true",
                     help="only two launches of the M=8192 prefill GEMM on random operands, for counters")
     args = ap.parse_args()
@@ -171,6 +209,9 @@ def main():
         sys.exit(2)
     if args.traffic_summary:
         print(json.dumps(traffic_summary(*args.traffic_summary), indent=1))
+        return
+    if args.trace_summary:
+        print(json.dumps(trace_summary(*args.trace_summary), indent=1))
         return
 
     import numpy as np
@@ -199,14 +240,6 @@ def main():
     roof_ms = [M for M in SWEEP if paths[M] == 2]
     if roof_ms != list(SWEEP):
         raise SystemExit(f"the packed fused call needs the one-launch MFMA path at every M; paths {paths}")
-
-    def graph_len(steps):
-        """Steps per captured graph: the largest divisor of `steps` not above R, so the
-        timed region is a whole number of replays and each step uses its own copy."""
-        for g in range(min(steps, R), 0, -1):
-            if steps % g == 0:
-                return g
-        return 1
 
     def capture(fn, n):
         """One graph running fn(r) for r = 0..n-1 back to back (one rotation slot each), so
@@ -246,9 +279,33 @@ def main():
         for M in Ms:
             wq.wq_fused_quant_matmul_packed(xs[M][r], wps[r], sws[r], N_A, y=ys[M][r])
 
+    def fused_call(slot, M):
+        wq.wq_fused_quant_matmul_packed(xs[M][slot], wps[slot], sws[slot], N_A, y=ys[M][slot])
+
     def fused_plain_step(r, Ms=SWEEP):
         for M in Ms:
             wq.wq_fused_quant_matmul(xs[M][r], ws[r], sws[r], y=ys[M][r])
+
+    def time_cycle(cycle, P, steps, warmup, make_partial):
+        """`cycle` runs P steps; replay it to cover `warmup` steps, then time exactly `steps`
+        steps between two events on the replay stream: whole cycles, then a graph of the
+        remaining steps (make_partial(n) captures the first n steps of a cycle, whose copies
+        were last used a whole cycle earlier).  Returns us per step."""
+        rest = steps % P
+        part = make_partial(rest) if rest else None
+        with torch.cuda.stream(stream):
+            for _ in range(-(-warmup // P)):
+                cycle.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(steps // P):
+                cycle.replay()
+            if part is not None:
+                part.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / steps
 
     def time_in_graph(fn, n=64):
         """Mean us per call of fn(r) over replays of a graph of n back-to-back calls
@@ -315,13 +372,19 @@ def main():
             assert bf16_ulp_distance(got, ref).max() <= 1, "fused linear disagrees with the oracle"
 
     # ---- headline: fused decode linear over the sweep -------------------------------------
-    G = graph_len(args.steps)
-    g_all = capture(lambda r: fused_step(r), G)
+    # Every call reads its own weight copy: step p of a cycle of R / len(SWEEP) steps runs
+    # the sweep's M values on copies len(SWEEP) p .. len(SWEEP) p + len(SWEEP) - 1, one graph
+    # per step, so the timed region cycles through all R copies (>= 512 MiB, past L2 and the
+    # Infinity Cache) whatever --steps is, and a copy comes back only after R other calls.
+    n_m = len(SWEEP)
+    P = R // n_m  # steps per cycle through all R copies
+    cycle = capture(lambda c: fused_call(c, SWEEP[c % n_m]), P * n_m)
     t0 = time.perf_counter()
-    us_step = time_graph(g_all, G, args.steps, args.warmup)
+    us_step = time_cycle(cycle, P, args.steps, args.warmup,
+                         lambda n: capture(lambda c: fused_call(c, SWEEP[c % n_m]), n * n_m))
     wall = time.perf_counter() - t0
-    us_per_call = us_step / len(SWEEP)
-    del g_all
+    us_per_call = us_step / n_m
+    del cycle
 
     # ---- per-M: fused (always, for the roofline) and standalone -----------------------------
     xq = {M: [torch.empty((M, K_A), dtype=torch.int8, device=dev) for _ in range(R)] for M in SWEEP}
@@ -383,8 +446,20 @@ def main():
                     traffic = tr.get("hbm_bytes_per_launch_mean")
             except Exception:
                 traffic = None
+        trace = None
+        if os.path.exists(TRACE_FILE):
+            try:
+                tf = json.load(open(TRACE_FILE))
+                if tf.get("kernel_source_hash") == kernel_source_hash():
+                    trace = tf.get("trace_us_per_launch_mean")
+            except Exception:
+                trace = None
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "duration_source": "HIP events around graph replays of cold calls on the replay stream; "
+                                       "the rocprofv3 kernel trace of the same workload reads longer per launch "
+                                       "(its per-dispatch cost weighs most on these few-us launches)",
+                    "trace_us_per_launch_mean": trace,
                     "kernel": ROOFLINE_KERNEL + "<R, CT, false, true> (fragment-order weights)",
                     "launches": f"one per fused call at M in {roof_ms} (K=4096, N=1024)",
                     "bytes_per_launch_mean": round(b_sum / len(roof_ms)),
@@ -468,13 +543,20 @@ def main():
             "workload": "wq_b wide linear INT8 GEMM (x_q given): M=8192, K=1024, N=32768, bf16 out",
             "kernel": "k_gemm_i8_big", "us": round(us_p, 2), "TOPS": round(tops, 1),
             "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
-        # ---- standalone per-token quant at the prefill shape (HBM bound) --------------------
-        us_q = time_in_graph(lambda r: wq.wq_dynamic_quant(xp, x_q=xqp, x_scale=xsp))
+        # ---- standalone per-token quant at the prefill shape (HBM bound): 24 rotating copies of
+        # X (16 MiB) and of its outputs (8 MiB + 32 KiB), 576 MiB in all, so every call is cold
+        del wp, yp
+        Rq = 24
+        xps = [xp.clone() for _ in range(Rq)]
+        xqs = [torch.empty_like(xqp) for _ in range(Rq)]
+        xss = [torch.empty_like(xsp) for _ in range(Rq)]
+        us_q = time_in_graph(lambda r: wq.wq_dynamic_quant(xps[r], x_q=xqs[r], x_scale=xss[r]), Rq)
         qb = 2 * Mp * Kp + Mp * Kp + 4 * Mp
-        rows["int8_quant_m8192"] = {"workload": "per-token INT8 quant X bf16 [8192, 1024] (one buffer, reused by every call)", "kernel": "k_dynamic_quant",
+        rows["int8_quant_m8192"] = {"workload": f"per-token INT8 quant X bf16 [8192, 1024], {Rq} rotating copies of "
+                                                "inputs and outputs (cold)", "kernel": "k_dynamic_quant",
                                     "us": round(us_q, 2), "GBps": round(qb / us_q / 1e3, 1),
                                     "frac_hbm": round(qb / us_q / 1e3 / HBM_PEAK_GBS, 4)}
-        del xp, wp, yp, xqp
+        del xp, xqp, xps, xqs, xss
 
         # ---- FP8 per-token-group quant (packed UE8M0) and the grouped contraction ----------
         # 16 rotating copies of the 32 MiB weight and of the activations (>= 512 MiB in all
