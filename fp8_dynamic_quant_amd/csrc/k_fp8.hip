@@ -16,8 +16,8 @@
 // power-of-two scaling.  The four exponent bytes meet in lane 0, which writes the whole
 // packed word - no byte-granular read-modify-write and no dependence on prior contents.
 // Waves with t in [T, TA) write the zero padding words.  On large grids (16384 waves or
-// more at one pack per wave) a wave takes two consecutive packs of its (t, g), with both
-// packs' loads issued before the first is quantised.
+// more at one pack per wave) a wave takes two, from 32768 four, consecutive packs of its
+// (t, g), with every pack's loads issued before the first is quantised.
 #include "wq_device.h"
 #include "wq_kernels.h"
 
@@ -41,6 +41,16 @@ __device__ __forceinline__ int ue8m0_exp(float a) {
   return e < -127 ? -127 : e;
 }
 
+// max over the 16 lanes of each DPP row (non-negative f32): quad swaps, then the half-row
+// and row mirrors; every lane of the row ends with the row's max
+__device__ __forceinline__ float row16_max(float a) {
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, false)));   // [1,0,3,2]
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, false)));   // [2,3,0,1]
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x141, 0xF, 0xF, false)));  // half mirror
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x140, 0xF, 0xF, false)));  // row mirror
+  return a;
+}
+
 // PPW packs per wave (consecutive packs of one (t, g)); their loads are issued first
 template <int PPW>
 __global__ __launch_bounds__(256) void k_group_quant_fp8(const uint16_t* __restrict__ x, int64_t T, int G,
@@ -62,7 +72,7 @@ __global__ __launch_bounds__(256) void k_group_quant_fp8(const uint16_t* __restr
   for (int i = 0; i < PPW; ++i) {  // clamped in-range loads, all before the first use
     const int h = min(4 * (pw * PPW + i) + q, HG - 1);
     const uint16_t* src = x + (min(t, T - 1) * G + g) * (int64_t)D + (int64_t)h * 128 + (lane & 15) * 8;
-    if constexpr (PPW == 2) {
+    if constexpr (PPW >= 2) {
       // large grids: streaming loads (the rows are read once; measured 14.7 -> 13.7 us at
       // T = 512, while the small grids measured slower with them)
       const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src));
@@ -89,8 +99,12 @@ __global__ __launch_bounds__(256) void k_group_quant_fp8(const uint16_t* __restr
       float a = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(v[j]));
+      if constexpr (PPW >= 4) {
+        a = row16_max(a);  // the quarter is one DPP row (exec covers whole rows here)
+      } else {
 #pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+        for (int o = 8; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+      }
       const int e = ue8m0_exp(a);
       const float sc = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-127, 126]
       uint32_t lo = 0, hi = 0;
@@ -190,17 +204,21 @@ hipError_t launch_group_quant_mx(const uint16_t* x, int64_t T, int G, int D, uin
 }
 
 hipError_t launch_group_quant_fp8(const uint16_t* x, int64_t T, int G, int D, uint8_t* xq, int32_t* xs,
-                                  hipStream_t st) {
+                                  hipStream_t st, int ppw_force) {
   const int HG = D / 128, PH = (HG + 3) / 4;
   const int64_t TA = (T + 3) / 4 * 4;
-  // two packs per wave once the grid is large (>= 64 waves per CU at one pack per
-  // wave): fewer, longer waves with both loads in flight measured faster there and
-  // slower on small grids
-  const int ppw = TA * G * PH >= 16384 ? 2 : 1;
+  // two packs per wave once the grid is large (>= 64 waves per CU at one pack per wave),
+  // four from 128: fewer, longer waves with every load in flight measured faster there and
+  // slower on small grids (G = 8, D = 4096, us at T = 64 / 256 / 512: one pack 3.77 / 8.79 /
+  // 14.2, two 4.61 / 7.81 / 13.75, four 4.77 / 8.05 / 12.62)
+  int ppw = TA * G * PH >= 32768 ? 4 : (TA * G * PH >= 16384 ? 2 : 1);
+  if (ppw_force == 1 || ppw_force == 2 || ppw_force == 4) ppw = ppw_force;
   const int64_t waves = TA * G * ((PH + ppw - 1) / ppw);
   if (waves == 0) return hipSuccess;
   dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-  if (ppw == 2)
+  if (ppw == 4)
+    hipLaunchKernelGGL(k_group_quant_fp8<4>, grid, block, 0, st, x, T, G, D, xq, xs);
+  else if (ppw == 2)
     hipLaunchKernelGGL(k_group_quant_fp8<2>, grid, block, 0, st, x, T, G, D, xq, xs);
   else
     hipLaunchKernelGGL(k_group_quant_fp8<1>, grid, block, 0, st, x, T, G, D, xq, xs);

@@ -42,6 +42,7 @@ struct wq_ctx {
   int fused_gemv_max_m;  // largest M the fused GEMV takes instead (WQ_FUSED_GEMV_MAX_M)
   int fused_r;           // one-launch fused kernel: rows per workgroup (WQ_FUSED_R; 0 = automatic)
   int fused_nt;          // one-launch fused kernel: columns per workgroup (WQ_FUSED_NT; 0 = automatic)
+  int gq_ppw;            // FP8 group quant: packs per wave (WQ_GQ_PPW, 1, 2 or 4; 0 = automatic)
 };
 
 namespace {
@@ -174,6 +175,9 @@ void read_env_knobs(wq_ctx* c) {
   c->fused_r = fr2 ? std::atoi(fr2) : 0;
   if (c->fused_r != 0 && c->fused_r != 1 && c->fused_r != 2 && c->fused_r != 4 && c->fused_r != 8 && c->fused_r != 16)
     c->fused_r = 0;
+  const char* gp = std::getenv("WQ_GQ_PPW");
+  c->gq_ppw = gp ? std::atoi(gp) : 0;
+  if (c->gq_ppw != 1 && c->gq_ppw != 2 && c->gq_ppw != 4) c->gq_ppw = 0;
   const char* fn = std::getenv("WQ_FUSED_NT");
   c->fused_nt = fn ? std::atoi(fn) : 0;
   if (c->fused_nt != 0 && c->fused_nt != 4 && c->fused_nt != 8 && c->fused_nt != 16 && c->fused_nt != 32)
@@ -302,7 +306,7 @@ int wq_group_quant_fp8_ue8m0(wq_ctx* c, const void* x, int64_t T, int64_t G, int
   if (!al16(x) || !al16(x_q) || !al16(x_s)) return WQ_ERR_ALIGN;
   DeviceGuard g(c->device);
   hipError_t e = wq::launch_group_quant_fp8(static_cast<const uint16_t*>(x), T, (int)G, (int)D, x_q, x_s,
-                                            static_cast<hipStream_t>(stream));
+                                            static_cast<hipStream_t>(stream), c->gq_ppw);
   if (c->log)
     std::fprintf(stderr, "[wq] group_quant_fp8 T=%lld G=%lld D=%lld waves=%lld\n", (long long)T, (long long)G,
                  (long long)D, (long long)(((T + 3) / 4 * 4) * G * ((D / 128 + 3) / 4)));

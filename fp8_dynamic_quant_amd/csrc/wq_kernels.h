@@ -103,7 +103,7 @@ bool fp8_decode32_fits(int T, int N, int K);
 
 // FP8 group quant with packed UE8M0 scales (k_fp8.hip).
 hipError_t launch_group_quant_fp8(const uint16_t* x, int64_t T, int G, int D, uint8_t* xq, int32_t* xs,
-                                  hipStream_t st);
+                                  hipStream_t st, int ppw_force = 0);
 // the same with MX-like 32-element blocks (D % 32 == 0; HG = D / 32)
 hipError_t launch_group_quant_mx(const uint16_t* x, int64_t T, int G, int D, uint8_t* xq, int32_t* xs,
                                  hipStream_t st);

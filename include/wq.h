@@ -92,7 +92,9 @@ size_t wq_workspace_bytes(void);
  *   WQ_FP8_RT=r       grouped FP8 contraction at T <= 16: 16-token tiles per workgroup
  *                     (1..4; 0 = auto, all of them);
  *   WQ_FP8_COLS=16    grouped FP8 contraction at 16 < T <= 64: keep the 16-column kernel
- *                     instead of the 32-column one (default 32).
+ *                     instead of the 32-column one (default 32);
+ *   WQ_GQ_PPW=p       FP8 group quant: packs of four hidden groups per wave (1, 2 or 4;
+ *                     0 = auto by grid size).
  * Values out of range fall back to the default.  Every setting gives bit-identical
  * results except WQ_FP8_COLS, which changes the order of the FP8 contraction's f32 sums
  * (4 or 8 partial sums per output; both within the contraction's stated tolerance).  The
