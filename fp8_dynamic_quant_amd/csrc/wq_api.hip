@@ -458,7 +458,7 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   t.acc_out = d->acc_out;
   t.seg_offsets = d->seg_offsets;
   t.batch = (int)d->batch;
-  if (wq::big_fits((int)M, (int)N, (int)K, d->lda, d->ldy) && c->num_cu % 8 == 0) {
+  if (wq::big_fits((int)M, (int)N, (int)K, d->lda, d->ldy, d->y, d->acc_out) && c->num_cu % 8 == 0) {
     hipError_t e = wq::launch_gemm_i8_big(t, c->num_cu, st);
     if (c->log)
       std::fprintf(stderr, "[wq] quant_matmul int8 persistent-256 M=%lld N=%lld K=%lld tiles=%lld grid=%d\n",

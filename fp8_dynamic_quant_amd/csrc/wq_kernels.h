@@ -87,7 +87,7 @@ hipError_t launch_seg_decode(const TileArgs& a, int num_cu, hipStream_t st);
 bool seg_decode_fits(int N, int K, int epilogue, int64_t batch);
 // persistent 256x256 INT8 tiles for large M (k_gemm_big.hip)
 hipError_t launch_gemm_i8_big(const TileArgs& a, int num_cu, hipStream_t st);
-bool big_fits(int M, int N, int K, int64_t lda, int64_t ldy);
+bool big_fits(int M, int N, int K, int64_t lda, int64_t ldy, const void* y, const void* acc_out);
 
 // FP8 grouped contraction for T <= 64, K % 512 == 0, K <= 4096 (k_fp8_decode.hip):
 // 16 output columns of one group and min(rt_per_wg, ceil(T / 16)) 16-token tiles per

@@ -200,7 +200,8 @@ def _bf16_rne_bits(f32):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-@pytest.mark.parametrize("M,K,N", [(2, 4096, 1024), (8, 4096, 1024), (70, 1024, 48), (300, 1024, 528), (512, 1024, 32768)])
+@pytest.mark.parametrize("M,K,N", [(2, 4096, 1024), (8, 4096, 1024), (70, 1024, 48), (300, 1024, 528), (512, 1024, 32768),
+                                   (1000, 2048, 1536), (257, 128, 256), (260, 256, 272), (2600, 256, 8208)])
 def test_epilogue_is_the_documented_f32_sequence(M, K, N):
     """Stricter than the 1-ulp bound: the bf16 output equals bf16_RN(RN(RN(f32(acc) * s_m) * sw_n))
     bit for bit, the f32 operation sequence the kernels document (f32(acc) rounds to nearest
@@ -237,6 +238,10 @@ def test_wq_b_prefill_8192_sampled_rows():
     accr = il.gemm_int8_int32(q, w)
     assert np.array_equal(host(acc[torch.from_numpy(rows).to(DEV)]), accr)
     _y_within_one_ulp(host_bf16_bits(y[torch.from_numpy(rows).to(DEV)]), il.epilogue_bf16(accr, s, sw))
+    # the production launch (no accumulator export) writes the same bytes
+    y2 = wq.wq_quant_matmul(xq, xs, wd, swd)
+    torch.cuda.synchronize()
+    assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
 
 
 @pytest.mark.parametrize("M,K,N", [(3, 272, 48), (65, 272, 48), (130, 1040, 208), (64, 64, 16), (17, 4096, 1040),
