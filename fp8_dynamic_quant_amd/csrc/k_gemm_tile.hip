@@ -306,6 +306,215 @@ __device__ __forceinline__ void tile_epilogue(const TileArgs& p, int m0, int row
   }
 }
 
+// FP8 (and MX) dense tiles: the same 128 x 128 tile and LDS ring, scheduled for one wave
+// per SIMD.  Per 128-byte slice each wave runs 8 block-scaled MFMAs; the schedule keeps the
+// MFMA pipe fed across the slice boundary:
+//  * the slice's nine DMA instructions per wave (A, B, the scale words) are issued one per
+//    MFMA instead of in one burst, which held the wave at the address unit for ~600 cycles a
+//    slice with the MFMA pipe idle;
+//  * LDS operand reads run a whole slice ahead, into a second register set: after slice
+//    kt's first MFMA comes the wait and barrier that make slice kt+1 visible, then slice
+//    kt+1's fragments and scale words are read while slice kt's other seven MFMAs run.
+//    (Under the DMA traffic an LDS read takes ~700 cycles to return, and with LDS-DMA loads
+//    in flight the compiler waits for all outstanding LDS reads at once, so a read must be
+//    issued well before the MFMA that needs it.)
+//  * the MFMA takes the W fragment as its first operand, so each lane ends with four
+//    consecutive output columns of one row; the epilogue stages bf16 rows through LDS and
+//    each store instruction writes eight whole 128-byte rows of Y.
+// The DMA issued during slice kt fills the stage of slice kt-1, whose reads every wave
+// finished (and waited for) before the barrier of slice kt-1.
+
+// DMA instruction i (0..3) of a 128-row x 128-byte operand slice (the i-th of dma_slice)
+__device__ __forceinline__ void dma_slice_one(const int8_t* src, int64_t ld, int r0, int rows, int k0, int8_t* dst,
+                                              int wv, int lane, int i) {
+  const int pos = (wv * 4 + i) * 64 + lane;
+  const int r = pos >> 3, pc = pos & 7;
+  const int c = pc ^ tswz_of(r);
+  const int gr = min(r0 + r, rows - 1);
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + (int64_t)gr * ld + k0 + c * 16),
+                                   (lds_ptr_t)(dst + (wv * 4 + i) * 1024), 16, 0, 0);
+}
+
+template <int STAGES, bool MX>
+__device__ __forceinline__ void fp8_tile_mainloop(const TileArgs& p, int8_t* smem, const int8_t* A, int m0, int row_hi,
+                                                  const int8_t* B, int n0, int g, v16f (&acc)[2][2]) {
+  using Ring = TileRing<true, false, STAGES>;
+  static_assert(Ring::kDmaPerSlice == 9, "A 4 + B 4 + scales 1 per wave");
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int K = p.K, N = p.N;
+  const int KT = K / kBK;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  constexpr bool mx = MX;  // a template parameter: a runtime flag put branches in the loop body
+  const int PH = mx ? KT : (KT + 3) >> 2;
+  const int32_t* xs_g = p.a_scale_packed + (int64_t)g * PH * p.a_scale_tokens;
+  const float* ws_g = !mx ? p.w_scale + ((int64_t)g * (N / 128) + (n0 >> 7)) * KT : nullptr;
+  const uint32_t* wsw_g = mx ? reinterpret_cast<const uint32_t*>(p.w_scale) + (int64_t)g * N * KT : nullptr;
+
+  // DMA instruction d (0..8) of slice kt: A 0-3, B 4-7, the scale words 8 (as tile_mainloop)
+  auto issue_one = [&](int kt, int d, int slot) {
+    int8_t* st = smem + (slot % Ring::kStages) * Ring::kStageB;
+    if (d < 4) {
+      dma_slice_one(A, p.lda, m0, row_hi, kt * kBK, st, wv, lane, d);
+    } else if (d < 8) {
+      dma_slice_one(B, K, n0, N, kt * kBK, st + kSlice, wv, lane, d - 4);
+    } else {
+      // both addresses computed on every lane and one picked by a select (a conditional
+      // address computation became a branch that split the loop body)
+      const int r = min(m0 + wv * 32 + (lane & 31), row_hi - 1);
+      const char* xa = reinterpret_cast<const char*>(xs_g + (int64_t)(mx ? kt : kt >> 2) * p.a_scale_tokens + r);
+      const char* wa = mx ? reinterpret_cast<const char*>(wsw_g + (int64_t)min(n0 + wv * 32 + (lane & 31), N - 1) * KT + kt)
+                          : reinterpret_cast<const char*>(ws_g + kt);
+      const bool w_lane = mx ? lane >= 32 : lane == 32;
+      const int64_t dw = wa - xa;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xa + (w_lane ? dw : (int64_t)0)),
+                                       (lds_ptr_t)(st + 2 * kSlice + wv * 256), 4, 0, 0);
+    }
+  };
+  // The loop body is straight-line code (a branch lets the compiler sink the MFMAs below
+  // it): every iteration issues the DMA of slice kt + STAGES - 1, past the last slice a copy
+  // of the last slice into the stage no later slice uses, so exactly STAGES - 2 later slices
+  // of 9 instructions each are in flight at every wait (loads complete in order), and the
+  // final iteration reads fragments it does not use.  __syncthreads() before the epilogue
+  // waits for those copies.
+  static_assert(Ring::kStages == 4, "the waits count the later slices in flight");
+  // at the wait for slice kt+1 (in slice kt, before slice kt+3's DMA goes out) only slice
+  // kt+2's nine instructions are in flight after it
+  auto wait_slice = [&]() { asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); };
+
+  const int ar = wm * 64 + (lane & 31), br = wn * 64 + (lane & 31);
+  const int kh = lane >> 5;
+  // fragments of K step ks (0, 1) of the slice at sa: lane group h holds K bytes 16h..16h+15
+  // of the step in registers 0-3 and 32+16h.. in 4-7 (128-block scales: any shared K order
+  // gives the same sum, so those keep 32 contiguous bytes per lane); row and column scale words
+  // one slice's operands in registers: both K steps' fragments and the scale words
+  struct Frags {
+    v8i a[2][2], b[2][2];  // [ks][i]
+    int rw[2], cw[2], scb;
+  };
+  auto read_slice = [&](const int8_t* sa, Frags& f) {
+    const int8_t* sb = sa + kSlice;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c0 = mx ? 4 * ks + kh : 4 * ks + 2 * kh, c1 = mx ? 4 * ks + 2 + kh : 4 * ks + 2 * kh + 1;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const v4i lo = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 32, c0));
+        const v4i hi = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 32, c1));
+        f.a[ks][i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const v4i blo = *reinterpret_cast<const v4i*>(sb + tswz(br + i * 32, c0));
+        const v4i bhi = *reinterpret_cast<const v4i*>(sb + tswz(br + i * 32, c1));
+        f.b[ks][i] = v8i{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
+      }
+    }
+    const int32_t* scw = reinterpret_cast<const int32_t*>(sa + 2 * kSlice);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = ar + i * 32;  // row in the tile; its word sits at (r / 32) * 64 + r % 32
+      f.rw[i] = scw[(r >> 5) * 64 + (r & 31)];
+      const int c = br + i * 32;  // column in the tile (MX): at (c / 32) * 64 + 32 + c % 32
+      f.cw[i] = mx ? scw[(c >> 5) * 64 + 32 + (c & 31)] : 0;
+    }
+    f.scb = (scw[32] >> 23) & 0xFF;  // exponent field of the f32 power-of-two block scale
+  };
+
+  // Slice kt on the operands in `cur` (read one slice earlier).  After its first MFMA: the
+  // wait for this wave's DMA of slice kt+1 and the barrier that makes slice kt+1 visible
+  // (every wave read slice kt-1 one slice ago, so the DMA issued below into its stage is
+  // safe), then slice kt+1's operands are read into `nxt`, a whole slice ahead of their use.
+  // The slice's other seven MFMAs carry the nine DMA instructions of slice kt+3.
+  auto step = [&](int kt, const Frags& cur, Frags& nxt) {
+    const int nk = min(kt + Ring::kStages - 1, KT - 1);
+    const int nst = kt + Ring::kStages - 1;  // the stage slot of slice nk (its copy past the end)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int sub = 2 * ks + kh;  // MX: this lane group's 32-element block of the slice
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = q >> 1, j = q & 1;
+        const int sca = mx ? (cur.rw[i] >> (8 * sub)) & 0xFF : (cur.rw[i] >> (8 * (kt & 3))) & 0xFF;
+        const int scb = mx ? (cur.cw[j] >> (8 * sub)) & 0xFF : cur.scb;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.b[ks][j], cur.a[ks][i], acc[i][j], 0, 0, 0, scb, 0, sca);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks == 0 && q == 0) {
+          wait_slice();
+          lds_barrier();
+          read_slice(smem + ((kt + 1) % Ring::kStages) * Ring::kStageB, nxt);
+        } else {
+          const int d = 4 * ks + q - 1;  // 0..6; the last two instructions go behind the final MFMA
+          issue_one(nk, d, nst);
+          if (ks == 1 && q == 3) {
+            issue_one(nk, 7, nst);
+            issue_one(nk, 8, nst);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  __syncthreads();  // the previous tile's LDS reads are done before the new DMA lands
+  for (int kt = 0; kt < Ring::kStages - 1; ++kt)
+    for (int d = 0; d < Ring::kDmaPerSlice; ++d) issue_one(min(kt, KT - 1), d, kt);
+  // slice 0 has landed once slices 1 and 2 alone may be outstanding
+  asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  lds_barrier();
+  Frags f0, f1;
+  read_slice(smem, f0);
+  // two slices per trip with the operand sets swapped, so no register copies; an odd last
+  // slice after the loop
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    step(kt, f0, f1);
+    step(kt + 1, f1, f0);
+  }
+  if (kt < KT) step(kt, f0, f1);
+}
+
+// FP8 epilogue: acc (W-first MFMA: lane holds row lane % 32 of each 32-row block and columns
+// 8q + 4(lane/32) + r of each 32-column block) -> bf16 rows staged through LDS (144-byte
+// pitch) -> 16-byte stores of whole 128-byte rows
+__device__ __forceinline__ void fp8_tile_epilogue(const TileArgs& p, int8_t* smem, int m0, int row_hi, int n0, int g,
+                                                  v16f (&acc)[2][2]) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wm = wv >> 1, wn = wv & 1, kh = lane >> 5;
+  constexpr int kPitch = 144;
+  __syncthreads();  // every wave is done with the ring: it becomes the staging area
+  int8_t* stg = smem + wv * 64 * kPitch;
+  int8_t* wr = stg + (lane & 31) * kPitch + kh * 8;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        typedef unsigned v2u __attribute__((ext_vector_type(2)));
+        const v16f& a = acc[i][j];
+        // round to nearest even (v_cvt_pk_bf16_f32), as f32_to_bf16_rn for finite values
+        const v2u w = {__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a[4 * q], a[4 * q + 1]}, bf16x2)),
+                       __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a[4 * q + 2], a[4 * q + 3]}, bf16x2))};
+        *reinterpret_cast<v2u*>(wr + i * 32 * kPitch + j * 64 + q * 16) = w;
+      }
+  uint16_t* Y = reinterpret_cast<uint16_t*>(p.y) + (int64_t)g * p.y_batch_stride;
+  const int8_t* rd = stg + (lane / 8) * kPitch + (lane % 8) * 16;
+  v4i rows[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) rows[k] = *reinterpret_cast<const v4i*>(rd + k * 8 * kPitch);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int m = m0 + wm * 64 + k * 8 + lane / 8;
+    if (m < row_hi)
+      __builtin_nontemporal_store(rows[k], reinterpret_cast<v4i*>(Y + (int64_t)m * p.ldy + n0 + wn * 64 + (lane % 8) * 8));
+  }
+}
+
 // Dense or strided groups: one tile per workgroup, (group, tile) items on a 1-D grid.
 template <bool FP8>
 __global__ __launch_bounds__(256) void k_gemm_tile(TileArgs p, int tiles_m, int tiles_n) {
@@ -334,8 +543,16 @@ __global__ __launch_bounds__(256) void k_gemm_tile(TileArgs p, int tiles_m, int 
   const int tm = gm0 + in % gsz, tn = in / gsz;
   const int m0 = tm * kBM, n0 = tn * kBN;
   acc_t<FP8> acc[2][2], acc2[2][2];
-  tile_mainloop<FP8, false, kDenseStages>(p, smem, A, m0, p.M, B, n0, 0, g, acc, acc2);
-  tile_epilogue<FP8, 1>(p, m0, p.M, n0, g, FP8 ? nullptr : p.w_scale + (int64_t)g * p.N, acc, acc2);
+  if constexpr (FP8) {
+    if (p.mx)
+      fp8_tile_mainloop<kDenseStages, true>(p, smem, A, m0, p.M, B, n0, g, acc);
+    else
+      fp8_tile_mainloop<kDenseStages, false>(p, smem, A, m0, p.M, B, n0, g, acc);
+    fp8_tile_epilogue(p, smem, m0, p.M, n0, g, acc);
+  } else {
+    tile_mainloop<FP8, false, kDenseStages>(p, smem, A, m0, p.M, B, n0, 0, g, acc, acc2);
+    tile_epilogue<FP8, 1>(p, m0, p.M, n0, g, p.w_scale + (int64_t)g * p.N, acc, acc2);
+  }
 }
 
 // Expert segments (INT8), persistent.  EPI 1: bf16 [rows, N]; EPI 2: f32 silu(gate)*up [rows, N/2].
