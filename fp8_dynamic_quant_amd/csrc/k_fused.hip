@@ -156,8 +156,9 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
   if constexpr (PREQ) s_pre = p.a_scale[row0 + min(lane, rows - 1)];
   const float wsc_v = p.w_scale[min(n0 + min(t, nt - 1), N - 1)];
   v4i b[CT][kFMaxSteps];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
+  // weight fragment idx = ct * kFMaxSteps + j
+  auto load_w = [&](int idx) {
+    const int ct = idx / kFMaxSteps, j = idx % kFMaxSteps;
     // B column cl of tile ct is output column ct * 16 + cl; columns past nt or N read a
     // column in range and are not stored
     const int c = CT == 1 ? (cl & (nt - 1)) : ct * 16 + cl;
@@ -170,15 +171,21 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
       // below reads half a 128-byte line per step and the other half one step later, so it
       // keeps ordinary loads.
       const int8_t* wfr = p.w + ((int64_t)(kbase >> 6) * (N >> 2) + (n >> 2)) * 256 + kg * 64 + (n & 3) * 16;
-#pragma unroll
-      for (int j = 0; j < kFMaxSteps; ++j)
-        b[ct][j] = __builtin_nontemporal_load(
-            reinterpret_cast<const v4i*>(wfr + (int64_t)min(j, steps - 1) * (N >> 2) * 256));
+      b[ct][j] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wfr + (int64_t)min(j, steps - 1) * (N >> 2) * 256));
     } else {
       const int8_t* wcol = p.w + (int64_t)n * K + kbase + 16 * kg;
-#pragma unroll
-      for (int j = 0; j < kFMaxSteps; ++j) b[ct][j] = *reinterpret_cast<const v4i*>(wcol + min(j, steps - 1) * 64);
+      b[ct][j] = *reinterpret_cast<const v4i*>(wcol + min(j, steps - 1) * 64);
     }
+  };
+  // With several rows to quantise the weights are requested only once the rows have landed,
+  // a few fragments per quantised row: issued up front they queued ahead of the rows at the
+  // address unit (which takes ~64 bytes a cycle per CU) and held back the absmax and the
+  // quantisation, whose VALU work then covers their flight instead.
+  constexpr bool kLateW = !PREQ && R >= 4;  // at R = 2 the late weights were measured slower (5.08 -> 5.21 us)
+  constexpr int kWLoads = CT * kFMaxSteps;
+  if constexpr (!kLateW) {
+#pragma unroll
+    for (int idx = 0; idx < kWLoads; ++idx) load_w(idx);
   }
 
   if constexpr (PREQ) {
@@ -212,6 +219,10 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
   uint32_t bad = 0;  // rows whose chunk needs the exact path (bit r)
 #pragma unroll
   for (int r = 0; r < R; ++r) {
+    if constexpr (kLateW) {  // this row's share of the weight fragments, outside any branch
+#pragma unroll
+      for (int idx = r * kWLoads / R; idx < (r + 1) * kWLoads / R; ++idx) load_w(idx);
+    }
     if (r < rows) {  // uniform
       const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_l), r));
       const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_l), r));
