@@ -146,6 +146,143 @@ def trace_summary(stats_csv, probe_log):
     }
 
 
+# kernels of the row probe: (label, kernel-name fragment, algorithmic bytes, algorithmic ops)
+def _row_kernels():
+    Mp, Kp, Np = 8192, 1024, 32768
+    G8, D8, N8 = 8, 4096, 1024
+    out = [("prefill GEMM M=8192 K=1024 N=32768", "k_gemm_i8_big", Mp * Kp + Np * Kp + 4 * (Mp + Np) + 2 * Mp * Np,
+            2 * Mp * Np * Kp)]
+    T = 512
+    PH, TA = 8, 512
+    out.append(("FP8 group quant T=512 (X bf16 [512, 8, 4096])", "k_group_quant_fp8",
+                3 * T * G8 * D8 + 4 * G8 * PH * TA, 0))
+    for T, name in ((64, "k_fp8_decode32"), (512, "k_gemm_tile<true>")):
+        TA = (T + 3) // 4 * 4
+        out.append((f"FP8 contraction T={T}", name,
+                    T * G8 * D8 + 4 * G8 * PH * TA + G8 * N8 * D8 + 4 * G8 * (N8 // 128) * (D8 // 128) + 2 * T * G8 * N8,
+                    2 * T * G8 * N8 * D8))
+    out.append(("MoE gate/up, small experts (fragment order)", "k_seg_decode<2", None, None))
+    out.append(("MoE gate/up, large experts (fragment order)", "k_gemm_seg<2>", None, None))
+    out.append(("MoE down, small experts", "k_seg_decode<1", None, None))
+    out.append(("MoE down, large experts", "k_gemm_seg<1>", None, None))
+    return out
+
+
+def rows_probe(wq, syn, dev):
+    """Two launches of each row kernel on cold copies of its inputs, then a 64 MiB device
+    copy for the counter calibration (the shapes and data of the bench rows)."""
+    import numpy as np
+    import torch
+
+    Mp, Kp, Np = 8192, 1024, 32768
+    xp = torch.from_numpy(syn.wq_b_x(Mp).view(np.int16)).to(dev).view(torch.bfloat16)
+    wp_h, swp_h = syn.wq_b_w()
+    wp = [torch.from_numpy(wp_h).to(dev) for _ in range(2)]
+    swp = torch.from_numpy(swp_h).to(dev)
+    xqp, xsp = wq.wq_dynamic_quant(xp)
+    yp = torch.empty((Mp, Np), dtype=torch.bfloat16, device=dev)
+    for r in range(2):
+        wq.wq_quant_matmul(xqp, xsp, wp[r], swp, y=yp)
+    torch.cuda.synchronize()
+    del wp, yp, xp
+    G8, D8, N8, R8 = 8, 4096, 1024, 4
+    wq8_h, ws8_h = syn.fp8_weights(42, G=G8, N=N8, D=D8)
+    wq8 = [torch.from_numpy(wq8_h).to(dev) for _ in range(R8)]
+    ws8 = torch.from_numpy(ws8_h).to(dev)
+    for T in (64, 512):
+        x8h = torch.from_numpy(syn.fp8_group_x(T, G=G8, D=D8).view(np.int16)).to(dev).view(torch.bfloat16)
+        x8 = [x8h.clone() for _ in range(2)]
+        outs = [wq.wq_group_quant_fp8_ue8m0(x8[r]) for r in range(2)]
+        y8 = torch.empty((T, G8, N8), dtype=torch.bfloat16, device=dev)
+        for r in range(2):
+            q8, _, st8 = outs[r]
+            wq.wq_quant_matmul(q8, st8, wq8[r], ws8, y=y8, fp8_groups=G8)
+        torch.cuda.synchronize()
+    del wq8
+    T, H, I, E, topk = 256, 4096, 2048, 256, 8
+    d = syn.moe_inputs(seed=51, T=T, H=H, I=I, E=E, TOPK=topk, weights=False)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5151)
+    w13 = wq.wq_pack_weight_i8(torch.randint(-127, 128, (E, 2 * I, H), generator=gen, device=dev, dtype=torch.int8))
+    w2 = wq.wq_pack_weight_i8(torch.randint(-127, 128, (E, H, I), generator=gen, device=dev, dtype=torch.int8))
+    sw13 = torch.rand((E, 2 * I), generator=gen, device=dev) * 9e-3 + 1e-3
+    sw2 = torch.rand((E, H), generator=gen, device=dev) * 9e-3 + 1e-3
+    ids = torch.from_numpy(d["ids"]).to(dev)
+    h = torch.from_numpy(d["h"].view(np.int16)).to(dev).view(torch.bfloat16)
+    gamma = torch.from_numpy(d["gamma"].view(np.int16)).to(dev).view(torch.bfloat16)
+    for _ in range(2):
+        perm, row_token, offsets = wq.wq_moe_sort(ids, E)
+        q1, s1 = wq.wq_dynamic_quant(h, rms_gamma=gamma, row_index=row_token)
+        hmid = wq.wq_quant_matmul(q1, s1, w13, sw13, seg_offsets=offsets, epilogue=wq.WQ_EPI_SWIGLU_F32, b_fragment=True)
+        q2, s2 = wq.wq_dynamic_quant(hmid)
+        wq.wq_quant_matmul(q2, s2, w2, sw2, seg_offsets=offsets, b_fragment=True)
+    torch.cuda.synchronize()
+    counts = np.bincount(d["ids"].reshape(-1), minlength=E)
+    src = torch.ones(64 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"rows_probe": {"launches_per_kernel": 2, "calibration_copy_bytes": 64 << 20,
+                                     "moe_active_experts": int((counts > 0).sum()),
+                                     "kernel_source_hash": kernel_source_hash()}}))
+
+
+def counter_summary(fetch_dir, write_dir, sq_dir, probe_log):
+    """Markdown table of per-kernel counters (second of the two launches of each kernel)
+    from three rocprofv3 --pmc runs of --rows-probe: FETCH_SIZE, WRITE_SIZE (scaled by the
+    64 MiB copy calibration) and the SQ / GRBM set."""
+    import csv
+
+    probe = None
+    for line in open(probe_log):
+        if line.startswith("{") and "rows_probe" in line:
+            probe = json.loads(line)["rows_probe"]
+    if probe is None:
+        raise SystemExit(f"no rows_probe line in {probe_log}")
+
+    def load(d):
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+        by = {}
+        for r in rows:
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            by.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        return sorted(by.items())
+
+    fetch, write, sq = load(fetch_dir), load(write_dir), load(sq_dir)
+    nbytes = probe["calibration_copy_bytes"]
+    cal_f = [v["FETCH_SIZE"] for (i, n), v in fetch if n == "__amd_rocclr_copyBuffer"][-1]
+    cal_w = [v["WRITE_SIZE"] for (i, n), v in write if n == "__amd_rocclr_copyBuffer"][-1]
+    ff, wf = nbytes / 1024 / cal_f, nbytes / 1024 / cal_w
+
+    def last(rows, frag, ctr):
+        vals = [v[ctr] for (i, n), v in rows if frag in n and ctr in v]
+        return vals[-1] if vals else None
+
+    lines = ["| Kernel (workload) | HBM fetch (MB) | HBM write (MB) | algorithmic (MB) | traffic / algorithmic | "
+             "MFMA instructions | SQ_VALU_MFMA_BUSY_CYCLES / (1024 x GRBM_GUI_ACTIVE / 8) |",
+             "|---|---|---|---|---|---|---|"]
+    for label, frag, alg, ops in _row_kernels():
+        f, w = last(fetch, frag, "FETCH_SIZE"), last(write, frag, "WRITE_SIZE")
+        if f is None or w is None:
+            lines.append(f"| {label} (`{frag}`) | not dispatched | | | | | |")
+            continue
+        fb, wb = f * ff * 1024, w * wf * 1024
+        busy = last(sq, frag, "SQ_VALU_MFMA_BUSY_CYCLES")
+        gui = last(sq, frag, "GRBM_GUI_ACTIVE")
+        mf = last(sq, frag, "SQ_INSTS_MFMA")
+        ratio = f"{busy / (1024 * gui / 8):.3f}" if busy is not None and gui else "-"
+        alg_s = f"{alg / 1e6:.1f}" if alg else "-"
+        tr = f"{(fb + wb) / alg:.2f}" if alg else "-"
+        lines.append(f"| {label} (`{frag}`) | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {alg_s} | {tr} | "
+                     f"{int(mf) if mf is not None else '-'} | {ratio} |")
+    lines.append("")
+    lines.append(f"Calibration: FETCH_SIZE x {ff:.3f}, WRITE_SIZE x {wf:.3f} (the counters' KiB for a 64 MiB "
+                 f"device copy).  MoE active experts: {probe['moe_active_experts']}.  Kernel sources: "
+                 f"{probe['kernel_source_hash']}.")
+    return "\n".join(lines)
+
+
 def cpu_baseline(budget_s=10.0):
     """Time the CPU oracle (as it stands) on the same workload: the full fused chain at
     every M of the sweep, repeated until about budget_s seconds have passed."""
@@ -202,6 +339,11 @@ def main():
                     help="write the kernel-trace JSON from a rocprofv3 --stats run of the headline (no GPU)")
     ap.add_argument("--prefill-probe", action="store_true",
                     help="only two launches of the M=8192 prefill GEMM on random operands, for counters")
+    ap.add_argument("--rows-probe", action="store_true",
+                    help="only the row kernels (prefill GEMM, FP8 group quant and contraction, MoE block), two "
+                         "launches each on cold copies, then a 64 MiB copy, for counters")
+    ap.add_argument("--counter-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "SQ_DIR", "PROBE_LOG"),
+                    help="write the per-kernel counter table from three rocprofv3 --pmc runs of --rows-probe (no GPU)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the kernels run on one MI355X and the "
@@ -212,6 +354,9 @@ def main():
         return
     if args.trace_summary:
         print(json.dumps(trace_summary(*args.trace_summary), indent=1))
+        return
+    if args.counter_summary:
+        print(counter_summary(*args.counter_summary))
         return
 
     import numpy as np
@@ -342,6 +487,10 @@ def main():
             wq.wq_quant_matmul(a, s, w, sw, y=y)
         torch.cuda.synchronize()
         print(json.dumps({"prefill_probe": {"M": Mp, "K": Kp, "N": Np, "launches": 2}}))
+        return
+
+    if args.rows_probe:
+        rows_probe(wq, syn, dev)
         return
 
     if args.traffic_probe:

@@ -41,14 +41,31 @@ constexpr int kF8MaxRT = 4;     // 16-token row tiles: T <= 64
 // bytes [G][N][K/32].  The MFMA applies the scale operand of lane group kq to K bytes
 // 32 kq .. 32 kq + 31 of the block (its operand layout is stated at the loads below), so
 // lane group kq passes byte kq of the activation word and of the column's scale word.
+// Workgroup -> (column slice, group, token-tile block).  Workgroups go to the 8 XCDs round
+// robin by linear id; each XCD gets a contiguous run of items ordered group-major, so with G
+// a multiple of 8 an XCD serves whole groups and its L2 fetches each group's activation
+// codes once (with the plain order every XCD read every group's: 1.41x the algorithmic
+// bytes at T = 64).
+struct Fp8Item {
+  int x, g, z;
+};
+__device__ __forceinline__ Fp8Item fp8_item() {
+  const int S = gridDim.x, G = gridDim.y, Z = gridDim.z;
+  const int L = blockIdx.x + S * (blockIdx.y + G * blockIdx.z);
+  const int total = S * G * Z;
+  const int w = (total & 7) == 0 ? (L & 7) * (total >> 3) + (L >> 3) : L;
+  return Fp8Item{w % S, w / (S * Z), (w / S) % Z};
+}
+
 template <int TPW, bool MX>
 __global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
   constexpr int NW = MX ? kF8MaxSteps : 3;  // packed activation words per token tile
   __shared__ float red[4][TPW][4][64];
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: the weight-scale loads go scalar
-  const int T = p.M, N = p.N, K = p.K, g = blockIdx.y;
-  const int n0 = blockIdx.x * kF8NT;
+  const Fp8Item item = fp8_item();
+  const int T = p.M, N = p.N, K = p.K, g = item.g;
+  const int n0 = item.x * kF8NT;
   const int KT = K >> 7;                 // 128-deep blocks
   const int steps = KT / 4;              // per wave
   const int kb0 = wv * steps;
@@ -61,7 +78,7 @@ __global__ __launch_bounds__(256) void k_fp8_decode(TileArgs p) {
   // K bytes 16q .. 16q+15 in its first four registers and 64+16q .. 64+16q+15 in the last
   // four, and the scale operand of lane group s applies to K bytes 32s .. 32s+31
   const int8_t* A = p.a + (int64_t)g * p.a_batch_stride + kq * 16;
-  const int rt_lo = blockIdx.z * TPW;    // this workgroup's 16-token tiles [rt_lo, rt_lo + TPW)
+  const int rt_lo = item.z * TPW;    // this workgroup's 16-token tiles [rt_lo, rt_lo + TPW)
 
   // Every load is issued before the first wait and none sits under a branch (K steps and
   // rows out of range read clamped in-range addresses; their values go unused), so the
@@ -181,8 +198,9 @@ __global__ __launch_bounds__(512) void k_fp8_decode32(TileArgs p) {
   __shared__ float red[8][TPW][2][4][64];
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int T = p.M, N = p.N, K = p.K, g = blockIdx.y;
-  const int n0 = blockIdx.x * 32;
+  const Fp8Item item = fp8_item();
+  const int T = p.M, N = p.N, K = p.K, g = item.g;
+  const int n0 = item.x * 32;
   const int KT = K >> 7;
   const int steps = KT >> 3;             // 128-deep blocks per wave (1..4)
   const int kb0 = wv * steps;
@@ -192,7 +210,7 @@ __global__ __launch_bounds__(512) void k_fp8_decode32(TileArgs p) {
   // plain: a lane's 32 bytes of a block at 32 kq (halves 16 apart); MX: at 16 kq and 64 + 16 kq
   const int koff = MX ? kq * 16 : kq * 32, khalf = MX ? 64 : 16;
   const int8_t* A = p.a + (int64_t)g * p.a_batch_stride + koff;
-  const int rt_lo = blockIdx.z * TPW;
+  const int rt_lo = item.z * TPW;
   const int w0 = kb0 >> 2;               // the wave's blocks touch packed words w0 and w0 + 1 at most
 
   // ---- weights of both column tiles, 32 bytes per lane per block ----------------------------
