@@ -120,28 +120,35 @@ def traffic_summary(fetch_dir, write_dir, probe_log):
     }
 
 
-def trace_summary(stats_csv, probe_log):
+def trace_summary(stats_csv, probe_log, bench_log=None):
     """Per-launch duration of the roofline kernel (fragment-order instances) from a
     rocprofv3 --kernel-trace --stats run of the headline (bench.py --no-rows --no-cpu-baseline
-    --no-sweep), next to the same run's event-timed figure."""
+    --no-sweep), next to the event-timed per-launch figure of an unprofiled bench run
+    (bench_log) and of the profiled run itself (whose graph replays the tracer slows)."""
     import csv
 
     line = [ln for ln in open(probe_log) if ln.startswith("{")][-1]
     run = json.loads(line)
+    plain = None
+    if bench_log:
+        bl = [ln for ln in open(bench_log) if ln.startswith("{")][-1]
+        plain = json.loads(bl)["roofline"]
     rows = [r for r in csv.DictReader(open(stats_csv)) if ROOFLINE_KERNEL in r["Name"] and "true>" in r["Name"]]
     calls = sum(int(r["Calls"]) for r in rows)
     total = sum(float(r["TotalDurationNs"]) for r in rows)
     return {
         "kernel": ROOFLINE_KERNEL + "<R, CT, false, true>",
         "command": "rocprofv3 --kernel-trace --stats -d gpurun_out/kt_head -o run --output-format csv -- python bench.py "
-                   "--no-rows --no-cpu-baseline --no-sweep > gpurun_out/kt_head.log; python bench.py --trace-summary "
-                   "gpurun_out/kt_head/run_kernel_stats.csv gpurun_out/kt_head.log > "
-                   "profiles/kernel_trace_k_fused_decode_wq_a.json",
+                   "--no-rows --no-cpu-baseline --no-sweep > gpurun_out/kt_head.log; python bench.py --no-sweep --no-cpu-baseline > "
+                   "gpurun_out/bench_plain.log; python bench.py --trace-summary gpurun_out/kt_head/run_kernel_stats.csv "
+                   "gpurun_out/kt_head.log gpurun_out/bench_plain.log > profiles/kernel_trace_k_fused_decode_wq_a.json",
         "instances": {r["Name"].split("(")[0].replace("void ", ""): {"calls": int(r["Calls"]),
                                                                    "mean_us": round(float(r["AverageNs"]) / 1e3, 3)}
                       for r in rows},
         "trace_us_per_launch_mean": round(total / calls / 1e3, 3),
-        "event_us_per_call_same_run": run["value"],
+        "event_us_per_launch_unprofiled_run": plain["us_per_launch_mean"] if plain else None,
+        "event_us_per_launch_by_M_unprofiled_run": plain["us_per_launch"] if plain else None,
+        "event_us_per_launch_same_run_under_the_tracer": run["roofline"]["us_per_launch_mean"],
         "kernel_source_hash": kernel_source_hash(),
     }
 
@@ -335,8 +342,8 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true", help="only the roofline kernel's launches, for counters")
     ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_LOG"),
                     help="write the traffic JSON from two --traffic-probe counter runs (no GPU)")
-    ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "RUN_LOG"),
-                    help="write the kernel-trace JSON from a rocprofv3 --stats run of the headline (no GPU)")
+    ap.add_argument("--trace-summary", nargs="+", metavar="FILE",
+                    help="STATS_CSV RUN_LOG [BENCH_LOG]: write the kernel-trace JSON from a rocprofv3 --stats run of the headline, against an unprofiled bench line (no GPU)")
     ap.add_argument("--prefill-probe", action="store_true",
                     help="only two launches of the M=8192 prefill GEMM on random operands, for counters")
     ap.add_argument("--rows-probe", action="store_true",
