@@ -215,7 +215,17 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
   }
 
   // ---- quantise this lane's 8 values of each row into the wave's tile ----------------------
+  // Straight-line per row: the fast codes are written whatever the check says, and a lane
+  // whose chunk fails it (a near-tie, or a scale that is zero or not normal) only sets the
+  // row's bit for the exact loop below, which overwrites them.  (Branching on the check per
+  // row cost ~35 scalar instructions and 8 branches per row.)  Rows past `rows` (the last
+  // tile) are quantised from their clamped copies into tile rows the MFMA never reads, and
+  // never marked.  The tile offset of chunk c of row r is r KW + ((c ^ (r % g)) << 4):
+  // the XOR with a per-row constant applies to this lane's fixed chunk offset.
   const bool export_q = p.xq_out != nullptr && slice == 0;
+  const int chunks = KW >> 4;
+  const int gmask = min(16, chunks & -chunks) - 1;
+  const int lane_off = ((lane >> 1) << 4) + (lane & 1) * 8;
   uint32_t bad = 0;  // rows whose chunk needs the exact path (bit r)
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -223,19 +233,15 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
 #pragma unroll
       for (int idx = r * kWLoads / R; idx < (r + 1) * kWLoads / R; ++idx) load_w(idx);
     }
-    if (r < rows) {  // uniform
-      const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_l), r));
-      const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_l), r));
-      if (xlane) {
-        bool ok;
-        const uint2 q = quant8_bf16_fast(xr[r], inv, &ok);
-        if (ok && quant_scale_normal(s)) {
-          *reinterpret_cast<uint2*>(tile + fswz(r, lane >> 1, KW) + (lane & 1) * 8) = q;
-          if (export_q) *reinterpret_cast<uint2*>(p.xq_out + (int64_t)(row0 + r) * K + kbase + lane * 8) = q;
-        } else {
-          bad |= 1u << r;
-        }
-      }
+    const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_l), r));
+    const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_l), r));
+    bool ok;
+    const uint2 q = quant8_bf16_fast(xr[r], inv, &ok);
+    const bool live = r < rows;  // uniform
+    if (!(ok && quant_scale_normal(s)) && live && xlane) bad |= 1u << r;
+    if (xlane) {
+      *reinterpret_cast<uint2*>(tile + r * KW + (lane_off ^ ((r & gmask) << 4))) = q;
+      if (export_q && live) *reinterpret_cast<uint2*>(p.xq_out + (int64_t)(row0 + r) * K + kbase + lane * 8) = q;
     }
   }
   // the exact path, one affected row per iteration (each lane re-reads its chunk from L2)
