@@ -244,12 +244,17 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
       if (export_q && live) *reinterpret_cast<uint2*>(p.xq_out + (int64_t)(row0 + r) * K + kbase + lane * 8) = q;
     }
   }
-  // the exact path, one affected row per iteration (each lane re-reads its chunk from L2)
+  // the exact path, one affected row per iteration; each lane picks its row's 8 values out
+  // of its registers (re-reading them from L2 cost a memory round trip per iteration, and
+  // about a third of the workgroups meet a near-tie somewhere)
   while (__any(bad != 0)) {
     const int r = bad != 0 ? __builtin_ctz(bad) : 0;
     const float s = __shfl(s_l, r, 64);
+    uint4 u = xr[0];
+#pragma unroll
+    for (int rr = 1; rr < R; ++rr)
+      if (r == rr) u = xr[rr];  // a per-lane select
     if (bad != 0) {
-      const uint4 u = *reinterpret_cast<const uint4*>(p.x + (int64_t)(row0 + r) * p.ldx + kbase + lane * 8);
       const uint2 q = quant8_bf16_exact(u, s);
       *reinterpret_cast<uint2*>(tile + fswz(r, lane >> 1, KW) + (lane & 1) * 8) = q;
       if (export_q) *reinterpret_cast<uint2*>(p.xq_out + (int64_t)(row0 + r) * K + kbase + lane * 8) = q;

@@ -63,15 +63,16 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
 // With inv = RN(1/s) and e = v * inv (exact product), |e - v/s| < 2^-17.  One fma gives
 // u = RN(e + P) with P = 1.5 * 2^23: in that binade the unit is 1, so u = P + n with
 // n = e rounded to the nearest integer, and u's low byte is n in two's complement.  A second
-// fma gives d = RN(e - n) (P - u = -n is exact).  When every |d| < 0.5 - 2^-14, RN(v/s),
-// which lies within 2^-16 of e, rounds to the same integer n, which is within [-127, 127],
+// fma gives d = RN(e - n) (P - u = -n is exact).  When every |d| < 0.5 - 2^-15, then
+// |e - n| < 0.5 - 2^-15 + 2^-25 and RN(v/s), which lies within 2^-16 of e, is strictly
+// within 0.5 of n, so it rounds to the same integer n, which is within [-127, 127],
 // so n is quant_i8's code and the clamp is moot.  Returns false for a near-tie (the caller
 // then takes the exact path for these N values; a wave branches once per N values, not per
 // value).  u[i] receives the bit patterns of the biased sums.
 template <int N>
 __device__ __forceinline__ bool quant_fast(const float* v, float inv, uint32_t* u) {
   constexpr float kPlace = 12582912.0f;          // 1.5 * 2^23
-  constexpr float kGuard = 0.49993896484375f;    // 0.5 - 2^-14
+  constexpr float kGuard = 0.499969482421875f;   // 0.5 - 2^-15
   float dmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
