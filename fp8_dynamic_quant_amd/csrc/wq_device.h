@@ -60,7 +60,9 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
 
 // Fast path of quant_i8 for N values at once, without the division, for a normal finite
 // scale s (s = RN(absmax/127), so |v/s| <= 127 (1 + 2^-23) for every value of the row).
-// With inv = RN(1/s) and e = v * inv (exact product), |e - v/s| < 2^-17.  One fma gives
+// With inv = RN(1/s) (or any inv within relative 2^-22.4 of 1/s: the slack below allows
+// 127 |inv s - 1| < 2^-15 - 2^-25 - 127 2^-24) and e = v * inv (exact product),
+// |e - v/s| < 2^-17.  One fma gives
 // u = RN(e + P) with P = 1.5 * 2^23: in that binade the unit is 1, so u = P + n with
 // n = e rounded to the nearest integer, and u's low byte is n in two's complement.  A second
 // fma gives d = RN(e - n) (P - u = -n is exact).  When every |d| < 0.5 - 2^-15, then
