@@ -40,19 +40,29 @@ constexpr int kSlice = kBM * kBK;  // bytes of one operand slice in LDS
 constexpr int kScaleB = 1024;      // FP8: the slice's packed activation-scale words (4 waves x 256 B)
 // LDS ring: STAGES - 1 slices in flight while one is multiplied (bytes per stage: A + B
 // [+ B2] [+ scales]).  Dense tiles use 4 stages (128 KiB); the persistent segment kernels
-// keep 32 KiB of static LDS for their work list, so they use 3 stages, or 2 with the
-// SwiGLU pair of B tiles (48 KiB per stage).
-template <bool FP8, bool DUAL, int STAGES>
+// keep 16 KiB of static LDS for their work list (seg_stages below).
+// MT (INT8 only): 128-row A tiles per workgroup tile (1, or 2 for the 256-row tiles of large
+// experts).
+template <bool FP8, bool DUAL, int STAGES, int MT = 1>
 struct TileRing {
-  static constexpr int kStageB = (DUAL ? 3 : 2) * kSlice + (FP8 ? kScaleB : 0);
+  static constexpr int kOperands = MT + (DUAL ? 2 : 1);  // A slices (MT) + B (+ B2)
+  static constexpr int kStageB = kOperands * kSlice + (FP8 ? kScaleB : 0);
   static constexpr int kStages = STAGES;
-  static constexpr int kDmaPerSlice = (DUAL ? 12 : 8) + (FP8 ? 1 : 0);  // per wave
+  static constexpr int kDmaPerSlice = 4 * kOperands + (FP8 ? 1 : 0);  // per wave
   static constexpr int kBytes = kStages * kStageB;
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+  static_assert(MT == 1 || (MT == 2 && !FP8), "256-row tiles are INT8 only");
 };
 constexpr int kDenseStages = 4;
-template <int EPI>
-constexpr int seg_stages() { return EPI == 2 ? 3 : 4; }
+// segment kernels (at most 144 KiB of ring next to the 16 KiB work list): 128-row tiles
+// 4 stages of 32 KiB (SwiGLU: 3 of 48 KiB); 256-row tiles 3 of 48 KiB (SwiGLU: 2 of 64 KiB)
+template <int EPI, int MT = 1>
+constexpr int seg_stages() { return MT == 1 ? (EPI == 2 ? 3 : 4) : (EPI == 2 ? 2 : 3); }
+static_assert(TileRing<false, true, seg_stages<2, 2>(), 2>::kBytes <= 144 * 1024 &&
+                  TileRing<false, false, seg_stages<1, 2>(), 2>::kBytes <= 144 * 1024 &&
+                  TileRing<false, true, seg_stages<2, 1>(), 1>::kBytes <= 144 * 1024 &&
+                  TileRing<false, false, seg_stages<1, 1>(), 1>::kBytes <= 144 * 1024,
+              "segment rings fit next to the 16 KiB work list");
 constexpr int kGroupM = 8;         // tile rows per group in the L2-friendly tile order
 constexpr int kMaxSegTiles = kSegMaxPairs;  // (expert, row tile) pairs a persistent workgroup lists
 
@@ -64,44 +74,50 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ int tswz_of(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int tswz(int r, int c) { return r * kBK + ((c ^ tswz_of(r)) << 4); }
 
-// DMA one 128-row x 128-byte slice: rows [r0, r0+128) of `src` (row stride ld bytes,
-// clamped to < rows), bytes [k0, k0+128); lands swizzled at `dst`
-// frag_n > 0: src holds INT8 weights in the fragment order of launch_pack_weight_i8 for
-// N = frag_n (the rows here are its columns): chunk c (bytes 16c.. of the slice at k0) of
-// row n sits at ((k0/64 + c/4) N/4 + n/4) 256 + 64 (c%4) + 16 (n%4)
-__device__ __forceinline__ void dma_slice(const int8_t* src, int64_t ld, int r0, int rows, int k0, int8_t* dst,
-                                          int wv, int lane, int frag_n = 0) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int pos = (wv * 4 + i) * 64 + lane;  // 16-byte position in the slice, 0..1023
-    const int r = pos >> 3, pc = pos & 7;
-    const int c = pc ^ tswz_of(r);
-    int gr = r0 + r;
-    gr = gr < rows ? gr : rows - 1;
-    const int64_t off = frag_n > 0 ? ((int64_t)((k0 >> 6) + (c >> 2)) * (frag_n >> 2) + (gr >> 2)) * 256 +
-                                         (c & 3) * 64 + (gr & 3) * 16
-                                   : (int64_t)gr * ld + k0 + c * 16;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + off),
-                                     (lds_ptr_t)(dst + (wv * 4 + i) * 1024), 16, 0, 0);
-  }
-}
+// A slice is 128 rows x 128 bytes (rows of the operand, bytes [k0, k0 + 128)), written to
+// LDS swizzled (tswz) by 16 DMA instructions of 64 lanes x 16 bytes: instruction w * 4 + i
+// (wave w) carries the slice's 16-byte positions (w * 4 + i) * 64 + lane, position q being
+// row q / 8, chunk (q % 8) ^ tswz_of(row), and lands at byte (w * 4 + i) * 1024.
+// INT8 weights in fragment order (launch_pack_weight_i8, for N columns): chunk c (bytes
+// 16c .. of the slice at k0) of column n sits at ((k0/64 + c/4) N/4 + n/4) 256 + 64 (c%4) + 16 (n%4).
 
-template <bool FP8>
-using acc_t = typename std::conditional<FP8, v16f, v16i>::type;
-
-// One 128 x 128 tile (two B tiles when DUAL): acc[i][j] (and acc2) over all K.
-// a: rows [m0, row_hi) clamped; b: columns [n0, ..) of w (row stride K), b2 at n0 + dual_off.
-template <bool FP8, bool DUAL, int STAGES>
+// One INT8 tile of 128 MT rows x 128 columns (two B tiles when DUAL): acc[i][j] (and acc2)
+// over all K.  a: rows [m0, row_hi) clamped; b: columns [n0, ..) of w (row stride K), b2 at
+// n0 + dual_off.  Four waves in a 2 x 2 grid; wave (wm, wn) holds the 32-row blocks
+// 2 i + wm (i < 2 MT) of the tile, so that a partly filled tile spreads its rows over both
+// wave rows, and columns wn * 64 .. + 63: (2 MT) x 2 MFMA tiles of 32 x 32.  The MT A
+// slices sit back to back in the stage, so A row r of the tile (0 .. 128 MT - 1) is at
+// tswz(r, c) of the stage's first slice.
+//
+// Schedule, per slice kt (the FP8 tiles below follow the same plan):
+//  * the slice's D DMA instructions per wave (for slice kt + STAGES - 1, into the stage of
+//    slice kt - 1) are issued one at a time between the MFMAs of its first three K steps,
+//    not in one burst: a burst held each wave at the address unit, MFMA pipe idle, for
+//    about as long as the slice's MFMAs take;
+//  * the LDS fragments of each K step are read one step ahead, into a second register set;
+//    after the first MFMA of the last K step come the wait and the barrier that make slice
+//    kt + 1 visible, and its first step's fragments are read there;
+//  * the body is straight-line code: past the last slice, the DMA copies the last slice
+//    into the stage no later slice uses, so every wait counts the same STAGES - 2 later
+//    slices.  The next tile's opening __syncthreads() waits for those copies.
+// With two stages only one slice is in flight, and its DMA goes out in the slice's first
+// K step, to leave the others for the latency.
+template <bool DUAL, int STAGES, int MT>
 __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, const int8_t* A, int m0, int row_hi,
-                                              const int8_t* B, int n0, int dual_off, int g, acc_t<FP8> (&acc)[2][2],
-                                              acc_t<FP8> (&acc2)[2][2]) {
-  using Ring = TileRing<FP8, DUAL, STAGES>;
+                                              const int8_t* B, int n0, int dual_off, v16i (&acc)[2 * MT][2],
+                                              v16i (&acc2)[2 * MT][2]) {
+  using Ring = TileRing<false, DUAL, STAGES, MT>;
+  constexpr int S = Ring::kStages, D = Ring::kDmaPerSlice;
+  constexpr int NB = DUAL ? 2 : 1;
+  constexpr int Q = 2 * MT * 2 * NB;          // MFMAs per K step
+  constexpr int kWin = S == 2 ? Q : 3 * Q;    // MFMA slots that carry the slice's DMA
+  static_assert(D <= kWin, "one DMA instruction per MFMA at most");
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int wm = wv >> 1, wn = wv & 1;
   const int K = p.K, N = p.N;
   const int KT = K / kBK;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2 * MT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -109,199 +125,187 @@ __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, c
         acc[i][j][e] = 0;
         acc2[i][j][e] = 0;
       }
-  // MX (FP8 only): one activation word per 128-deep block holds its four 32-element scales,
-  // and the weights have one such word per (column, block)
-  const bool mx = FP8 && p.mx != 0;
-  const int PH = mx ? KT : (KT + 3) >> 2;
-  const int32_t* xs_g = FP8 ? p.a_scale_packed + (int64_t)g * PH * p.a_scale_tokens : nullptr;
-  const float* ws_g = FP8 && !mx ? p.w_scale + ((int64_t)g * (N / 128) + (n0 >> 7)) * KT : nullptr;
-  const uint32_t* wsw_g = mx ? reinterpret_cast<const uint32_t*>(p.w_scale) + (int64_t)g * N * KT : nullptr;
 
-  // issue slice kt into its ring stage: A, B (, B2) and, for FP8, the 128 rows' packed
-  // scale words (wave w: rows m0 + 32w .. +31, one 4-byte word per lane 0..31) and the
-  // slice's weight block scale (lane 32; lanes 33..63 repeat row words into the unused
-  // rest of the wave's 256 bytes).  Staging the scales with the operands keeps every load
-  // of the loop an LDS DMA, so the ring's vmcnt waits count exactly these.
-  auto issue = [&](int kt) {
-    int8_t* st = smem + (kt % Ring::kStages) * Ring::kStageB;
-    dma_slice(A, p.lda, m0, row_hi, kt * kBK, st, wv, lane);
-    const int frag_n = (!FP8 && p.b_frag) ? N : 0;
-    dma_slice(B, K, n0, N, kt * kBK, st + kSlice, wv, lane, frag_n);
-    if constexpr (DUAL) dma_slice(B, K, n0 + dual_off, N, kt * kBK, st + 2 * kSlice, wv, lane, frag_n);
-    if constexpr (FP8) {
-      // MX: lanes 0..31 the rows' words for block kt, lanes 32..63 the words of columns
-      // n0 + 32w .. n0 + 32w + 31
-      const int r = min(m0 + wv * 32 + (lane & 31), row_hi - 1);
-      const void* src =
-          mx ? (lane < 32 ? reinterpret_cast<const void*>(xs_g + (int64_t)kt * p.a_scale_tokens + r)
-                          : reinterpret_cast<const void*>(wsw_g + (int64_t)min(n0 + wv * 32 + (lane & 31), N - 1) * KT + kt))
-             : lane == 32 ? reinterpret_cast<const void*>(ws_g + kt)
-                          : reinterpret_cast<const void*>(xs_g + (int64_t)(kt >> 2) * p.a_scale_tokens + r);
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(st + (DUAL ? 3 : 2) * kSlice + wv * 256), 4, 0, 0);
+  // Every DMA instruction is a wave-uniform base plus a 32-bit lane offset.  The offsets
+  // (rows clamped to the tile's valid range, chunks swizzled as tswz places them) are fixed
+  // for the tile; the bases step one slice at a time.  Weights in fragment order: column
+  // n0 + g, chunk c of the slice at k0 sits at byte
+  // k0 N + 64 n0 + (c / 4) 64 N + (g / 4) 256 + (c % 4) 64 + (g % 4) 16 (n0 % 4 = 0).
+  // The second B tile's columns (n0 + dual_off + g) never need the clamp: SwiGLU tiles have
+  // n0 + 127 < N / 2 = dual_off.
+  const bool frag = p.b_frag != 0;
+  uint32_t aoff[MT][4], boff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pos = (wv * 4 + i) * 64 + lane;  // 16-byte position in the slice, 0..1023
+    const int r = pos >> 3, c = (pos & 7) ^ tswz_of(r);
+#pragma unroll
+    for (int h = 0; h < MT; ++h) aoff[h][i] = (uint32_t)(min(h * kBM + r, row_hi - 1 - m0) * (int)p.lda + c * 16);
+    const int gr = min(r, N - 1 - n0);
+    boff[i] = frag ? (uint32_t)((c >> 2) * (N >> 2) * 256 + (gr >> 2) * 256 + (c & 3) * 64 + (gr & 3) * 16)
+                   : (uint32_t)(gr * K + c * 16);
+  }
+  const int8_t* a_base = A + (int64_t)m0 * p.lda;
+  const int8_t* b_base = B + (int64_t)n0 * (frag ? 64 : K);
+  const int64_t b_step = frag ? (int64_t)kBK * N : kBK;
+  const int64_t b2_shift = (int64_t)dual_off * (frag ? 64 : K);
+
+  // DMA instruction d of slice kt into ring slot `slot`: A (slice h = d / 4) for d < 4 MT,
+  // then B, then B2
+  auto issue_one = [&](int kt, int d, int slot) {
+    int8_t* st = smem + (slot % S) * Ring::kStageB + wv * 4096;
+    const int8_t* bk = b_base + kt * b_step;
+    const int8_t* src;
+    int8_t* dst;
+    if (d < 4 * MT) {
+      src = a_base + kt * kBK + aoff[d >> 2][d & 3];
+      dst = st + (d >> 2) * kSlice + (d & 3) * 1024;
+    } else if (d < 4 * MT + 4) {
+      src = bk + boff[d - 4 * MT];
+      dst = st + MT * kSlice + (d - 4 * MT) * 1024;
+    } else {
+      src = bk + b2_shift + boff[d - 4 * MT - 4];
+      dst = st + (MT + 1) * kSlice + (d - 4 * MT - 4) * 1024;
+    }
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (lds_ptr_t)dst, 16, 0, 0);
+  };
+
+  const int ar = wm * 32 + (lane & 31), br = wn * 64 + (lane & 31);
+  const int kh = lane >> 5;  // which half of the K step this lane carries: chunk 2 ks + kh
+  struct Frags {
+    v4i a[2 * MT], b[2], b2[2];
+  };
+  auto read_step = [&](int slot, int ks, Frags& f) {
+    const int8_t* sa = smem + (slot % S) * Ring::kStageB;
+    const int8_t* sb = sa + MT * kSlice;
+#pragma unroll
+    for (int i = 0; i < 2 * MT; ++i) f.a[i] = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 64, 2 * ks + kh));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f.b[j] = *reinterpret_cast<const v4i*>(sb + tswz(br + j * 32, 2 * ks + kh));
+      if constexpr (DUAL) f.b2[j] = *reinterpret_cast<const v4i*>(sb + kSlice + tswz(br + j * 32, 2 * ks + kh));
+    }
+  };
+  auto wait_slice = [&]() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D * (S - 2)) : "memory"); };
+
+  // K step ks of slice kt on `cur`; `nxt` receives the following step's fragments
+  auto step = [&](int kt, int ks, const Frags& cur, Frags& nxt) {
+    const int nk = min(kt + S - 1, KT - 1);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int i = q / (2 * NB), j = (q / NB) & 1;
+      if (NB == 1 || (q & 1) == 0)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0);
+      else
+        acc2[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[i], cur.b2[j], acc2[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q == 0) {
+        if (ks < 3) {
+          read_step(kt, ks + 1, nxt);
+        } else {
+          wait_slice();
+          lds_barrier();  // slice kt + 1 is in LDS for everyone; every wave has read slice kt
+          read_step(kt + 1, 0, nxt);
+        }
+      }
+      const int g = ks * Q + q;  // MFMA slot in the slice
+#pragma unroll
+      for (int d = 0; d < D; ++d)
+        if (((2 * d + 1) * kWin) / (2 * D) == g) issue_one(nk, d, kt + S - 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  __syncthreads();  // the previous tile's LDS reads are done before the new DMA lands
-  for (int kt = 0; kt < Ring::kStages - 1 && kt < KT; ++kt) issue(kt);
-
+  __syncthreads();  // the previous tile's LDS reads (and its copies past the end) are done
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue_one(min(s, KT - 1), d, s);
+  wait_slice();  // slice 0 has landed once only slices 1 .. S-2 may be outstanding
+  lds_barrier();
+  Frags f0, f1;
+  read_step(0, 0, f0);
   for (int kt = 0; kt < KT; ++kt) {
-    // this wave's DMA of slice kt has landed once at most the later issued slices'
-    // instructions are outstanding (loads complete in order)
-    const int later = min(Ring::kStages - 2, KT - 1 - kt);
-    if (later >= 2) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * Ring::kDmaPerSlice) : "memory");
-    } else if (later == 1) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Ring::kDmaPerSlice) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    lds_barrier();  // slice kt is in LDS for everyone; the stage of slice kt-1 is free
-    if (kt + Ring::kStages - 1 < KT) issue(kt + Ring::kStages - 1);
-    int8_t* sa = smem + (kt % Ring::kStages) * Ring::kStageB;
-    int8_t* sb = sa + kSlice;
-    int8_t* sb2 = sa + 2 * kSlice;
-    const int ar = wm * 64 + (lane & 31), br = wn * 64 + (lane & 31);
-    const int kh = lane >> 5;  // which half of the K step this lane carries
-    if constexpr (FP8) {
-      const int32_t* scw = reinterpret_cast<const int32_t*>(sa + 2 * kSlice);
-      int rw[2], cw[2];  // the rows' and (MX) the columns' scale words of this slice
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = ar + i * 32;  // row in the tile; its word sits at (r / 32) * 64 + r % 32
-        rw[i] = scw[(r >> 5) * 64 + (r & 31)];
-        const int c = br + i * 32;  // column in the tile (MX): at (c / 32) * 64 + 32 + c % 32
-        cw[i] = mx ? scw[(c >> 5) * 64 + 32 + (c & 31)] : 0;
-      }
-      const int scb128 = (scw[32] >> 23) & 0xFF;  // exponent field of the f32 power-of-two block scale
-      // two K=64 MFMAs per slice.  Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4: lane
-      // group h (lanes 32h .. 32h+31) holds K bytes 16h .. 16h+15 of the step in its first
-      // four registers and 32+16h .. 32+16h+15 in the last four, and the scale operand of
-      // lane group h applies to K bytes 32h .. 32h+31 of the step.  With one scale per
-      // 128-deep block any K order shared by both operands gives the same sum, so the
-      // 128-block path keeps its contiguous 32 bytes per lane.
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int c0 = mx ? 4 * ks + kh : 4 * ks + 2 * kh, c1 = mx ? 4 * ks + 2 + kh : 4 * ks + 2 * kh + 1;
-        v8i af[2], bf[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const v4i lo = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 32, c0));
-          const v4i hi = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 32, c1));
-          af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const v4i blo = *reinterpret_cast<const v4i*>(sb + tswz(br + i * 32, c0));
-          const v4i bhi = *reinterpret_cast<const v4i*>(sb + tswz(br + i * 32, c1));
-          bf[i] = v8i{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
-        }
-        const int sub = 2 * ks + kh;  // MX: this lane group's 32-element block of the slice
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int sca = mx ? (rw[i] >> (8 * sub)) & 0xFF : (rw[i] >> (8 * (kt & 3))) & 0xFF;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int scb = mx ? (cw[j] >> (8 * sub)) & 0xFF : scb128;
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, sca, 0, scb);
-          }
-        }
-      }
-    } else {
-      // four K=32 MFMAs per slice; a lane carries 16 bytes = chunk 2*ks + kh
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        v4i af[2], bf[2], bf2[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          af[i] = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 32, 2 * ks + kh));
-          bf[i] = *reinterpret_cast<const v4i*>(sb + tswz(br + i * 32, 2 * ks + kh));
-          if constexpr (DUAL) bf2[i] = *reinterpret_cast<const v4i*>(sb2 + tswz(br + i * 32, 2 * ks + kh));
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-            if constexpr (DUAL) acc2[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf2[j], acc2[i][j], 0, 0, 0);
-          }
-      }
-    }
+    step(kt, 0, f0, f1);
+    step(kt, 1, f1, f0);
+    step(kt, 2, f0, f1);
+    step(kt, 3, f1, f0);
   }
 }
 
-// Epilogue.  The lane holds column (lane & 31) and rows 8*(e/4) + 4*(lane>>5) + e%4 of each
-// 32 x 32 MFMA tile.
-template <bool FP8, int EPI>
-__device__ __forceinline__ void tile_epilogue(const TileArgs& p, int m0, int row_hi, int n0, int g,
-                                              const float* wsc, acc_t<FP8> (&acc)[2][2], acc_t<FP8> (&acc2)[2][2]) {
+// INT8 epilogue.  The lane holds column (lane & 31) and rows 8*(e/4) + 4*(lane>>5) + e%4 of
+// each 32 x 32 MFMA tile (row blocks as in tile_mainloop), two MFMA row tiles at a time.
+template <int EPI, int MT>
+__device__ __forceinline__ void tile_epilogue(const TileArgs& p, int m0, int row_hi, int n0, int g, const float* wsc,
+                                              v16i (&acc)[2 * MT][2], v16i (&acc2)[2 * MT][2]) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wm = wv >> 1, wn = wv & 1;
   const int N = p.N;
-  const int mb = m0 + wm * 64 + 4 * (lane >> 5);  // this lane's rows: mb + 32 i + 8 (e / 4) + e % 4
-  // Every scale this lane needs is loaded first, at clamped in-range indices, with no branch
-  // between the loads: a scale loaded next to each store made every store group wait for
-  // the stores before it.
-  float rs[2][16];
-  if constexpr (!FP8) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) rs[i][e] = p.a_scale[min(mb + i * 32 + 8 * (e >> 2) + (e & 3), row_hi - 1)];
-  }
+  const int mb = m0 + wm * 32 + 4 * (lane >> 5);  // this lane's rows: mb + 64 i + 8 (e / 4) + e % 4
   float sw[2] = {1.0f, 1.0f}, sw2[2] = {0.0f, 0.0f};
-  if constexpr (!FP8) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-      if constexpr (EPI == 2) {
-        const int I = N / 2;
-        sw[j] = wsc[min(n, I - 1)];
-        sw2[j] = wsc[min(n, I - 1) + I];
-      } else {
-        sw[j] = wsc[min(n, N - 1)];
-      }
-    }
-    // one wait for all of them, as a real s_waitcnt (vmcnt(0)) that the compiler's wait
-    // accounting sees: without it, the per-row store branches made it wait again before
-    // each scale's use, and so for every store issued before
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int n = n0 + wn * 64 + j * 32 + (lane & 31);
     if constexpr (EPI == 2) {
       const int I = N / 2;
-      if (n >= I) continue;
-      float* H = reinterpret_cast<float*>(p.y);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = mb + i * 32 + 8 * (e >> 2) + (e & 3);
-          if (m < row_hi) {
-            const float s = rs[i][e];
-            const float gv = __fmul_rn(__fmul_rn((float)acc[i][j][e], s), sw[j]);
-            const float uv = __fmul_rn(__fmul_rn((float)acc2[i][j][e], s), sw2[j]);
-            const float sg = __fdiv_rn(gv, __fadd_rn(1.0f, exp_fixed(-gv)));
-            H[(int64_t)m * p.ldy + n] = __fmul_rn(sg, uv);
-          }
-        }
+      sw[j] = wsc[min(n, I - 1)];
+      sw2[j] = wsc[min(n, I - 1) + I];
     } else {
-      if (n >= N) continue;
-      uint16_t* Y = reinterpret_cast<uint16_t*>(p.y) + (p.seg_offsets ? 0 : (int64_t)g * p.y_batch_stride);
+      sw[j] = wsc[min(n, N - 1)];
+    }
+  }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+  for (int hh = 0; hh < MT; ++hh) {
+    // Every scale this half needs is loaded first, at clamped in-range indices, with no
+    // branch between the loads: a scale loaded next to each store made every store group
+    // wait for the stores before it.
+    float rs[2][16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = mb + i * 32 + 8 * (e >> 2) + (e & 3);
-          if (m < row_hi) {
-            uint16_t out;
-            if constexpr (FP8) {
-              out = (uint16_t)f32_to_bf16_rn(acc[i][j][e]);
-            } else {
-              out = (uint16_t)f32_to_bf16_rn(__fmul_rn(__fmul_rn((float)acc[i][j][e], rs[i][e]), sw[j]));
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        rs[ii][e] = p.a_scale[min(mb + (2 * hh + ii) * 64 + 8 * (e >> 2) + (e & 3), row_hi - 1)];
+    // one wait for all of them, as a real s_waitcnt (vmcnt(0)) that the compiler's wait
+    // accounting sees: without it, the per-row store branches made it wait again before
+    // each scale's use, and so for every store issued before
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+      if constexpr (EPI == 2) {
+        const int I = N / 2;
+        if (n >= I) continue;
+        float* H = reinterpret_cast<float*>(p.y);
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int i = 2 * hh + ii;
+            const int m = mb + i * 64 + 8 * (e >> 2) + (e & 3);
+            if (m < row_hi) {
+              const float s = rs[ii][e];
+              const float gv = __fmul_rn(__fmul_rn((float)acc[i][j][e], s), sw[j]);
+              const float uv = __fmul_rn(__fmul_rn((float)acc2[i][j][e], s), sw2[j]);
+              const float sg = __fdiv_rn(gv, __fadd_rn(1.0f, exp_fixed(-gv)));
+              H[(int64_t)m * p.ldy + n] = __fmul_rn(sg, uv);
+            }
+          }
+      } else {
+        if (n >= N) continue;
+        uint16_t* Y = reinterpret_cast<uint16_t*>(p.y) + (p.seg_offsets ? 0 : (int64_t)g * p.y_batch_stride);
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int i = 2 * hh + ii;
+            const int m = mb + i * 64 + 8 * (e >> 2) + (e & 3);
+            if (m < row_hi) {
+              Y[(int64_t)m * p.ldy + n] =
+                  (uint16_t)f32_to_bf16_rn(__fmul_rn(__fmul_rn((float)acc[i][j][e], rs[ii][e]), sw[j]));
               if (p.acc_out) p.acc_out[(int64_t)m * N + n] = acc[i][j][e];
             }
-            Y[(int64_t)m * p.ldy + n] = out;
           }
-        }
+      }
     }
   }
 }
@@ -324,7 +328,7 @@ __device__ __forceinline__ void tile_epilogue(const TileArgs& p, int m0, int row
 // The DMA issued during slice kt fills the stage of slice kt-1, whose reads every wave
 // finished (and waited for) before the barrier of slice kt-1.
 
-// DMA instruction i (0..3) of a 128-row x 128-byte operand slice (the i-th of dma_slice)
+// DMA instruction i (0..3) of a 128-row x 128-byte operand slice (this wave's i-th, as above)
 __device__ __forceinline__ void dma_slice_one(const int8_t* src, int64_t ld, int r0, int rows, int k0, int8_t* dst,
                                               int wv, int lane, int i) {
   const int pos = (wv * 4 + i) * 64 + lane;
@@ -542,38 +546,44 @@ __global__ __launch_bounds__(256) void k_gemm_tile(TileArgs p, int tiles_m, int 
   const int in = lin - group * kGroupM * tiles_n;
   const int tm = gm0 + in % gsz, tn = in / gsz;
   const int m0 = tm * kBM, n0 = tn * kBN;
-  acc_t<FP8> acc[2][2], acc2[2][2];
   if constexpr (FP8) {
+    v16f acc[2][2];
     if (p.mx)
       fp8_tile_mainloop<kDenseStages, true>(p, smem, A, m0, p.M, B, n0, g, acc);
     else
       fp8_tile_mainloop<kDenseStages, false>(p, smem, A, m0, p.M, B, n0, g, acc);
     fp8_tile_epilogue(p, smem, m0, p.M, n0, g, acc);
   } else {
-    tile_mainloop<FP8, false, kDenseStages>(p, smem, A, m0, p.M, B, n0, 0, g, acc, acc2);
-    tile_epilogue<FP8, 1>(p, m0, p.M, n0, g, p.w_scale + (int64_t)g * p.N, acc, acc2);
+    v16i acc[2][2], acc2[2][2];
+    tile_mainloop<false, kDenseStages, 1>(p, smem, A, m0, p.M, B, n0, 0, acc, acc2);
+    tile_epilogue<1, 1>(p, m0, p.M, n0, g, p.w_scale + (int64_t)g * p.N, acc, acc2);
   }
 }
 
 // Expert segments (INT8), persistent.  EPI 1: bf16 [rows, N]; EPI 2: f32 silu(gate)*up [rows, N/2].
-template <int EPI>
+// An expert's rows go in units of 256.  A unit of more than 128 rows is one tall tile
+// (MT = 2: 256 rows), so that each column tile of the expert's weights is streamed once for
+// it; a unit of at most 128 rows (only an expert's last unit can be one) is a 128-row tile
+// (MT = 1).  One launch per MT takes the units of its kind, so that each keeps its own
+// register allocation.
+template <int EPI, int MT>
 __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-  // one word per (expert, row tile) pair: expert << 16 | tile index within the expert
-  // (16 KiB, so that with three SwiGLU stages of 48 KiB the workgroup holds 160 KiB)
+  // one word per (expert, unit) of this kind: expert << 16 | the unit's first 128-row block
+  // (16 KiB, so that with the largest ring of 144 KiB the workgroup holds 160 KiB)
   __shared__ int pair_list[kMaxSegTiles];
   const int t = threadIdx.x;
-  // list the non-empty (expert, row tile) pairs, in expert order (one wave, scan by shuffles)
+  // list the units, in expert order (one wave, scan by shuffles)
   if (t < 64) {
     int base = 0;
     for (int e0 = 0; e0 < p.batch; e0 += 64) {
       const int e = e0 + t;
-      int cnt = 0;
-      int64_t lo = 0;
+      int cnt = 0, units = 0;
       if (e < p.batch) {
-        lo = p.seg_offsets[e];
-        const int64_t rows = p.seg_offsets[e + 1] - lo;
-        cnt = rows >= p.seg_min_rows ? (int)((rows + kBM - 1) / kBM) : 0;
+        const int64_t rows = p.seg_offsets[e + 1] - p.seg_offsets[e];
+        units = rows > 0 && rows >= p.seg_min_rows ? (int)((rows + 2 * kBM - 1) / (2 * kBM)) : 0;
+        const bool short_tail = units > 0 && rows - (int64_t)(units - 1) * 2 * kBM <= kBM;
+        cnt = MT == 2 ? units - (short_tail ? 1 : 0) : (short_tail ? 1 : 0);
       }
       int incl = cnt;
 #pragma unroll
@@ -582,8 +592,10 @@ __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
         if (t >= o) incl += u;
       }
       const int start = base + incl - cnt;
+      // MT = 2: units 0 .. cnt-1; MT = 1: the last unit
+      const int u0 = MT == 2 ? 0 : units - 1;
       for (int j = 0; j < cnt; ++j)
-        if (start + j < kMaxSegTiles) pair_list[start + j] = (e << 16) | j;
+        if (start + j < kMaxSegTiles) pair_list[start + j] = (e << 16) | (2 * (u0 + j));
       base += __shfl(incl, 63, 64);
     }
     // the count goes through the ring's first word, which no DMA touches before the
@@ -593,41 +605,54 @@ __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
   __syncthreads();
   const int npair = *reinterpret_cast<const int*>(smem);
   const int nn = (EPI == 2) ? (p.N / 2 + kBN - 1) / kBN : tiles_n;
-  const int total = npair * nn;
+  // The items of one (expert, unit) pair (its nn column tiles) share item % 8, and so, with
+  // the grid a multiple of 8 and workgroups dealt to the 8 XCDs in turn, one XCD: its rows
+  // of the activations come into that XCD's L2 once.  Pairs go in groups of 8, one per XCD;
+  // the last group's missing pairs are skipped.
+  const int total = (npair + 7) / 8 * 8 * nn;
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const int pi = item / nn, tn = item - pi * nn;
+    const int rest = item >> 3, grp = rest / nn, tn = rest - grp * nn;
+    const int pi = grp * 8 + (item & 7);
+    if (pi >= npair) continue;
     const int pw = pair_list[pi];
     const int e = pw >> 16;
     const int m0 = (int)p.seg_offsets[e] + (pw & 0xFFFF) * kBM;
     const int row_hi = (int)p.seg_offsets[e + 1];
     const int8_t* B = p.w + (int64_t)e * p.w_batch_stride;
     const float* wsc = p.w_scale + (int64_t)e * p.N;
-    acc_t<false> acc[2][2], acc2[2][2];
     const int n0 = tn * kBN;
-    tile_mainloop<false, EPI == 2, seg_stages<EPI>()>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, 0, acc, acc2);
-    tile_epilogue<false, EPI>(p, m0, row_hi, n0, 0, wsc, acc, acc2);
+    v16i acc[2 * MT][2], acc2[2 * MT][2];
+    tile_mainloop<EPI == 2, seg_stages<EPI, MT>(), MT>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
+    tile_epilogue<EPI, MT>(p, m0, row_hi, n0, 0, wsc, acc, acc2);
   }
 }
 
-bool tile_fits(int K) { return K % kBK == 0; }
+bool tile_fits(int K, int64_t lda) { return K % kBK == 0 && lda < (1 << 23); }
 
 hipError_t launch_gemm_tile(const TileArgs& a, bool fp8, hipStream_t st) {
-  if (!tile_fits(a.K)) return hipErrorInvalidValue;
+  if (!tile_fits(a.K, a.lda)) return hipErrorInvalidValue;
   const int tiles_n = (a.N + kBN - 1) / kBN;
   if (a.seg_offsets) {
     if (fp8) return hipErrorInvalidValue;
     if (a.epilogue == 2 && (a.N % 256) != 0) return hipErrorInvalidValue;
-    const int dual = a.epilogue == 2;
-    const size_t lds = dual ? (size_t)TileRing<false, true, seg_stages<2>()>::kBytes
-                            : (size_t)TileRing<false, false, seg_stages<1>()>::kBytes;
-    auto kfn = dual ? k_gemm_seg<2> : k_gemm_seg<1>;
-    hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kfn), (int)lds);
-    if (e != hipSuccess) return e;
+    const bool dual = a.epilogue == 2;
     int dev = 0, cus = 256;
     (void)hipGetDevice(&dev);
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    hipLaunchKernelGGL(kfn, dim3((unsigned)(2 * cus)), dim3(256), lds, st, a, tiles_n);
-    return hipGetLastError();
+    // the tall units first: they hold the most work per item
+    for (int mt = 2; mt >= 1; --mt) {
+      const size_t lds = dual ? (mt == 2 ? TileRing<false, true, seg_stages<2, 2>(), 2>::kBytes
+                                         : TileRing<false, true, seg_stages<2, 1>(), 1>::kBytes)
+                              : (mt == 2 ? TileRing<false, false, seg_stages<1, 2>(), 2>::kBytes
+                                         : TileRing<false, false, seg_stages<1, 1>(), 1>::kBytes);
+      auto kfn = dual ? (mt == 2 ? k_gemm_seg<2, 2> : k_gemm_seg<2, 1>) : (mt == 2 ? k_gemm_seg<1, 2> : k_gemm_seg<1, 1>);
+      hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kfn), (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kfn, dim3((unsigned)(2 * cus)), dim3(256), lds, st, a, tiles_n);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int nt = tiles_m * tiles_n;

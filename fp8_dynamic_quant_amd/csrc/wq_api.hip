@@ -347,7 +347,7 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
   }
   if (d->seg_offsets != nullptr) {
     // expert segments: persistent 128x128 tiles over the non-empty (expert, row tile) pairs
-    if (!wq::tile_fits((int)K) || d->acc_out) return WQ_ERR_UNSUPPORTED;
+    if (!wq::tile_fits((int)K, d->lda) || d->acc_out) return WQ_ERR_UNSUPPORTED;
     if (d->epilogue == WQ_EPI_SWIGLU_F32 && N % 256 != 0) return WQ_ERR_SHAPE;
     if (d->b_batch_stride < N * K) return WQ_ERR_SHAPE;
     if (d->batch > 4096) return WQ_ERR_SHAPE;
@@ -466,7 +466,7 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
                    c->num_cu);
     return status_of(e);
   }
-  const bool dma_tiles = wq::tile_fits((int)K);
+  const bool dma_tiles = wq::tile_fits((int)K, d->lda);
   hipError_t e = dma_tiles ? wq::launch_gemm_tile(t, false, st) : wq::launch_gemm_i8_tile(t, st);
   if (c->log)
     std::fprintf(stderr, "[wq] quant_matmul int8 %s M=%lld N=%lld K=%lld grid=%lld\n",

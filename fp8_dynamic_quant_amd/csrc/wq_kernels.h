@@ -77,7 +77,7 @@ struct TileArgs {
 hipError_t launch_gemm_i8_tile(const TileArgs& a, hipStream_t st);
 // 128x128 tiles with DMA-fed LDS (k_gemm_tile.hip); K % 128 == 0
 hipError_t launch_gemm_tile(const TileArgs& a, bool fp8, hipStream_t st);
-bool tile_fits(int K);
+bool tile_fits(int K, int64_t lda);  // K % 128 == 0, lda < 2^23 (32-bit DMA lane offsets)
 // (expert, 128-row tile) pairs the segmented kernel can hold
 constexpr int kSegMaxPairs = 4096;
 // Segments: experts with at most this many rows go to the weight-streaming kernel

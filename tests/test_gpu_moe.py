@@ -164,20 +164,26 @@ BOUNDARY_COUNTS = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 129]
 # experts of three to five 128-row tiles between small ones: the tiled kernel's work list
 # names a tile by its index within the expert
 MANY_TILE_COUNTS = [300, 0, 513, 1, 256, 257, 16, 384]
+# both sides of the 128-row mark, where an expert's rows become one 256-row tile, and of
+# the 256- and 384-row marks, where a 128-row tile follows the 256-row ones
+TALL_COUNTS = [127, 128, 129, 130, 17, 160, 192, 255, 0, 256, 257, 260, 383, 384, 385, 640]
 
 
-@pytest.mark.parametrize("counts", [BOUNDARY_COUNTS, MANY_TILE_COUNTS], ids=["boundary", "many_tiles"])
+@pytest.mark.parametrize("counts", [BOUNDARY_COUNTS, MANY_TILE_COUNTS, TALL_COUNTS],
+                         ids=["boundary", "many_tiles", "tall_tiles"])
 @pytest.mark.parametrize("frag", [False, True])
 @pytest.mark.parametrize("epi", ["bf16", "swiglu"])
-def test_segments_across_the_small_expert_boundary(epi, frag, counts):
+def test_segments_across_the_small_expert_boundary(epi, frag, counts, N=512):
     """Expert row counts on both sides of the 16-row split between the weight-streaming
     kernel and the tiled one, and of the tiled kernel's 64- and 128-row marks (0, 1, 15,
-    16, 17, 31, 32, 33, 63, 64, 65, 129 rows), and experts of several 128-row tiles;
+    16, 17, 31, 32, 33, 63, 64, 65, 129 rows); experts of several 128-row tiles; and
+    127 .. 640 rows around the marks where the tiled kernel takes an expert's rows as
+    256-row tiles (more than 128 rows in a unit of 256) or as a last 128-row tile.
     K = 1024 so both kernels take part; every expert's rows against the oracle's dense
     per-expert product.
     frag: the expert weights cast to fragment order (both kernels read that layout)."""
     counts = np.array(counts, np.int64)
-    E, K, N = counts.size, 1024, 512
+    E, K = counts.size, 1024
     M = int(counts.sum())
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
     x = syn.activations((62, M, K), M, K, outlier_frac=0.01, outlier_mul=20.0)
@@ -205,3 +211,10 @@ def test_segments_across_the_small_expert_boundary(epi, frag, counts):
         else:
             ref = moe.silu_mul_f32(acc, s[lo:hi], np.broadcast_to(sw[e], (hi - lo, N)))
             assert_same(f"h[expert {e}, {hi - lo} rows]", host(y[lo:hi]), ref)
+
+
+@pytest.mark.parametrize("frag", [False, True])
+def test_segments_ragged_columns(frag):
+    """bf16 expert segments with N = 400 (the last column tile is 16 columns wide, its
+    weight rows clamped) over 128-row and 256-row tiles."""
+    test_segments_across_the_small_expert_boundary("bf16", frag, [129, 1, 300, 17, 64], N=400)
