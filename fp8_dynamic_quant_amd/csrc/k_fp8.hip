@@ -23,9 +23,14 @@
 
 namespace wq {
 
-// e = ceil(log2(r)) for r = RN_f32(a / 448) >= 0, clamped to >= -127.
+// e = ceil(log2(r)) for r = RN_f32(a / 448) >= 0, clamped to >= -127, for a bf16 value a
+// (an absmax of bf16 elements).  r comes without a division: m = RN(a c) with c = RN(1/448),
+// then r = fma(fma(-448, m, a), c, m), which equals the correctly rounded quotient for every
+// non-negative finite bf16 a (checked exhaustively with exact rationals on the CPU).
 __device__ __forceinline__ int ue8m0_exp(float a) {
-  const float r = __fdiv_rn(a, 448.0f);
+  const float c = 2.23214295692741870880126953125e-3f;  // RN_f32(1/448) = 0x3B124925
+  const float m = __fmul_rn(a, c);
+  const float r = __fmaf_rn(__fmaf_rn(-448.0f, m, a), c, m);
   const uint32_t b = __float_as_uint(r);
   const int ef = (int)(b >> 23) & 0xFF;
   const uint32_t fr = b & 0x7FFFFFu;
@@ -51,27 +56,30 @@ __device__ __forceinline__ float row16_max(float a) {
   return a;
 }
 
-// PPW packs per wave (consecutive packs of one (t, g)); their loads are issued first
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// PPW packs per wave (consecutive packs of one (t, g)); their loads are issued first.  The
+// wave's indices are scalar (TA * G * PH < 2^31, checked by the host) and every access is a
+// scalar row base plus a 32-bit lane offset, so the address arithmetic stays off the vector
+// ALU, which bounds this kernel once the loads are in flight.
 template <int PPW>
-__global__ __launch_bounds__(256) void k_group_quant_fp8(const uint16_t* __restrict__ x, int64_t T, int G,
-                                                         int D, uint8_t* __restrict__ xq,
-                                                         int32_t* __restrict__ xs) {
+__global__ __launch_bounds__(256) void k_group_quant_fp8(const uint16_t* __restrict__ x, int T, int G, int D,
+                                                         uint8_t* __restrict__ xq, int32_t* __restrict__ xs) {
   const int lane = threadIdx.x & 63;
   const int HG = D / 128, PH = (HG + 3) / 4, PW = (PH + PPW - 1) / PPW;
-  const int64_t TA = (T + 3) / 4 * 4;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t total = TA * G * PW;
-  if (wid >= total) return;
-  const int pw = (int)(wid % PW);
-  const int64_t tg = wid / PW;
-  const int g = (int)(tg % G);
-  const int64_t t = tg / G;
+  const int TA = (T + 3) / 4 * 4;
+  const int wid = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  if (wid >= TA * G * PW) return;
+  const int pw = wid % PW, tg = wid / PW;
+  const int g = tg % G, t = tg / G;
   const int q = lane >> 4;  // quarter: hidden group 4p + q
+  const int64_t row = (int64_t)(min(t, T - 1) * G + g) * D;
+  const uint16_t* xr = x + row;
   uint4 u[PPW];
 #pragma unroll
   for (int i = 0; i < PPW; ++i) {  // clamped in-range loads, all before the first use
     const int h = min(4 * (pw * PPW + i) + q, HG - 1);
-    const uint16_t* src = x + (min(t, T - 1) * G + g) * (int64_t)D + (int64_t)h * 128 + (lane & 15) * 8;
+    const uint16_t* src = xr + (uint32_t)(h * 128 + (lane & 15) * 8);
     if constexpr (PPW >= 2) {
       // large grids: streaming loads (the rows are read once; measured 14.7 -> 13.7 us at
       // T = 512, while the small grids measured slower with them)
@@ -81,14 +89,14 @@ __global__ __launch_bounds__(256) void k_group_quant_fp8(const uint16_t* __restr
       u[i] = *reinterpret_cast<const uint4*>(src);
     }
   }
+  uint8_t* qr = xq + row;
 #pragma unroll
   for (int i = 0; i < PPW; ++i) {
     const int p = pw * PPW + i;
     if (p >= PH) break;  // uniform
     const int h = 4 * p + q;
     int byte = 0;
-    if (t < T && h < HG) {
-      const int64_t off = (t * G + g) * (int64_t)D + (int64_t)h * 128 + (lane & 15) * 8;
+    if (t < T && h < HG) {  // whole quarters (DPP rows) take part or not
       float v[8];
       const uint32_t w4[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
 #pragma unroll
@@ -99,12 +107,7 @@ __global__ __launch_bounds__(256) void k_group_quant_fp8(const uint16_t* __restr
       float a = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(v[j]));
-      if constexpr (PPW >= 4) {
-        a = row16_max(a);  // the quarter is one DPP row (exec covers whole rows here)
-      } else {
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-      }
+      a = row16_max(a);
       const int e = ue8m0_exp(a);
       const float sc = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-127, 126]
       uint32_t lo = 0, hi = 0;
@@ -112,15 +115,22 @@ __global__ __launch_bounds__(256) void k_group_quant_fp8(const uint16_t* __restr
       lo = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[2], sc), __fmul_rn(v[3], sc), lo, true);
       hi = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[4], sc), __fmul_rn(v[5], sc), hi, false);
       hi = __builtin_amdgcn_cvt_pk_fp8_f32(__fmul_rn(v[6], sc), __fmul_rn(v[7], sc), hi, true);
-      *reinterpret_cast<uint2*>(xq + off) = uint2{lo, hi};
+      v2u* dst = reinterpret_cast<v2u*>(qr + (uint32_t)(h * 128 + (lane & 15) * 8));
+      if constexpr (PPW >= 2) {
+        // the codes are written once and read by another kernel: streaming stores
+        __builtin_nontemporal_store(v2u{lo, hi}, dst);
+      } else {
+        *dst = v2u{lo, hi};
+      }
       byte = e + 127;
     }
-    // gather the four quarter bytes into lane 0 (quarters whose h >= HG contribute 0)
-    const int b1 = __shfl(byte, 16, 64), b2 = __shfl(byte, 32, 64), b3 = __shfl(byte, 48, 64);
-    if (lane == 0) {
-      const uint32_t word = (uint32_t)byte | ((uint32_t)b1 << 8) | ((uint32_t)b2 << 16) | ((uint32_t)b3 << 24);
-      xs[((int64_t)g * PH + p) * TA + t] = (int32_t)word;
-    }
+    // the four quarter bytes (0 for hidden groups past HG) form the pack word, read out of
+    // lanes 0, 16, 32, 48 into scalar registers; lane 0 stores it
+    const uint32_t word = (uint32_t)__builtin_amdgcn_readlane(byte, 0) |
+                          ((uint32_t)__builtin_amdgcn_readlane(byte, 16) << 8) |
+                          ((uint32_t)__builtin_amdgcn_readlane(byte, 32) << 16) |
+                          ((uint32_t)__builtin_amdgcn_readlane(byte, 48) << 24);
+    if (lane == 0) xs[(g * PH + p) * TA + t] = (int32_t)word;
   }
 }
 
@@ -212,16 +222,20 @@ hipError_t launch_group_quant_fp8(const uint16_t* x, int64_t T, int G, int D, ui
   // slower on small grids (G = 8, D = 4096, us at T = 64 / 256 / 512: one pack 3.77 / 8.79 /
   // 14.2, two 4.61 / 7.81 / 13.75, four 4.77 / 8.05 / 12.62)
   int ppw = TA * G * PH >= 32768 ? 4 : (TA * G * PH >= 16384 ? 2 : 1);
-  if (ppw_force == 1 || ppw_force == 2 || ppw_force == 4) ppw = ppw_force;
+  if (ppw_force == 1 || ppw_force == 2 || ppw_force == 4 || ppw_force == 8) ppw = ppw_force;
   const int64_t waves = TA * G * ((PH + ppw - 1) / ppw);
   if (waves == 0) return hipSuccess;
+  if (TA * G * PH >= ((int64_t)1 << 31)) return hipErrorInvalidValue;  // 32-bit wave and word indices
   dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-  if (ppw == 4)
-    hipLaunchKernelGGL(k_group_quant_fp8<4>, grid, block, 0, st, x, T, G, D, xq, xs);
+  const int Ti = (int)T;
+  if (ppw == 8)
+    hipLaunchKernelGGL(k_group_quant_fp8<8>, grid, block, 0, st, x, Ti, G, D, xq, xs);
+  else if (ppw == 4)
+    hipLaunchKernelGGL(k_group_quant_fp8<4>, grid, block, 0, st, x, Ti, G, D, xq, xs);
   else if (ppw == 2)
-    hipLaunchKernelGGL(k_group_quant_fp8<2>, grid, block, 0, st, x, T, G, D, xq, xs);
+    hipLaunchKernelGGL(k_group_quant_fp8<2>, grid, block, 0, st, x, Ti, G, D, xq, xs);
   else
-    hipLaunchKernelGGL(k_group_quant_fp8<1>, grid, block, 0, st, x, T, G, D, xq, xs);
+    hipLaunchKernelGGL(k_group_quant_fp8<1>, grid, block, 0, st, x, Ti, G, D, xq, xs);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ struct wq_ctx {
   int fused_gemv_max_m;  // largest M the fused GEMV takes instead (WQ_FUSED_GEMV_MAX_M)
   int fused_r;           // one-launch fused kernel: rows per workgroup (WQ_FUSED_R; 0 = automatic)
   int fused_nt;          // one-launch fused kernel: columns per workgroup (WQ_FUSED_NT; 0 = automatic)
-  int gq_ppw;            // FP8 group quant: packs per wave (WQ_GQ_PPW, 1, 2 or 4; 0 = automatic)
+  int gq_ppw;            // FP8 group quant: packs per wave (WQ_GQ_PPW, 1, 2, 4 or 8; 0 = automatic)
 };
 
 namespace {
@@ -177,7 +177,7 @@ void read_env_knobs(wq_ctx* c) {
     c->fused_r = 0;
   const char* gp = std::getenv("WQ_GQ_PPW");
   c->gq_ppw = gp ? std::atoi(gp) : 0;
-  if (c->gq_ppw != 1 && c->gq_ppw != 2 && c->gq_ppw != 4) c->gq_ppw = 0;
+  if (c->gq_ppw != 1 && c->gq_ppw != 2 && c->gq_ppw != 4 && c->gq_ppw != 8) c->gq_ppw = 0;
   const char* fn = std::getenv("WQ_FUSED_NT");
   c->fused_nt = fn ? std::atoi(fn) : 0;
   if (c->fused_nt != 0 && c->fused_nt != 4 && c->fused_nt != 8 && c->fused_nt != 16 && c->fused_nt != 32)
@@ -301,6 +301,8 @@ int wq_group_quant_fp8_ue8m0(wq_ctx* c, const void* x, int64_t T, int64_t G, int
                              int32_t* x_s, void* stream) {
   if (!c) return WQ_ERR_NULL;
   if (T < 0 || G <= 0 || D <= 0 || D % 128 != 0 || G > 65535 || D > (1 << 20)) return WQ_ERR_SHAPE;
+  // the kernel indexes waves and packed words in 32 bits
+  if ((T + 3) / 4 * 4 * G * ((D / 128 + 3) / 4) >= ((int64_t)1 << 31)) return WQ_ERR_SHAPE;
   if (T == 0) return WQ_OK;
   if (!x || !x_q || !x_s) return WQ_ERR_NULL;
   if (!al16(x) || !al16(x_q) || !al16(x_s)) return WQ_ERR_ALIGN;

@@ -146,7 +146,8 @@ int wq_dynamic_quant(wq_ctx* ctx, const void* x, int x_dtype, int64_t M, int64_t
  *   byte e + 127 goes to byte (h % 4) of int32 word (g * PH + h / 4) * TA + t of x_s
  * x_s: int32 storage [G, PH, TA] (16-byte aligned).  Every byte of x_s not written this
  * way - the tail of the last pack and the token-padding words t in [T, TA) - is written
- * as zero.  The logical [T, G, PH] view has element strides (1, PH * TA, TA). */
+ * as zero.  The logical [T, G, PH] view has element strides (1, PH * TA, TA).
+ * TA * G * PH < 2^31 (WQ_ERR_SHAPE otherwise). */
 int wq_group_quant_fp8_ue8m0(wq_ctx* ctx, const void* x, int64_t T, int64_t G, int64_t D,
                              uint8_t* x_q, int32_t* x_s, void* stream);
 
