@@ -674,14 +674,20 @@ def main():
             he = torch.empty((Mt, Ie), dtype=torch.float32, device=dev)
             us = time_events(lambda: wq.wq_quant_matmul(qe, se, w13e, sw13e, seg_offsets=offe, y=he,
                                                         epilogue=wq.WQ_EPI_SWIGLU_F32, b_fragment=True), 5, warm=2)
+            # the same call with the expected-rows hint set to the actual M_e
+            us_h = time_events(lambda: wq.wq_quant_matmul(qe, se, w13e, sw13e, seg_offsets=offe, y=he,
+                                                          epilogue=wq.WQ_EPI_SWIGLU_F32, b_fragment=True,
+                                                          expected_rows=Me), 5, warm=2)
             wb = Ee * 2 * Ie * He
-            me_rows[str(Me)] = {"us": round(us, 1), "us_per_expert": round(us / Ee, 2),
+            me_rows[str(Me)] = {"us": round(us, 1), "us_with_hint": round(us_h, 1), "us_per_expert": round(us / Ee, 2),
                                 "weight_GBps": round(wb / us / 1e3, 1), "TOPS": round(2 * Mt * 2 * Ie * He / us / 1e6, 1),
-                                "kernel": "k_seg_decode<2, 8, true>" if Me <= 16 else "k_gemm_seg<2>"}
+                                "kernel": ("k_seg_decode<2, 8, true>" if Me <= 16 else
+                                           "k_gemm_seg<2, 1> (128-row tiles)" if Me <= 128 else
+                                           "k_gemm_seg<2, 2> (256-row tiles)" + (", k_gemm_seg<2, 1>" if Me % 256 and Me % 256 <= 128 else ""))}
             del qe, se, he
         rows["moe_expert_rows_sweep"] = {
             "workload": "segmented gate/up GEMM + SwiGLU, 32 experts x W13 int8 [4096 -> 2x2048] (fragment order), "
-                        "M_e rows per expert", "by_M_e": me_rows}
+                        "M_e rows per expert; us_with_hint: expected_rows = M_e", "by_M_e": me_rows}
         del w13e
 
         # ---- prefill GEMM: wq_b-shaped M=8192, K=1024, N=32768 -----------------------------

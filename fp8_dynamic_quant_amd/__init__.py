@@ -51,6 +51,7 @@ class MatmulDesc(ctypes.Structure):
         ("y", _c_void_p), ("ldy", _i64), ("y_batch_stride", _i64),
         ("acc_out", _c_void_p),
         ("b_layout", ctypes.c_int32),
+        ("expected_rows", _i64),
     ]
 
 
@@ -221,7 +222,7 @@ def wq_group_quant_fp8_ue8m0(x: torch.Tensor, x_q: torch.Tensor | None = None, s
 
 def wq_quant_matmul(a, a_scale, b, b_scale, *, y=None, acc_out=None, seg_offsets=None,
                     epilogue=WQ_EPI_BF16, fp8_groups=None, a_scale_tokens=0, b_fragment=False, n=None,
-                    mx=False):
+                    mx=False, expected_rows=0):
     """INT8: a int8 [M, K] (row stride a.stride(0)), a_scale f32 [M], b int8 [N, K] (or
     [E, N, K] with seg_offsets int64 [E+1]), b_scale f32 [N] (or [E, N]) -> y.
     FP8 (fp8_groups=G): a uint8 [M, G, K], a_scale = packed storage [G, PH, TA],
@@ -230,9 +231,12 @@ def wq_quant_matmul(a, a_scale, b, b_scale, *, y=None, acc_out=None, seg_offsets
     wq_group_quant_mxfp8 [G, K/128, TA], b_scale = UE8M0 bytes uint8 [G, N, K/32].
     b_fragment: INT8 weights cast by wq_pack_weight_i8: expert weights [E, N, K] (same shape
     and strides) with seg_offsets, or a dense [N, K] cast (flat N*K bytes; give n = N) at
-    M < 256 (K % 512 == 0, K <= 4096)."""
+    M < 256 (K % 512 == 0, K <= 4096).
+    expected_rows: with seg_offsets, the rows per expert the caller expects (a kernel-choice
+    hint; the same bytes for every value)."""
     d = MatmulDesc()
     d.b_layout = WQ_LAYOUT_FRAGMENT if b_fragment else WQ_LAYOUT_PLAIN
+    d.expected_rows = expected_rows
     dev = a.device
     if fp8_groups is not None:
         G = fp8_groups

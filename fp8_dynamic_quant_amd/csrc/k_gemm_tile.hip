@@ -581,9 +581,16 @@ __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
       int cnt = 0, units = 0;
       if (e < p.batch) {
         const int64_t rows = p.seg_offsets[e + 1] - p.seg_offsets[e];
-        units = rows > 0 && rows >= p.seg_min_rows ? (int)((rows + 2 * kBM - 1) / (2 * kBM)) : 0;
-        const bool short_tail = units > 0 && rows - (int64_t)(units - 1) * 2 * kBM <= kBM;
-        cnt = MT == 2 ? units - (short_tail ? 1 : 0) : (short_tail ? 1 : 0);
+        const bool take = rows > 0 && rows >= p.seg_min_rows;
+        if (p.seg_tall) {
+          units = take ? (int)((rows + 2 * kBM - 1) / (2 * kBM)) : 0;
+          const bool short_tail = units > 0 && rows - (int64_t)(units - 1) * 2 * kBM <= kBM;
+          cnt = MT == 2 ? units - (short_tail ? 1 : 0) : (short_tail ? 1 : 0);
+        } else {
+          // 128-row tiles only (the MT = 1 launch lists every 128-row block)
+          units = 0;
+          cnt = MT == 1 && take ? (int)((rows + kBM - 1) / kBM) : 0;
+        }
       }
       int incl = cnt;
 #pragma unroll
@@ -592,10 +599,12 @@ __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
         if (t >= o) incl += u;
       }
       const int start = base + incl - cnt;
-      // MT = 2: units 0 .. cnt-1; MT = 1: the last unit
-      const int u0 = MT == 2 ? 0 : units - 1;
+      // 256-row units: MT = 2 takes units 0 .. cnt-1, MT = 1 the last unit; 128-row tiles
+      // only: blocks 0 .. cnt-1
+      const int b0 = !p.seg_tall ? 0 : MT == 2 ? 0 : 2 * (units - 1);
+      const int bstep = p.seg_tall ? 2 : 1;
       for (int j = 0; j < cnt; ++j)
-        if (start + j < kMaxSegTiles) pair_list[start + j] = (e << 16) | (2 * (u0 + j));
+        if (start + j < kMaxSegTiles) pair_list[start + j] = (e << 16) | (b0 + bstep * j);
       base += __shfl(incl, 63, 64);
     }
     // the count goes through the ring's first word, which no DMA touches before the
@@ -640,7 +649,7 @@ hipError_t launch_gemm_tile(const TileArgs& a, bool fp8, hipStream_t st) {
     (void)hipGetDevice(&dev);
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     // the tall units first: they hold the most work per item
-    for (int mt = 2; mt >= 1; --mt) {
+    for (int mt = a.seg_tall ? 2 : 1; mt >= 1; --mt) {
       const size_t lds = dual ? (mt == 2 ? TileRing<false, true, seg_stages<2, 2>(), 2>::kBytes
                                          : TileRing<false, true, seg_stages<2, 1>(), 1>::kBytes)
                               : (mt == 2 ? TileRing<false, false, seg_stages<1, 2>(), 2>::kBytes

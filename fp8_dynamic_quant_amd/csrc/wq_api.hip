@@ -36,6 +36,7 @@ struct wq_ctx {
   // every workgroup quantises the rows of its own row tile (no workgroup waits for another);
   // above the limit the call runs the quant kernel and then the GEMM.
   int seg_small;         // expert segments: small experts on the streaming kernel (WQ_SEG_SMALL=0 turns off)
+  int64_t expected_tokens;  // expert segments: default expected rows per expert (WQ_EXPECTED_TOKENS; 0 = none)
   int fp8_rt;            // FP8 decode: 16-token tiles per workgroup (WQ_FP8_RT, 1..4; 0 = automatic)
   int fp8_cols;          // FP8 decode: output columns per workgroup (WQ_FP8_COLS, 16 or 32; default 32)
   int fused_max_m;       // largest M the one-launch fused kernel takes (WQ_FUSED_MAX_M)
@@ -50,7 +51,7 @@ namespace {
 constexpr size_t kWsQBytes = 64u << 20;      // INT8 payload staged between two launches
 constexpr size_t kWsScaleBytes = 1u << 20;   // its f32 per-row scales
 constexpr size_t kWsBytes = kWsQBytes + kWsScaleBytes;
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 inline bool al16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -168,6 +169,9 @@ void read_env_knobs(wq_ctx* c) {
   if (c->fp8_rt < 0 || c->fp8_rt > 4) c->fp8_rt = 0;
   const char* ss = std::getenv("WQ_SEG_SMALL");
   c->seg_small = ss ? std::atoi(ss) != 0 : 1;
+  const char* et = std::getenv("WQ_EXPECTED_TOKENS");
+  c->expected_tokens = et ? std::atoll(et) : 0;
+  if (c->expected_tokens < 0) c->expected_tokens = 0;
   const char* gm = std::getenv("WQ_FUSED_GEMV_MAX_M");
   c->fused_gemv_max_m = gm ? std::atoi(gm) : 0;
   if (c->fused_gemv_max_m < 0 || c->fused_gemv_max_m > 4) c->fused_gemv_max_m = 0;
@@ -371,9 +375,16 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
     t.batch = (int)d->batch;
     t.b_frag = d->b_layout == WQ_LAYOUT_FRAGMENT ? 1 : 0;
     // experts with few rows stream their weights through the 16-column kernel; the tiled
-    // kernel takes the rest (both read the offsets on the device and skip the other set)
-    const bool small = c->seg_small && wq::seg_decode_fits((int)N, (int)K, d->epilogue, d->batch);
+    // kernel takes the rest (both read the offsets on the device and skip the other set).
+    // The expected-rows hint only chooses which launches run: expecting more than 64 rows
+    // per expert, every expert goes to the tiled kernel (no streaming launch); expecting at
+    // most 128, the tiled kernel takes 128-row tiles only (no 256-row launch).  Either way
+    // every expert's rows are computed, with the same bytes.
+    const int64_t hint = d->expected_rows > 0 ? d->expected_rows : c->expected_tokens;
+    const bool small = c->seg_small && wq::seg_decode_fits((int)N, (int)K, d->epilogue, d->batch) &&
+                       !(hint > 4 * wq::kSegSmallRows);
     t.seg_min_rows = small ? wq::kSegSmallRows + 1 : 0;
+    t.seg_tall = hint > 0 && hint <= 128 ? 0 : 1;
     if (small) {
       hipError_t e = wq::launch_seg_decode(t, c->num_cu, st);
       if (e != hipSuccess) return status_of(e);
@@ -381,8 +392,9 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
     hipError_t e = wq::launch_gemm_tile(t, false, st);
     if (c->log)
       std::fprintf(stderr, "[wq] quant_matmul int8 segments E=%lld rows=%lld N=%lld K=%lld epilogue=%s persistent grid=%d "
-                   "small-expert kernel=%s\n", (long long)d->batch, (long long)M, (long long)N, (long long)K,
-                   d->epilogue == WQ_EPI_SWIGLU_F32 ? "swiglu-f32" : "bf16", 2 * c->num_cu, small ? "yes" : "no");
+                   "small-expert kernel=%s 256-row tiles=%s expected rows=%lld\n", (long long)d->batch, (long long)M,
+                   (long long)N, (long long)K, d->epilogue == WQ_EPI_SWIGLU_F32 ? "swiglu-f32" : "bf16", 2 * c->num_cu,
+                   small ? "yes" : "no", t.seg_tall ? "yes" : "no", (long long)hint);
     return status_of(e);
   }
   if (d->epilogue != WQ_EPI_BF16) return WQ_ERR_UNSUPPORTED;

@@ -73,6 +73,7 @@ struct TileArgs {
   int seg_min_rows;            // segments: experts with fewer rows are left to another kernel
   int b_frag;                  // INT8 segments: each expert's w in the fragment order of launch_pack_weight_i8
   int mx;                      // FP8: MX-like 32-element blocks (storage [G, K/128, TA]; w_scale bytes [G][N][K/32])
+  int seg_tall;                // INT8 segments: 256-row tiles for experts' units of 129..256 rows (else 128-row tiles only)
 };
 hipError_t launch_gemm_i8_tile(const TileArgs& a, hipStream_t st);
 // 128x128 tiles with DMA-fed LDS (k_gemm_tile.hip); K % 128 == 0

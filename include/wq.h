@@ -60,7 +60,7 @@ enum { WQ_LAYOUT_PLAIN = 0, WQ_LAYOUT_FRAGMENT = 1 };
 /* Human-readable text for a status code (static storage). */
 const char* wq_status_str(int status);
 
-/* ABI revision of this header. */
+/* ABI revision of this header (3: wq_matmul_desc.expected_rows). */
 int wq_abi_version(void);
 
 /* ---- context ----------------------------------------------------------------------- */
@@ -93,8 +93,10 @@ size_t wq_workspace_bytes(void);
  *                     (1..4; 0 = auto, all of them);
  *   WQ_FP8_COLS=16    grouped FP8 contraction at 16 < T <= 64: keep the 16-column kernel
  *                     instead of the 32-column one (default 32);
- *   WQ_GQ_PPW=p       FP8 group quant: packs of four hidden groups per wave (1, 2 or 4;
- *                     0 = auto by grid size).
+ *   WQ_GQ_PPW=p       FP8 group quant: packs of four hidden groups per wave (1, 2, 4 or
+ *                     8; 0 = auto by grid size);
+ *   WQ_EXPECTED_TOKENS=n  expert segments: the expected rows per expert when a call's
+ *                     descriptor gives none (wq_matmul_desc.expected_rows; 0 = no hint).
  * Values out of range fall back to the default.  Every setting gives bit-identical
  * results except WQ_FP8_COLS, which changes the order of the FP8 contraction's f32 sums
  * (4 or 8 partial sums per output; both within the contraction's stated tolerance).  The
@@ -217,6 +219,13 @@ typedef struct {
                               K % 512 == 0, K <= 4096 and WQ_EPI_BF16; other combinations
                               give WQ_ERR_UNSUPPORTED.  Outputs are the same bytes as with
                               the plain layout.                                             */
+  int64_t expected_rows;   /* segments: the rows per expert the caller expects (the
+                              expected-tokens hint of section 五 of the W8A8 article, which
+                              picks the grouped GEMM's tiling from it); 0 = no hint, and the
+                              context's WQ_EXPECTED_TOKENS applies.  It selects kernels only:
+                              above 64 no expert goes to the 16-row streaming kernel; at
+                              most 128, no 256-row tiles (one launch fewer).  Every value
+                              gives the same bytes; row counts may differ from it freely.   */
 } wq_matmul_desc;
 
 int wq_quant_matmul(wq_ctx* ctx, const wq_matmul_desc* desc, void* stream);

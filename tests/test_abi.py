@@ -44,7 +44,7 @@ def test_host_only_calls():
     from fp8_dynamic_quant_amd import lib, EXPORTS
     L = lib()
     assert set(EXPORTS) == set(declared_functions())
-    assert L.wq_abi_version() == 2
+    assert L.wq_abi_version() == 3
     assert L.wq_workspace_bytes() >= 1 << 20
     for s in range(0, 7):
         assert len(L.wq_status_str(s)) > 0

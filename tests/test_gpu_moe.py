@@ -213,6 +213,34 @@ def test_segments_across_the_small_expert_boundary(epi, frag, counts, N=512):
             assert_same(f"h[expert {e}, {hi - lo} rows]", host(y[lo:hi]), ref)
 
 
+@pytest.mark.parametrize("counts", [BOUNDARY_COUNTS, MANY_TILE_COUNTS, TALL_COUNTS],
+                         ids=["boundary", "many_tiles", "tall_tiles"])
+@pytest.mark.parametrize("epi", ["bf16", "swiglu"])
+def test_expected_rows_hint_gives_the_same_bytes(epi, counts):
+    """The expected-rows hint (W8A8 article, section 五: the grouped GEMM's tiling chosen
+    from the expected tokens per expert) only chooses launches: no streaming kernel above
+    64 expected rows, no 256-row tiles at most 128.  Every hint, right or wrong for the
+    actual counts, gives the bytes of the call without one (fragment-order weights)."""
+    counts = np.array(counts, np.int64)
+    E, K, N = counts.size, 1024, 512
+    M = int(counts.sum())
+    offsets = dev(np.concatenate([[0], np.cumsum(counts)]).astype(np.int64))
+    x = syn.activations((64, M, K), M, K, outlier_frac=0.01, outlier_mul=20.0)
+    q, s = il.quant_int8_per_token(x)
+    w = np.empty((E, N, K), np.int8)
+    sw = np.empty((E, N), np.float32)
+    for e in range(E):
+        w[e], sw[e] = syn.int8_weights((65, e), N, K)
+    wd = wq.wq_pack_weight_i8(dev(w))
+    kw = {} if epi == "bf16" else {"epilogue": wq.WQ_EPI_SWIGLU_F32}
+    base = host(wq.wq_quant_matmul(dev(q), dev(s), wd, dev(sw), seg_offsets=offsets, b_fragment=True,
+                                   **kw).view(torch.uint8))
+    for hint in (1, 16, 64, 65, 128, 129, 100000):
+        got = host(wq.wq_quant_matmul(dev(q), dev(s), wd, dev(sw), seg_offsets=offsets, b_fragment=True,
+                                      expected_rows=hint, **kw).view(torch.uint8))
+        assert np.array_equal(got, base), f"expected_rows={hint}"
+
+
 @pytest.mark.parametrize("frag", [False, True])
 def test_segments_ragged_columns(frag):
     """bf16 expert segments with N = 400 (the last column tile is 16 columns wide, its
