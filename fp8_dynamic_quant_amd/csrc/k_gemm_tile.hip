@@ -561,51 +561,53 @@ __global__ __launch_bounds__(256) void k_gemm_tile(TileArgs p, int tiles_m, int 
 }
 
 // Expert segments (INT8), persistent.  EPI 1: bf16 [rows, N]; EPI 2: f32 silu(gate)*up [rows, N/2].
-// An expert's rows go in units of 256.  A unit of more than 128 rows is one tall tile
-// (MT = 2: 256 rows), so that each column tile of the expert's weights is streamed once for
-// it; a unit of at most 128 rows (only an expert's last unit can be one) is a 128-row tile
-// (MT = 1).  One launch per MT takes the units of its kind, so that each keeps its own
-// register allocation.
-template <int EPI, int MT>
+// With seg_tall, an expert's rows go in units of 256: a unit of more than 128 rows is one
+// tall tile (256 rows, MT = 2), so that each column tile of the expert's weights is streamed
+// once for it; a unit of at most 128 rows (only an expert's last unit can be one) is a
+// 128-row tile (MT = 1).  Without it every 128-row block is a 128-row tile.  One launch
+// takes both kinds, tall tiles first (a launch of its own left the few tall tiles of a
+// typical routing alone on a few CUs).
+template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) int8_t smem[];
-  // one word per (expert, unit) of this kind: expert << 16 | the unit's first 128-row block
-  // (16 KiB, so that with the largest ring of 144 KiB the workgroup holds 160 KiB)
+  // one word per tile: expert << 16 | first 128-row block << 1 | tall (16 KiB, so that with
+  // the largest ring of 144 KiB the workgroup holds 160 KiB)
   __shared__ int pair_list[kMaxSegTiles];
   const int t = threadIdx.x;
-  // list the units, in expert order (one wave, scan by shuffles)
+  // list the tiles in expert order, the tall ones first (one wave, scan by shuffles)
   if (t < 64) {
     int base = 0;
-    for (int e0 = 0; e0 < p.batch; e0 += 64) {
-      const int e = e0 + t;
-      int cnt = 0, units = 0;
-      if (e < p.batch) {
-        const int64_t rows = p.seg_offsets[e + 1] - p.seg_offsets[e];
-        const bool take = rows > 0 && rows >= p.seg_min_rows;
-        if (p.seg_tall) {
-          units = take ? (int)((rows + 2 * kBM - 1) / (2 * kBM)) : 0;
-          const bool short_tail = units > 0 && rows - (int64_t)(units - 1) * 2 * kBM <= kBM;
-          cnt = MT == 2 ? units - (short_tail ? 1 : 0) : (short_tail ? 1 : 0);
-        } else {
-          // 128-row tiles only (the MT = 1 launch lists every 128-row block)
-          units = 0;
-          cnt = MT == 1 && take ? (int)((rows + kBM - 1) / kBM) : 0;
+    for (int pass = 0; pass < 2; ++pass) {
+      const bool tall_pass = pass == 0;
+      if (tall_pass && !p.seg_tall) continue;
+      for (int e0 = 0; e0 < p.batch; e0 += 64) {
+        const int e = e0 + t;
+        int cnt = 0, b0 = 0, bstep = 1;
+        if (e < p.batch) {
+          const int64_t rows = p.seg_offsets[e + 1] - p.seg_offsets[e];
+          const bool take = rows > 0 && rows >= p.seg_min_rows;
+          if (p.seg_tall) {
+            const int units = take ? (int)((rows + 2 * kBM - 1) / (2 * kBM)) : 0;
+            const bool short_tail = units > 0 && rows - (int64_t)(units - 1) * 2 * kBM <= kBM;
+            // tall pass: units 0 .. cnt-1; short pass: the last unit
+            cnt = tall_pass ? units - (short_tail ? 1 : 0) : (short_tail ? 1 : 0);
+            b0 = tall_pass ? 0 : 2 * (units - 1);
+            bstep = 2;
+          } else {
+            cnt = take ? (int)((rows + kBM - 1) / kBM) : 0;
+          }
         }
-      }
-      int incl = cnt;
+        int incl = cnt;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(incl, o, 64);
-        if (t >= o) incl += u;
+        for (int o = 1; o < 64; o <<= 1) {
+          const int u = __shfl_up(incl, o, 64);
+          if (t >= o) incl += u;
+        }
+        const int start = base + incl - cnt;
+        for (int j = 0; j < cnt; ++j)
+          if (start + j < kMaxSegTiles) pair_list[start + j] = (e << 16) | ((b0 + bstep * j) << 1) | (tall_pass ? 1 : 0);
+        base += __shfl(incl, 63, 64);
       }
-      const int start = base + incl - cnt;
-      // 256-row units: MT = 2 takes units 0 .. cnt-1, MT = 1 the last unit; 128-row tiles
-      // only: blocks 0 .. cnt-1
-      const int b0 = !p.seg_tall ? 0 : MT == 2 ? 0 : 2 * (units - 1);
-      const int bstep = p.seg_tall ? 2 : 1;
-      for (int j = 0; j < cnt; ++j)
-        if (start + j < kMaxSegTiles) pair_list[start + j] = (e << 16) | (b0 + bstep * j);
-      base += __shfl(incl, 63, 64);
     }
     // the count goes through the ring's first word, which no DMA touches before the
     // mainloop's opening barrier
@@ -614,10 +616,10 @@ __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
   __syncthreads();
   const int npair = *reinterpret_cast<const int*>(smem);
   const int nn = (EPI == 2) ? (p.N / 2 + kBN - 1) / kBN : tiles_n;
-  // The items of one (expert, unit) pair (its nn column tiles) share item % 8, and so, with
-  // the grid a multiple of 8 and workgroups dealt to the 8 XCDs in turn, one XCD: its rows
-  // of the activations come into that XCD's L2 once.  Pairs go in groups of 8, one per XCD;
-  // the last group's missing pairs are skipped.
+  // The items of one tile row (its nn column tiles) share item % 8, and so, with the grid a
+  // multiple of 8 and workgroups dealt to the 8 XCDs in turn, one XCD: its rows of the
+  // activations come into that XCD's L2 once.  Tile rows go in groups of 8, one per XCD;
+  // the last group's missing ones are skipped.
   const int total = (npair + 7) / 8 * 8 * nn;
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int rest = item >> 3, grp = rest / nn, tn = rest - grp * nn;
@@ -625,15 +627,28 @@ __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
     if (pi >= npair) continue;
     const int pw = pair_list[pi];
     const int e = pw >> 16;
-    const int m0 = (int)p.seg_offsets[e] + (pw & 0xFFFF) * kBM;
+    const int m0 = (int)p.seg_offsets[e] + ((pw & 0xFFFF) >> 1) * kBM;
     const int row_hi = (int)p.seg_offsets[e + 1];
     const int8_t* B = p.w + (int64_t)e * p.w_batch_stride;
     const float* wsc = p.w_scale + (int64_t)e * p.N;
     const int n0 = tn * kBN;
-    v16i acc[2 * MT][2], acc2[2 * MT][2];
-    tile_mainloop<EPI == 2, seg_stages<EPI, MT>(), MT>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
-    tile_epilogue<EPI, MT>(p, m0, row_hi, n0, 0, wsc, acc, acc2);
+    if (pw & 1) {
+      v16i acc[4][2], acc2[4][2];
+      tile_mainloop<EPI == 2, seg_stages<EPI, 2>(), 2>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
+      tile_epilogue<EPI, 2>(p, m0, row_hi, n0, 0, wsc, acc, acc2);
+    } else {
+      v16i acc[2][2], acc2[2][2];
+      tile_mainloop<EPI == 2, seg_stages<EPI, 1>(), 1>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
+      tile_epilogue<EPI, 1>(p, m0, row_hi, n0, 0, wsc, acc, acc2);
+    }
   }
+}
+
+template <bool DUAL>
+constexpr size_t seg_ring_bytes() {
+  constexpr size_t a = TileRing<false, DUAL, seg_stages<DUAL ? 2 : 1, 1>(), 1>::kBytes;
+  constexpr size_t b = TileRing<false, DUAL, seg_stages<DUAL ? 2 : 1, 2>(), 2>::kBytes;
+  return a > b ? a : b;
 }
 
 bool tile_fits(int K, int64_t lda) { return K % kBK == 0 && lda < (1 << 23); }
@@ -648,20 +663,12 @@ hipError_t launch_gemm_tile(const TileArgs& a, bool fp8, hipStream_t st) {
     int dev = 0, cus = 256;
     (void)hipGetDevice(&dev);
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    // the tall units first: they hold the most work per item
-    for (int mt = a.seg_tall ? 2 : 1; mt >= 1; --mt) {
-      const size_t lds = dual ? (mt == 2 ? TileRing<false, true, seg_stages<2, 2>(), 2>::kBytes
-                                         : TileRing<false, true, seg_stages<2, 1>(), 1>::kBytes)
-                              : (mt == 2 ? TileRing<false, false, seg_stages<1, 2>(), 2>::kBytes
-                                         : TileRing<false, false, seg_stages<1, 1>(), 1>::kBytes);
-      auto kfn = dual ? (mt == 2 ? k_gemm_seg<2, 2> : k_gemm_seg<2, 1>) : (mt == 2 ? k_gemm_seg<1, 2> : k_gemm_seg<1, 1>);
-      hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kfn), (int)lds);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(kfn, dim3((unsigned)(2 * cus)), dim3(256), lds, st, a, tiles_n);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    const size_t lds = dual ? seg_ring_bytes<true>() : seg_ring_bytes<false>();
+    auto kfn = dual ? k_gemm_seg<2> : k_gemm_seg<1>;
+    hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kfn), (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kfn, dim3((unsigned)(2 * cus)), dim3(256), lds, st, a, tiles_n);
+    return hipGetLastError();
   }
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int nt = tiles_m * tiles_n;
