@@ -1,5 +1,5 @@
 // Fused decode linear in one launch: per-token INT8 quant of the bf16 rows, INT8 GEMM and
-// the bf16 scale epilogue, for M <= 64 rows and K <= 4096.
+// the bf16 scale epilogue, for M < 256 rows and K <= 4096.
 //
 // Operation: "DeepSeek-V4 W8A8 性能分析", section 一 (BF16 X -> per-token dynamic quant ->
 // INT8 GEMM -> BF16 Y, and the fused form that skips the standalone quant launch and the
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(256) void k_pack_weight_i8(const int8_t* __restrict
 }  // namespace
 
 bool fused_decode_fits(int M, int K) {
-  return M >= 1 && M <= 64 && K % (kFW * 64) == 0 && K / kFW <= kFMaxKW;
+  return M >= 1 && M < 256 && K % (kFW * 64) == 0 && K / kFW <= kFMaxKW;
 }
 
 bool given_decode_fits(int M, int K) {

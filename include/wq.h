@@ -81,8 +81,8 @@ size_t wq_workspace_bytes(void);
  *   WQ_DECODE_NT=n    columns per workgroup of the decode GEMM of wq_quant_matmul (4, 8
  *                     or 16; 0 = auto);
  *   WQ_DECODE_MT=t    16-row tiles per workgroup of the decode GEMM (1, 2 or 4; 0 = auto);
- *   WQ_FUSED_MAX_M=m  the largest M wq_fused_quant_matmul runs as one launch (0..64,
- *                     default 64; 0 = always two launches);
+ *   WQ_FUSED_MAX_M=m  the largest M wq_fused_quant_matmul runs as one launch (0..255,
+ *                     default 255; 0 = always two launches);
  *   WQ_FUSED_GEMV_MAX_M=m  up to this M (0..4, default 0) that one launch is the dot4
  *                     GEMV kernel rather than the 8-wave MFMA kernel;
  *   WQ_FUSED_R=r, WQ_FUSED_NT=n  rows (1, 2, 4, 8, 16) and columns (4, 8, 16, 32) per
@@ -234,7 +234,7 @@ int wq_quant_matmul(wq_ctx* ctx, const wq_matmul_desc* desc, void* stream);
  * The whole chain of section 一 of the W8A8 article: per-token quant of the bf16 x [M, K]
  * (row stride ldx), the INT8 GEMM against w [N, K] and the bf16 epilogue.  Outputs are
  * bit-identical to wq_dynamic_quant followed by wq_quant_matmul.  y: bf16 [M, N] row
- * stride ldy.  For M up to the one-launch limit (WQ_FUSED_MAX_M, default 64) one kernel
+ * stride ldy.  For M up to the one-launch limit (WQ_FUSED_MAX_M, default 255) one kernel
  * quantises in registers and never writes the INT8 payload to HBM; above it the call runs
  * the quant and the GEMM as two launches, staging the payload in x_q_out / x_scale_out
  * when given, else in the context workspace (WQ_ERR_WORKSPACE if M*K bytes exceed it).
@@ -287,7 +287,7 @@ int wq_pack_weight_i8(wq_ctx* ctx, const int8_t* w, int64_t N, int64_t K, int64_
 
 /* wq_fused_quant_matmul with the weights in fragment order (wp from wq_pack_weight_i8),
  * same arguments otherwise and bit-identical outputs.  Only the one-launch MFMA path:
- * 1 <= M <= 64 (and M <= WQ_FUSED_MAX_M), K % 512 == 0, K <= 4096, N % 16 == 0; other
+ * 1 <= M <= 255 (and M <= WQ_FUSED_MAX_M), K % 512 == 0, K <= 4096, N % 16 == 0; other
  * sizes give WQ_ERR_SHAPE (M = 0 returns WQ_OK with nothing launched). */
 int wq_fused_quant_matmul_packed(wq_ctx* ctx, const void* x, int64_t M, int64_t K, int64_t ldx,
                                  const int8_t* wp, const float* w_scale, int64_t N, void* y, int64_t ldy,

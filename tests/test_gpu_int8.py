@@ -67,11 +67,11 @@ def test_wq_a_decode_standalone_and_fused(M):
     assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
 
 
-def test_wq_a_m128_two_launch_path():
-    """wq_a at M = 128, above the one-launch limit: the fused call runs the quant kernel and
+def test_wq_a_m256_two_launch_path():
+    """wq_a at M = 256, above the one-launch limit: the fused call runs the quant kernel and
     the GEMM, through the workspace or the exported tuple, with the same bytes."""
-    x, w, sw = syn.wq_a_linear(128)
-    assert wq.wq_fused_path(128, 4096, 1024) == 0
+    x, w, sw = syn.wq_a_linear(256)
+    assert wq.wq_fused_path(256, 4096, 1024) == 0
     y1 = _check_linear(x, w, sw, fused=True)
     y2 = wq.wq_fused_quant_matmul(bf16_dev(x), dev(w), dev(sw))
     torch.cuda.synchronize()
@@ -79,10 +79,12 @@ def test_wq_a_m128_two_launch_path():
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 512, 64), (15, 1024, 128), (16, 2048, 256), (17, 4096, 1040), (31, 4096, 48),
-                                   (48, 1024, 1040), (64, 4096, 1024), (2, 4096, 32768), (9, 512, 4096)])
+                                   (48, 1024, 1040), (64, 4096, 1024), (2, 4096, 32768), (9, 512, 4096),
+                                   (65, 4096, 1024), (128, 4096, 1024), (200, 2048, 272), (255, 512, 48)])
 def test_fused_one_launch_shapes(M, K, N):
-    # the one-launch fused kernel takes K % 512 == 0, K <= 4096, M <= 64: one 16-row group
+    # the one-launch fused kernel takes K % 512 == 0, K <= 4096, M < 256: one 16-row group
     # and several, a partial last group, narrow and wide N, exported x_q / x_scale / acc
+    assert wq.wq_fused_path(M, K, N) == 2
     x = syn.activations((97, M, K), M, K, outlier_frac=0.005, outlier_mul=30.0)
     w, sw = syn.int8_weights((98, N, K), N, K)
     _check_linear(x, w, sw, fused=True)

@@ -100,7 +100,8 @@ def test_packed_wkv_decode(M):
     _check_packed(x, w, sw)
 
 
-@pytest.mark.parametrize("M,K,N", [(3, 512, 528), (33, 1536, 272), (64, 2048, 48), (17, 4096, 1040), (5, 1024, 16)])
+@pytest.mark.parametrize("M,K,N", [(3, 512, 528), (33, 1536, 272), (64, 2048, 48), (17, 4096, 1040), (5, 1024, 16),
+                                   (96, 4096, 1024), (128, 4096, 1024), (255, 512, 48)])
 def test_packed_ragged_shapes(M, K, N):
     x = syn.activations((12, M, K), M, K, outlier_frac=0.01, outlier_mul=40.0)
     w, sw = syn.int8_weights((12, N, K), N, K)
@@ -219,7 +220,7 @@ def test_packed_errors():
     N, K = 64, 512
     w, sw = syn.int8_weights((13, N, K), N, K)
     wp = wq.wq_pack_weight_i8(dev(w))
-    for M, Kx in ((65, 512), (4, 4608), (4, 528)):
+    for M, Kx in ((256, 512), (4, 4608), (4, 528)):
         x = bf16_dev(syn.activations((13, M, Kx), M, Kx))
         with pytest.raises(wq.WqError):
             wq.wq_fused_quant_matmul_packed(x, torch.zeros(N * Kx, dtype=torch.int8, device=DEV), dev(sw), N)
