@@ -102,16 +102,22 @@ __device__ __forceinline__ int tswz(int r, int c) { return r * kBK + ((c ^ tswz_
 //    slices.  The next tile's opening __syncthreads() waits for those copies.
 // With two stages only one slice is in flight, and its DMA goes out in the slice's first
 // K step, to leave the others for the latency.
-template <bool DUAL, int STAGES, int MT>
+// NV (<= 2 MT): the wave's row blocks that hold a valid row, i < NV (the caller counts them):
+// the MFMAs and fragment reads of the others are skipped; their accumulators stay zero and
+// their rows are never stored.  Every wave still issues its whole share of the slices' DMA
+// and meets every barrier, whatever its NV.
+template <bool DUAL, int STAGES, int MT, int NV = 2 * MT>
 __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, const int8_t* A, int m0, int row_hi,
                                               const int8_t* B, int n0, int dual_off, v16i (&acc)[2 * MT][2],
                                               v16i (&acc2)[2 * MT][2]) {
   using Ring = TileRing<false, DUAL, STAGES, MT>;
   constexpr int S = Ring::kStages, D = Ring::kDmaPerSlice;
   constexpr int NB = DUAL ? 2 : 1;
-  constexpr int Q = 2 * MT * 2 * NB;          // MFMAs per K step
-  constexpr int kWin = S == 2 ? Q : 3 * Q;    // MFMA slots that carry the slice's DMA
-  static_assert(D <= kWin, "one DMA instruction per MFMA at most");
+  static_assert(NV >= 1 && NV <= 2 * MT, "valid row blocks");
+  constexpr int Q = NV * 2 * NB;              // MFMAs per K step
+  // MFMA slots that carry the slice's DMA (several instructions share a slot when there are
+  // fewer slots than instructions)
+  constexpr int kWin = S == 2 ? (Q > D ? Q : (2 * Q < D ? 3 * Q : 2 * Q)) : 3 * Q;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int wm = wv >> 1, wn = wv & 1;
   const int K = p.K, N = p.N;
@@ -173,13 +179,13 @@ __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, c
   const int ar = wm * 32 + (lane & 31), br = wn * 64 + (lane & 31);
   const int kh = lane >> 5;  // which half of the K step this lane carries: chunk 2 ks + kh
   struct Frags {
-    v4i a[2 * MT], b[2], b2[2];
+    v4i a[NV], b[2], b2[2];
   };
   auto read_step = [&](int slot, int ks, Frags& f) {
     const int8_t* sa = smem + (slot % S) * Ring::kStageB;
     const int8_t* sb = sa + MT * kSlice;
 #pragma unroll
-    for (int i = 0; i < 2 * MT; ++i) f.a[i] = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 64, 2 * ks + kh));
+    for (int i = 0; i < NV; ++i) f.a[i] = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 64, 2 * ks + kh));
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       f.b[j] = *reinterpret_cast<const v4i*>(sb + tswz(br + j * 32, 2 * ks + kh));
@@ -632,13 +638,28 @@ __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
     const int8_t* B = p.w + (int64_t)e * p.w_batch_stride;
     const float* wsc = p.w_scale + (int64_t)e * p.N;
     const int n0 = tn * kBN;
+    // this wave's row blocks 2 i + wm with a valid row: i < nv (wave-uniform)
+    const int wm = (int)threadIdx.x >> 7;
+    const int nblk = (row_hi - m0 + 31) >> 5;
+    const int nv = __builtin_amdgcn_readfirstlane((nblk - wm + 1) >> 1);
+    constexpr bool DU = EPI == 2;
     if (pw & 1) {
       v16i acc[4][2], acc2[4][2];
-      tile_mainloop<EPI == 2, seg_stages<EPI, 2>(), 2>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
+      constexpr int S2 = seg_stages<EPI, 2>();
+      if (nv <= 2)  // a tall tile holds at least 129 rows: every wave has two blocks or more
+        tile_mainloop<DU, S2, 2, 2>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
+      else if (nv == 3)
+        tile_mainloop<DU, S2, 2, 3>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
+      else
+        tile_mainloop<DU, S2, 2, 4>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
       tile_epilogue<EPI, 2>(p, m0, row_hi, n0, 0, wsc, acc, acc2);
     } else {
       v16i acc[2][2], acc2[2][2];
-      tile_mainloop<EPI == 2, seg_stages<EPI, 1>(), 1>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
+      constexpr int S1 = seg_stages<EPI, 1>();
+      if (nv <= 1)  // (a wave with no valid block multiplies its padding rows)
+        tile_mainloop<DU, S1, 1, 1>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
+      else
+        tile_mainloop<DU, S1, 1, 2>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
       tile_epilogue<EPI, 1>(p, m0, row_hi, n0, 0, wsc, acc, acc2);
     }
   }
