@@ -40,28 +40,37 @@ constexpr int kSlice = kBM * kBK;  // bytes of one operand slice in LDS
 constexpr int kScaleB = 1024;      // FP8: the slice's packed activation-scale words (4 waves x 256 B)
 // LDS ring: STAGES - 1 slices in flight while one is multiplied (bytes per stage: A + B
 // [+ B2] [+ scales]).  Dense tiles use 4 stages (128 KiB); the persistent segment kernels
-// keep 16 KiB of static LDS for their work list (seg_stages below).
+// keep 16 KiB of static LDS for their work list (SegRing below).
 // MT (INT8 only): 128-row A tiles per workgroup tile (1, or 2 for the 256-row tiles of large
 // experts).
-template <bool FP8, bool DUAL, int STAGES, int MT = 1>
+// KB (INT8 only): the slice's depth in bytes, 128 or 64 (a 64-deep slice keeps twice as
+// many slices in flight in the same LDS).
+template <bool FP8, bool DUAL, int STAGES, int MT = 1, int KB = 128>
 struct TileRing {
   static constexpr int kOperands = MT + (DUAL ? 2 : 1);  // A slices (MT) + B (+ B2)
-  static constexpr int kStageB = kOperands * kSlice + (FP8 ? kScaleB : 0);
+  static constexpr int kOpB = kBM * KB;                  // bytes of one 128-row operand slice
+  static constexpr int kStageB = kOperands * kOpB + (FP8 ? kScaleB : 0);
   static constexpr int kStages = STAGES;
-  static constexpr int kDmaPerSlice = 4 * kOperands + (FP8 ? 1 : 0);  // per wave
+  static constexpr int kDmaPerSlice = (KB / 32) * kOperands + (FP8 ? 1 : 0);  // per wave
   static constexpr int kBytes = kStages * kStageB;
-  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+  static_assert(STAGES >= 2 && STAGES <= 6, "ring depth");
+  static_assert(KB == 128 || (KB == 64 && !FP8), "64-deep slices are INT8 only");
   static_assert(MT == 1 || (MT == 2 && !FP8), "256-row tiles are INT8 only");
 };
 constexpr int kDenseStages = 4;
-// segment kernels (at most 144 KiB of ring next to the 16 KiB work list): 128-row tiles
-// 4 stages of 32 KiB (SwiGLU: 3 of 48 KiB); 256-row tiles 3 of 48 KiB (SwiGLU: 2 of 64 KiB)
-template <int EPI, int MT = 1>
-constexpr int seg_stages() { return MT == 1 ? (EPI == 2 ? 3 : 4) : (EPI == 2 ? 2 : 3); }
-static_assert(TileRing<false, true, seg_stages<2, 2>(), 2>::kBytes <= 144 * 1024 &&
-                  TileRing<false, false, seg_stages<1, 2>(), 2>::kBytes <= 144 * 1024 &&
-                  TileRing<false, true, seg_stages<2, 1>(), 1>::kBytes <= 144 * 1024 &&
-                  TileRing<false, false, seg_stages<1, 1>(), 1>::kBytes <= 144 * 1024,
+// Segment kernels (at most 144 KiB of ring next to the 16 KiB work list): slice depth and
+// ring depth per epilogue and tile height.
+template <int EPI, int MT>
+struct SegRing {
+  static constexpr int kKB = (EPI == 2 && MT == 2) ? 64 : 128;
+  // 128-row tiles: 4 stages of 32 KiB (SwiGLU: 3 of 48 KiB; 6 of 24 KiB with 64-deep slices
+  // measured no faster); 256-row tiles: 3 of 48 KiB (SwiGLU: 4 of 32 KiB with 64-deep
+  // slices; 2 of 64 KiB left one slice in flight)
+  static constexpr int kStages = MT == 1 ? (EPI == 2 ? 3 : 4) : (EPI == 2 ? 4 : 3);
+  using Ring = TileRing<false, EPI == 2, kStages, MT, kKB>;
+};
+static_assert(SegRing<2, 2>::Ring::kBytes <= 144 * 1024 && SegRing<1, 2>::Ring::kBytes <= 144 * 1024 &&
+                  SegRing<2, 1>::Ring::kBytes <= 144 * 1024 && SegRing<1, 1>::Ring::kBytes <= 144 * 1024,
               "segment rings fit next to the 16 KiB work list");
 constexpr int kGroupM = 8;         // tile rows per group in the L2-friendly tile order
 constexpr int kMaxSegTiles = kSegMaxPairs;  // (expert, row tile) pairs a persistent workgroup lists
@@ -106,22 +115,34 @@ __device__ __forceinline__ int tswz(int r, int c) { return r * kBK + ((c ^ tswz_
 // the MFMAs and fragment reads of the others are skipped; their accumulators stay zero and
 // their rows are never stored.  Every wave still issues its whole share of the slices' DMA
 // and meets every barrier, whatever its NV.
-template <bool DUAL, int STAGES, int MT, int NV = 2 * MT>
+// KB: slice depth in bytes.  A 128-deep slice keeps operand row r at tswz(r, chunk); in a
+// 64-deep slice rows 2R and 2R + 1 share the 128-byte LDS row R, as its chunks 0..3 and
+// 4..7 (same swizzle, also free of bank conflicts for the fragment reads).
+__device__ __forceinline__ int slice_off(int r, int c, int kb) {
+  return kb == 128 ? tswz(r, c) : tswz(r >> 1, c + ((r & 1) << 2));
+}
+
+template <bool DUAL, int STAGES, int MT, int NV = 2 * MT, int KB = 128>
 __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, const int8_t* A, int m0, int row_hi,
                                               const int8_t* B, int n0, int dual_off, v16i (&acc)[2 * MT][2],
                                               v16i (&acc2)[2 * MT][2]) {
-  using Ring = TileRing<false, DUAL, STAGES, MT>;
-  constexpr int S = Ring::kStages, D = Ring::kDmaPerSlice;
+  using Ring = TileRing<false, DUAL, STAGES, MT, KB>;
+  constexpr int S = Ring::kStages, D = Ring::kDmaPerSlice, OPB = Ring::kOpB;
   constexpr int NB = DUAL ? 2 : 1;
+  constexpr int KS = KB / 32;   // K steps (32 deep) per slice
+  constexpr int DPO = KB / 32;  // DMA instructions per wave per 128-row operand slice
   static_assert(NV >= 1 && NV <= 2 * MT, "valid row blocks");
   constexpr int Q = NV * 2 * NB;              // MFMAs per K step
-  // MFMA slots that carry the slice's DMA (several instructions share a slot when there are
-  // fewer slots than instructions)
-  constexpr int kWin = S == 2 ? (Q > D ? Q : (2 * Q < D ? 3 * Q : 2 * Q)) : 3 * Q;
+  // MFMA slots that carry the slice's DMA: those of the slice's K steps before the last
+  // (several instructions share a slot when there are fewer slots than instructions); with
+  // two stages, as early as the address unit allows, to leave the rest for the latency
+  constexpr int kMaxWin = (KS - 1) * Q;
+  constexpr int kWin = S == 2 ? (Q >= D ? Q : (2 * Q >= D ? 2 * Q : kMaxWin)) : kMaxWin;
+  static_assert(kWin <= kMaxWin, "DMA window");
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int wm = wv >> 1, wn = wv & 1;
   const int K = p.K, N = p.N;
-  const int KT = K / kBK;
+  const int KT = K / KB;
 #pragma unroll
   for (int i = 0; i < 2 * MT; ++i)
 #pragma unroll
@@ -133,18 +154,21 @@ __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, c
       }
 
   // Every DMA instruction is a wave-uniform base plus a 32-bit lane offset.  The offsets
-  // (rows clamped to the tile's valid range, chunks swizzled as tswz places them) are fixed
-  // for the tile; the bases step one slice at a time.  Weights in fragment order: column
-  // n0 + g, chunk c of the slice at k0 sits at byte
+  // (rows clamped to the tile's valid range, chunks swizzled as slice_off places them) are
+  // fixed for the tile; the bases step one slice at a time.  Weights in fragment order:
+  // column n0 + g, chunk c of the 128-deep slice at k0 sits at byte
   // k0 N + 64 n0 + (c / 4) 64 N + (g / 4) 256 + (c % 4) 64 + (g % 4) 16 (n0 % 4 = 0).
   // The second B tile's columns (n0 + dual_off + g) never need the clamp: SwiGLU tiles have
   // n0 + 127 < N / 2 = dual_off.
   const bool frag = p.b_frag != 0;
-  uint32_t aoff[MT][4], boff[4];
+  uint32_t aoff[MT][DPO], boff[DPO];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int pos = (wv * 4 + i) * 64 + lane;  // 16-byte position in the slice, 0..1023
-    const int r = pos >> 3, c = (pos & 7) ^ tswz_of(r);
+  for (int i = 0; i < DPO; ++i) {
+    // 16-byte position in the operand slice; its LDS row, the chunk it holds there, and
+    // the operand row and chunk that is
+    const int pos = (wv * DPO + i) * 64 + lane;
+    const int R = pos >> 3, cp = (pos & 7) ^ tswz_of(R);
+    const int r = KB == 128 ? R : 2 * R + (cp >> 2), c = KB == 128 ? cp : (cp & 3);
 #pragma unroll
     for (int h = 0; h < MT; ++h) aoff[h][i] = (uint32_t)(min(h * kBM + r, row_hi - 1 - m0) * (int)p.lda + c * 16);
     const int gr = min(r, N - 1 - n0);
@@ -153,25 +177,25 @@ __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, c
   }
   const int8_t* a_base = A + (int64_t)m0 * p.lda;
   const int8_t* b_base = B + (int64_t)n0 * (frag ? 64 : K);
-  const int64_t b_step = frag ? (int64_t)kBK * N : kBK;
+  const int64_t b_step = frag ? (int64_t)KB * N : KB;
   const int64_t b2_shift = (int64_t)dual_off * (frag ? 64 : K);
 
-  // DMA instruction d of slice kt into ring slot `slot`: A (slice h = d / 4) for d < 4 MT,
-  // then B, then B2
+  // DMA instruction d of slice kt into ring slot `slot`: A (slice h = d / DPO) for
+  // d < DPO MT, then B, then B2
   auto issue_one = [&](int kt, int d, int slot) {
-    int8_t* st = smem + (slot % S) * Ring::kStageB + wv * 4096;
+    int8_t* st = smem + (slot % S) * Ring::kStageB + wv * (DPO * 1024);
     const int8_t* bk = b_base + kt * b_step;
     const int8_t* src;
     int8_t* dst;
-    if (d < 4 * MT) {
-      src = a_base + kt * kBK + aoff[d >> 2][d & 3];
-      dst = st + (d >> 2) * kSlice + (d & 3) * 1024;
-    } else if (d < 4 * MT + 4) {
-      src = bk + boff[d - 4 * MT];
-      dst = st + MT * kSlice + (d - 4 * MT) * 1024;
+    if (d < DPO * MT) {
+      src = a_base + kt * KB + aoff[d / DPO][d % DPO];
+      dst = st + (d / DPO) * OPB + (d % DPO) * 1024;
+    } else if (d < DPO * (MT + 1)) {
+      src = bk + boff[d - DPO * MT];
+      dst = st + MT * OPB + (d - DPO * MT) * 1024;
     } else {
-      src = bk + b2_shift + boff[d - 4 * MT - 4];
-      dst = st + (MT + 1) * kSlice + (d - 4 * MT - 4) * 1024;
+      src = bk + b2_shift + boff[d - DPO * (MT + 1)];
+      dst = st + (MT + 1) * OPB + (d - DPO * (MT + 1)) * 1024;
     }
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (lds_ptr_t)dst, 16, 0, 0);
   };
@@ -183,13 +207,16 @@ __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, c
   };
   auto read_step = [&](int slot, int ks, Frags& f) {
     const int8_t* sa = smem + (slot % S) * Ring::kStageB;
-    const int8_t* sb = sa + MT * kSlice;
+    const int8_t* sb = sa + MT * OPB;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) f.a[i] = *reinterpret_cast<const v4i*>(sa + tswz(ar + i * 64, 2 * ks + kh));
+    for (int i = 0; i < NV; ++i) {
+      const int r = ar + i * 64;  // tile row; a 256-row tile's second A slice follows the first
+      f.a[i] = *reinterpret_cast<const v4i*>(sa + (r >> 7) * OPB + slice_off(r & 127, 2 * ks + kh, KB));
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      f.b[j] = *reinterpret_cast<const v4i*>(sb + tswz(br + j * 32, 2 * ks + kh));
-      if constexpr (DUAL) f.b2[j] = *reinterpret_cast<const v4i*>(sb + kSlice + tswz(br + j * 32, 2 * ks + kh));
+      f.b[j] = *reinterpret_cast<const v4i*>(sb + slice_off(br + j * 32, 2 * ks + kh, KB));
+      if constexpr (DUAL) f.b2[j] = *reinterpret_cast<const v4i*>(sb + OPB + slice_off(br + j * 32, 2 * ks + kh, KB));
     }
   };
   auto wait_slice = [&]() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D * (S - 2)) : "memory"); };
@@ -206,7 +233,7 @@ __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, c
         acc2[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[i], cur.b2[j], acc2[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (q == 0) {
-        if (ks < 3) {
+        if (ks < KS - 1) {
           read_step(kt, ks + 1, nxt);
         } else {
           wait_slice();
@@ -232,10 +259,11 @@ __device__ __forceinline__ void tile_mainloop(const TileArgs& p, int8_t* smem, c
   Frags f0, f1;
   read_step(0, 0, f0);
   for (int kt = 0; kt < KT; ++kt) {
-    step(kt, 0, f0, f1);
-    step(kt, 1, f1, f0);
-    step(kt, 2, f0, f1);
-    step(kt, 3, f1, f0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ks += 2) {
+      step(kt, ks, f0, f1);
+      step(kt, ks + 1, f1, f0);
+    }
   }
 }
 
@@ -645,21 +673,21 @@ __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
     constexpr bool DU = EPI == 2;
     if (pw & 1) {
       v16i acc[4][2], acc2[4][2];
-      constexpr int S2 = seg_stages<EPI, 2>();
+      constexpr int S2 = SegRing<EPI, 2>::kStages, KB2 = SegRing<EPI, 2>::kKB;
       if (nv <= 2)  // a tall tile holds at least 129 rows: every wave has two blocks or more
-        tile_mainloop<DU, S2, 2, 2>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
+        tile_mainloop<DU, S2, 2, 2, KB2>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
       else if (nv == 3)
-        tile_mainloop<DU, S2, 2, 3>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
+        tile_mainloop<DU, S2, 2, 3, KB2>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
       else
-        tile_mainloop<DU, S2, 2, 4>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
+        tile_mainloop<DU, S2, 2, 4, KB2>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
       tile_epilogue<EPI, 2>(p, m0, row_hi, n0, 0, wsc, acc, acc2);
     } else {
       v16i acc[2][2], acc2[2][2];
-      constexpr int S1 = seg_stages<EPI, 1>();
+      constexpr int S1 = SegRing<EPI, 1>::kStages, KB1 = SegRing<EPI, 1>::kKB;
       if (nv <= 1)  // (a wave with no valid block multiplies its padding rows)
-        tile_mainloop<DU, S1, 1, 1>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
+        tile_mainloop<DU, S1, 1, 1, KB1>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
       else
-        tile_mainloop<DU, S1, 1, 2>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
+        tile_mainloop<DU, S1, 1, 2, KB1>(p, smem, p.a, m0, row_hi, B, n0, p.N / 2, acc, acc2);
       tile_epilogue<EPI, 1>(p, m0, row_hi, n0, 0, wsc, acc, acc2);
     }
   }
@@ -667,8 +695,8 @@ __global__ __launch_bounds__(256) void k_gemm_seg(TileArgs p, int tiles_n) {
 
 template <bool DUAL>
 constexpr size_t seg_ring_bytes() {
-  constexpr size_t a = TileRing<false, DUAL, seg_stages<DUAL ? 2 : 1, 1>(), 1>::kBytes;
-  constexpr size_t b = TileRing<false, DUAL, seg_stages<DUAL ? 2 : 1, 2>(), 2>::kBytes;
+  constexpr size_t a = SegRing<DUAL ? 2 : 1, 1>::Ring::kBytes;
+  constexpr size_t b = SegRing<DUAL ? 2 : 1, 2>::Ring::kBytes;
   return a > b ? a : b;
 }
 
