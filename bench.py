@@ -666,28 +666,43 @@ def main():
                                                   dtype=torch.int8))
         sw13e = torch.rand((Ee, 2 * Ie), generator=gen_e, device=dev) * 9e-3 + 1e-3
         me_rows = {}
-        for Me in (1, 2, 4, 8, 16, 17, 32, 64, 96, 127, 128, 129, 160, 192, 256):
+        me_list = (1, 2, 4, 8, 16, 17, 32, 64, 96, 127, 128, 129, 160, 192, 256)
+        me_cases = {}
+        for Me in me_list:
             Mt = Ee * Me
             qe = torch.randint(-127, 128, (Mt, He), generator=gen_e, device=dev, dtype=torch.int8)
             se = torch.rand((Mt,), generator=gen_e, device=dev) * 0.05 + 0.01
             offe = torch.arange(0, Ee + 1, device=dev, dtype=torch.int64) * Me
             he = torch.empty((Mt, Ie), dtype=torch.float32, device=dev)
-            us = time_events(lambda: wq.wq_quant_matmul(qe, se, w13e, sw13e, seg_offsets=offe, y=he,
-                                                        epilogue=wq.WQ_EPI_SWIGLU_F32, b_fragment=True), 5, warm=2)
-            # the same call with the expected-rows hint set to the actual M_e
-            us_h = time_events(lambda: wq.wq_quant_matmul(qe, se, w13e, sw13e, seg_offsets=offe, y=he,
-                                                          epilogue=wq.WQ_EPI_SWIGLU_F32, b_fragment=True,
-                                                          expected_rows=Me), 5, warm=2)
+            me_cases[Me] = (qe, se, offe, he)
+        # the sizes alternate over 5 rounds of 10 calls each, with and without the hint
+        # expected_rows = M_e; each figure is the median round (the spread between rounds,
+        # from clocks and the memory system, is a few per cent)
+        me_us = {Me: ([], []) for Me in me_list}
+        for _ in range(5):
+            for Me, (qe, se, offe, he) in me_cases.items():
+                for hint, out in ((0, me_us[Me][0]), (Me, me_us[Me][1])):
+                    out.append(time_events(lambda: wq.wq_quant_matmul(qe, se, w13e, sw13e, seg_offsets=offe, y=he,
+                                                                      epilogue=wq.WQ_EPI_SWIGLU_F32, b_fragment=True,
+                                                                      expected_rows=hint), 10, warm=2))
+        for Me in me_list:
+            Mt = Ee * Me
+            us, us_h = float(np.median(me_us[Me][0])), float(np.median(me_us[Me][1]))
             wb = Ee * 2 * Ie * He
             me_rows[str(Me)] = {"us": round(us, 1), "us_with_hint": round(us_h, 1), "us_per_expert": round(us / Ee, 2),
                                 "weight_GBps": round(wb / us / 1e3, 1), "TOPS": round(2 * Mt * 2 * Ie * He / us / 1e6, 1),
                                 "kernel": ("k_seg_decode<2, 8, true>" if Me <= 16 else
-                                           "k_gemm_seg<2, 1> (128-row tiles)" if Me <= 128 else
-                                           "k_gemm_seg<2, 2> (256-row tiles)" + (", k_gemm_seg<2, 1>" if Me % 256 and Me % 256 <= 128 else ""))}
-            del qe, se, he
+                                           "k_gemm_seg<2>, 128-row tiles" if Me <= 128 else
+                                           "k_gemm_seg<2>, 256-row tiles" + (" + 128-row tiles" if Me % 256 and Me % 256 <= 128 else ""))}
+        del me_cases
+        steps = {}
+        for lo_, hi_ in ((16, 17), (128, 129)):
+            for key, name in (("us", ""), ("us_with_hint", "_with_hint")):
+                steps[f"{lo_}_to_{hi_}{name}"] = round(me_rows[str(hi_)][key] / me_rows[str(lo_)][key] - 1, 4)
         rows["moe_expert_rows_sweep"] = {
             "workload": "segmented gate/up GEMM + SwiGLU, 32 experts x W13 int8 [4096 -> 2x2048] (fragment order), "
-                        "M_e rows per expert; us_with_hint: expected_rows = M_e", "by_M_e": me_rows}
+                        "M_e rows per expert; us_with_hint: expected_rows = M_e; medians of 5 alternating rounds",
+            "steps": steps, "by_M_e": me_rows}
         del w13e
 
         # ---- prefill GEMM: wq_b-shaped M=8192, K=1024, N=32768 -----------------------------
