@@ -86,27 +86,6 @@ __device__ __forceinline__ uint2 quant8_bf16_fast(const uint4 u, float inv, bool
   return uint2{pack4_biased(b), pack4_biased(b + 4)};
 }
 
-// RN(a / 127) for a non-negative bf16 value a (absmax of bf16 rows): m = RN(a c) with
-// c = RN(1/127), then one correction step with the exact residual a - 127 m.  Equal to the
-// correctly rounded quotient for every non-negative finite bf16 a (checked exhaustively,
-// with exact arithmetic, in tests/test_scale_division.py); it replaces a division sequence
-// of ~10 dependent instructions on the path to the first quantised row.
-__device__ __forceinline__ float div127_bf16(float a) {
-  constexpr float c = 1.0f / 127.0f;  // RN(1/127)
-  const float m = __fmul_rn(a, c);
-  const float r = __builtin_fmaf(-127.0f, m, a);
-  return __builtin_fmaf(r, c, m);
-}
-
-// 1/s for a normal s with relative error below 2^-24 (1 + 2^-22): v_rcp_f32 (1 ulp) and one
-// Newton step.  The fast quant path needs only that bound (see quant_fast's proof, which
-// allows 2^-22.4); the exact path divides by s itself.
-__device__ __forceinline__ float recip_refined(float s) {
-  const float r0 = __builtin_amdgcn_rcpf(s);
-  const float e = __builtin_fmaf(-s, r0, 1.0f);
-  return __builtin_fmaf(r0, e, r0);
-}
-
 // INT8 codes of 8 bf16 values by the exact quant_i8 (correctly rounded division)
 __device__ __forceinline__ uint2 quant8_bf16_exact(const uint4 u, float s) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};

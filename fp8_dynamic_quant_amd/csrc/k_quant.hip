@@ -79,6 +79,89 @@ __device__ __forceinline__ float rms_inv(double ss, int K, float eps) {
   return __fdiv_rn(1.0f, sqrtf(d));
 }
 
+// The row in registers (CH chunks of 16 bytes per lane, lane l taking chunks l, l + 64, ...):
+// every chunk load (and, with RMSNorm, every gamma chunk) is issued before the first use,
+// and none sits under a branch: lanes past the row re-read its last chunk.  (Loads under a
+// per-lane branch made the compiler wait for each one before issuing the next.)
+template <typename TIn, int CH>
+__device__ __forceinline__ void load_row(const TIn* xr, int C, int lane, uint4 (&raw)[CH]) {
+  constexpr int EPC = In<TIn>::EPC;
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+    raw[i] = *reinterpret_cast<const uint4*>(xr + (uint32_t)(min(lane + 64 * i, C - 1) * EPC));
+}
+
+template <typename TIn, int CH>
+__device__ __forceinline__ void load_gamma_chunks(const uint16_t* gamma, int C, int lane, uint4 (&graw)[CH]) {
+  constexpr int EPC = In<TIn>::EPC;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = min(lane + 64 * i, C - 1);
+    if constexpr (EPC == 8) {
+      graw[i] = *reinterpret_cast<const uint4*>(gamma + (int64_t)c * 8);
+    } else {
+      const uint2 g2 = *reinterpret_cast<const uint2*>(gamma + (int64_t)c * 4);
+      graw[i] = uint4{g2.x, g2.y, 0u, 0u};
+    }
+  }
+}
+
+// Quantise one row held in registers: chunks [c0, c1) of it are stored (a K slice), and the
+// scale goes to *xs_row when xs_row is not null.
+template <typename TIn, int CH, bool RMS>
+__device__ __forceinline__ void quant_row(const uint4 (&raw)[CH], const uint4* graw, int C, int K, float eps,
+                                          int lane, int c0, int c1, int8_t* qr, float* xs_row) {
+  constexpr int EPC = In<TIn>::EPC;
+  float v[CH][EPC];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    In<TIn>::unpack(raw[i], v[i]);
+    if constexpr (RMS) {
+      // lanes past the row hold copies of its last chunk: no part of the sum of squares
+      // (for the absmax alone they are harmless, and they are never stored)
+      const bool in = lane + 64 * i < C;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) v[i][e] = in ? v[i][e] : 0.0f;
+    }
+  }
+  if constexpr (RMS) {
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) ss += (double)v[i][e] * (double)v[i][e];
+    ss = wave_sum_f64(ss);
+    const float inv = rms_inv(ss, K, eps);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const bool in = lane + 64 * i < C;
+      const uint32_t gw[4] = {graw[i].x, graw[i].y, graw[i].z, graw[i].w};
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const float g = (e & 1) ? __uint_as_float(gw[e >> 1] & 0xFFFF0000u) : __uint_as_float(gw[e >> 1] << 16);
+        v[i][e] = in ? __fmul_rn(__fmul_rn(v[i][e], inv), g) : 0.0f;
+      }
+    }
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) a = fmaxf(a, fabsf(v[i][e]));
+  a = wave_max_nonneg(a);
+  // s = RN(a / 127): for bf16 rows without RMSNorm a is a bf16 value and the corrected
+  // product gives the quotient exactly (checked for every bf16 value on the CPU); the fast
+  // quant path needs 1/s only within 2^-22.4 (quant_fast), which rcp and one Newton step give
+  const float s = (sizeof(TIn) == 2 && !RMS) ? div127_bf16(a) : __fdiv_rn(a, 127.0f);
+  const float inv = recip_refined(s);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= c0 && c < c1) store_codes<EPC>(qr + (uint32_t)(c * EPC), v[i], s, inv);
+  }
+  if (xs_row && lane == 0) *xs_row = s;
+}
+
 // CH > 0: the row is cached in registers (CH chunks per lane).  CH == 0: rows longer than
 // the register cache are streamed in three passes (sum of squares, absmax, quantise).
 template <typename TIn, int CH, bool RMS>
@@ -89,80 +172,24 @@ __global__ __launch_bounds__(256) void k_dynamic_quant(const TIn* __restrict__ x
                                                        int S) {
   constexpr int EPC = In<TIn>::EPC;
   const int lane = threadIdx.x & 63;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t row = gw / S;
-  const int j = (int)(gw - row * S);
+  // the wave's row and K slice, in scalar registers (no division when S == 1)
+  const int64_t gw = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int64_t row = S == 1 ? gw : gw / S;
+  const int j = S == 1 ? 0 : (int)(gw - row * S);
   if (row >= M) return;
   const int64_t src = row_index ? (int64_t)row_index[row] : row;
   const TIn* xr = x + src * ldx;
   const int C = K / EPC;
-  const int c0 = (int)((int64_t)C * j / S), c1 = (int)((int64_t)C * (j + 1) / S);
+  const int c0 = S == 1 ? 0 : (int)((int64_t)C * j / S), c1 = S == 1 ? C : (int)((int64_t)C * (j + 1) / S);
   int8_t* qr = xq + row * (int64_t)K;
 
   if constexpr (CH > 0) {
-    // Every chunk load (and, with RMSNorm, every gamma chunk) is issued before the first
-    // wait, and none sits under a branch: lanes past the row re-read its last chunk and
-    // their values are zeroed after the load.  (Loads under a per-lane branch made the
-    // compiler wait for each one before issuing the next.)
     uint4 raw[CH];
-#pragma unroll
-    for (int i = 0; i < CH; ++i)
-      raw[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)min(lane + 64 * i, C - 1) * EPC);
+    load_row<TIn, CH>(xr, C, lane, raw);
     uint4 graw[RMS ? CH : 1];
-    if constexpr (RMS) {
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const int c = min(lane + 64 * i, C - 1);
-        if constexpr (EPC == 8) {
-          graw[i] = *reinterpret_cast<const uint4*>(gamma + (int64_t)c * 8);
-        } else {
-          const uint2 g2 = *reinterpret_cast<const uint2*>(gamma + (int64_t)c * 4);
-          graw[i] = uint4{g2.x, g2.y, 0u, 0u};
-        }
-      }
-    }
+    if constexpr (RMS) load_gamma_chunks<TIn, CH>(gamma, C, lane, graw);
     __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use
-    float v[CH][EPC];
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const bool in = lane + 64 * i < C;
-      In<TIn>::unpack(raw[i], v[i]);
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) v[i][e] = in ? v[i][e] : 0.0f;
-    }
-    if constexpr (RMS) {
-      double ss = 0.0;
-#pragma unroll
-      for (int i = 0; i < CH; ++i)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) ss += (double)v[i][e] * (double)v[i][e];
-      ss = wave_sum_f64(ss);
-      const float inv = rms_inv(ss, K, eps);
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const bool in = lane + 64 * i < C;
-        const uint32_t gw[4] = {graw[i].x, graw[i].y, graw[i].z, graw[i].w};
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const float g = (e & 1) ? __uint_as_float(gw[e >> 1] & 0xFFFF0000u) : __uint_as_float(gw[e >> 1] << 16);
-          v[i][e] = in ? __fmul_rn(__fmul_rn(v[i][e], inv), g) : 0.0f;
-        }
-      }
-    }
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < CH; ++i)
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) a = fmaxf(a, fabsf(v[i][e]));
-    a = wave_max(a);
-    const float s = __fdiv_rn(a, 127.0f);
-    const float inv = __fdiv_rn(1.0f, s);
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = lane + 64 * i;
-      if (c >= c0 && c < c1) store_codes<EPC>(qr + (int64_t)c * EPC, v[i], s, inv);
-    }
-    if (j == 0 && lane == 0) xs[row] = s;
+    quant_row<TIn, CH, RMS>(raw, graw, C, K, eps, lane, c0, c1, qr, j == 0 ? xs + row : nullptr);
   } else {
     float inv = 1.0f;
     if constexpr (RMS) {

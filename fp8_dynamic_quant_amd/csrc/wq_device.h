@@ -39,6 +39,40 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// max over the 64 lanes of a wave of non-negative floats (compared as their bit patterns),
+// returned to every lane: quad swaps, half-row and row mirrors by DPP, then the four rows'
+// maxima through readlane
+__device__ __forceinline__ float wave_max_nonneg(float f) {
+  uint32_t v = __float_as_uint(f);
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row half mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return __uint_as_float(max(a, b));
+}
+
+// RN(a / 127) for a non-negative bf16 value a: m = RN(a c) with c = RN(1/127), then one
+// correction step with the exact residual a - 127 m.  Equal to the correctly rounded
+// quotient for every bf16 a (checked exhaustively with exact rationals on the CPU); the plain
+// product alone misses it for some.
+__device__ __forceinline__ float div127_bf16(float a) {
+  constexpr float c = 1.0f / 127.0f;  // RN(1/127)
+  const float m = __fmul_rn(a, c);
+  const float r = __builtin_fmaf(-127.0f, m, a);
+  return __builtin_fmaf(r, c, m);
+}
+
+// 1/s for a normal s with relative error below 2^-24 (1 + 2^-22): v_rcp_f32 (1 ulp) and one
+// Newton step.  The fast quant path needs only that bound (see quant_fast's proof, which
+// allows 2^-22.4); the exact path divides by s itself.
+__device__ __forceinline__ float recip_refined(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, r0, 1.0f);
+  return __builtin_fmaf(r0, e, r0);
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -283,6 +283,24 @@ def test_quant_strided_rows_and_splits():
         assert np.array_equal(host(q), q_ref) and np.array_equal(host(s), s_ref)
 
 
+@pytest.mark.parametrize("M,K,f32", [(4096, 1024, False), (4097, 16, False), (4099, 528, False), (4103, 1008, False),
+                                     (5000, 512, True), (4098, 272, True)])
+def test_quant_many_short_rows(M, K, f32):
+    """Thousands of short rows (a row per wave, one or two 16-byte chunks per lane, lanes past
+    the row idle), row counts that leave the last workgroup partly empty."""
+    x = syn.activations((97, M, K), M, K, outlier_frac=0.01, outlier_mul=20.0)
+    if f32:
+        xf = nm.bf16_to_f32(x) * np.float32(1.0 + 2.0 ** -9)  # values off the bf16 grid
+        q, s = wq.wq_dynamic_quant(torch.from_numpy(xf).to(DEV))
+        q_ref, s_ref = il.quant_int8_per_token(xf, is_bf16_bits=False)
+    else:
+        q, s = wq.wq_dynamic_quant(bf16_dev(x))
+        q_ref, s_ref = il.quant_int8_per_token(x)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host(q), q_ref)
+
+
 def test_quant_long_rows_streamed():
     M, K = 3, 32768  # beyond the register cache: three streamed passes
     x = syn.activations((95,), M, K, outlier_frac=0.001, outlier_mul=100.0)

@@ -50,7 +50,7 @@ def test_expert_sort_drops_out_of_range_ids():
     assert (host(perm)[kept:] == -1).all() and (host(row_token)[kept:] == 0).all()
 
 
-@pytest.mark.parametrize("T,H", [(16, 512), (8, 4096), (5, 2064)])
+@pytest.mark.parametrize("T,H", [(16, 512), (8, 4096), (5, 2064), (1025, 1024), (1100, 272)])
 def test_rmsnorm_quant_gather(T, H):
     h = syn.activations((60, T, H), T, H)
     gamma = syn.to_bf16_bits(np.random.default_rng(T).uniform(0.5, 1.5, H).astype(np.float32))
