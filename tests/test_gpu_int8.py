@@ -224,6 +224,36 @@ def test_epilogue_is_the_documented_f32_sequence(M, K, N):
         assert np.array_equal(got, want), f"fused={fused}: {(got != want).sum()} outputs differ"
 
 
+@pytest.mark.parametrize("M,K,N", [(1000, 128, 16384), (1024, 256, 16400)])
+def test_large_gemm_tile_orders_sampled_rows(M, K, N):
+    """The M, N >= 256 GEMM in both tile orders: N-range (each XCD walks a range of W's columns,
+    nontemporal output; 1000 x 16384) and row groups (cached output; 1024 x 16400), each with
+    a last tile row or column shifted back to end at M or N, so some rows or columns are
+    computed by two tiles.  Sampled rows (every row the shifted tile shares) against the
+    oracle's accumulators and the documented f32 epilogue, and the production launch against
+    the one that also exports the accumulators."""
+    x = syn.activations((101, M, K), M, K, outlier_frac=0.01, outlier_mul=20.0)
+    w, sw = syn.int8_weights((102, N, K), N, K)
+    xq, xs = wq.wq_dynamic_quant(bf16_dev(x))
+    wd, swd = dev(w), dev(sw)
+    acc = poison((M, N), torch.int32)
+    y_acc = wq.wq_quant_matmul(xq, xs, wd, swd, acc_out=acc)
+    y = wq.wq_quant_matmul(xq, xs, wd, swd)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_acc.view(torch.int16))
+    last = (M - 1) // 256 * 256  # the last tile row's nominal origin; the shifted one is M - 256
+    rows = np.unique(np.concatenate([[0, 1, 255, 256], np.arange(M - 256 - 2, M - 256 + 3), np.arange(last - 3, last + 3),
+                                     np.random.default_rng(M).choice(M, 24, replace=False), [M - 2, M - 1]]))
+    rows = rows[(rows >= 0) & (rows < M)]
+    q, s = il.quant_int8_per_token(x[rows])
+    accr = il.gemm_int8_int32(q, w)
+    ridx = torch.from_numpy(rows).to(DEV)
+    assert np.array_equal(host(acc[ridx]), accr)
+    want = _bf16_rne_bits((accr.astype(np.float32) * s[:, None]).astype(np.float32) * sw[None, :].astype(np.float32))
+    got = host_bf16_bits(y[ridx])
+    assert np.array_equal(got, want), f"{(got != want).sum()} outputs differ"
+
+
 def test_wq_b_prefill_8192_sampled_rows():
     M = 8192
     x = syn.wq_b_x(M)
