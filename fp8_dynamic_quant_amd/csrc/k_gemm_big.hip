@@ -181,10 +181,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
   v16i acc[4][2];  // set by each tile's first K step (an MFMA with a zero accumulator)
   const v16i zero16 = {};
 
-  // Wave (wm, wn) computes rows wm*128 + [0, 128) and the two 32-column blocks j*128 + wn*32
-  // (j = 0, 1): the four waves of a row half cover 128 consecutive columns with each block, so
-  // the halves of every 128-byte output line are stored by two waves at about the same time.
-  const int ar = wm * 128 + (lane & 31), br = wn * 32 + (lane & 31);
+  // Wave (wm, wn) computes rows wm*128 + [0, 128) and two 32-column blocks j = 0, 1 at tile
+  // column col0(j).  With cached output stores they are j*128 + wn*32: the four waves of a
+  // row half cover 128 consecutive columns with each block, so the two 64-byte halves of a
+  // line are stored by two waves at about the same point and meet in the L2.  With
+  // nontemporal stores (written back early, so halves from two waves often reach memory
+  // apart) they are wn*64 + j*32: one wave stores both halves of its lines.
+  auto col0 = [&](int j) __attribute__((always_inline)) { return NT ? wn * 64 + j * 32 : j * 128 + wn * 32; };
+  const int ar = wm * 128 + (lane & 31);
+  auto brow = [&](int j) __attribute__((always_inline)) { return col0(j) + (lane & 31); };  // W row of block j
   const int kh = lane >> 5;
   // this wave's output staging: one 32 x 32 block, 32 rows of 64 bytes at an 80-byte pitch
   int8_t* const stg = smem + kStages * kStageB + wv * kStgWave;
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
   // columns j*128 + wn*32 + 8q + 4(lane/32) + r (register 4q + r).  Four values become two
   // words of two bf16 each (round to nearest even, v_cvt_pk_bf16_f32).
   auto col_scales = [&](const float* sc, int j, int q) __attribute__((always_inline)) {
-    return *reinterpret_cast<const float4*>(sc + 256 + j * 128 + wn * 32 + 8 * q + 4 * kh);
+    return *reinterpret_cast<const float4*>(sc + 256 + col0(j) + 8 * q + 4 * kh);
   };
   auto conv = [&](const float4 cs, int i, int j, int q, float rs, v2u& w) __attribute__((always_inline)) {
     const v16i& a = acc[i][j];
@@ -223,17 +228,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int m = om0 + wm * 128 + i * 32 + (lane & 31);
-          const int n = on0 + j * 128 + wn * 32 + 8 * q + 4 * kh;
+          const int n = on0 + col0(j) + 8 * q + 4 * kh;
           *reinterpret_cast<v4i*>(p.acc_out + (int64_t)m * N + n) =
               v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         }
   };
   // Staging of one block: every lane writes its four 8-byte pieces (one row, 16 columns);
-  // read back, four lanes take one 64-byte row, and each nontemporal store writes 16 rows
-  // of 64 bytes (an aligned half of each 128-byte line; the neighbouring wave, wn ^ 1, writes
-  // the other half of those lines at the same point of its own sequence).  A wave's LDS
-  // operations run in order, so the next block's writes may follow this block's reads
-  // without a wait.
+  // read back, four lanes take one 64-byte row, and each store writes 16 rows of 64 bytes
+  // (an aligned half of each 128-byte line; col0 above says who writes the other half).  A
+  // wave's LDS operations run in order, so the next block's writes may follow this block's
+  // reads without a wait.
   auto stage_write = [&](const v2u (&w)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) *reinterpret_cast<v2u*>(stg_wr + q * 16) = w[q];
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int rr = wm * 128 + i * 32 + k * 16;  // first of the 16 rows of this store, in the tile
-      const int cc = j * 128 + wn * 32;           // first of the 32 columns, in the tile
+      const int cc = col0(j);                     // first of the 32 columns, in the tile
       // Scalar tile base and offset, 32-bit lane offset (256 ldy < 2^30).  Nontemporal
       // (streaming) when each XCD keeps a block of W resident in its L2 across many row blocks
       // (the N-range tile order): the output then stays out of the L2's reuse set.  Otherwise
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
 #pragma unroll
       for (int i = 0; i < 4; ++i) a4[i] = *reinterpret_cast<const v4i*>(sa + bswz(ar + i * 32, 2 * ks + kh));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b2[j] = *reinterpret_cast<const v4i*>(sb + bswz(br + j * 128, 2 * ks + kh));
+      for (int j = 0; j < 2; ++j) b2[j] = *reinterpret_cast<const v4i*>(sb + bswz(brow(j), 2 * ks + kh));
     };
     read_frags(0, af[0], bf[0]);
 #pragma unroll
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
     v4i bfr[4], afr[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bfr[ks] = *reinterpret_cast<const v4i*>(sb + bswz(br, 2 * ks + kh));
+      bfr[ks] = *reinterpret_cast<const v4i*>(sb + bswz(brow(0), 2 * ks + kh));
       afr[ks] = *reinterpret_cast<const v4i*>(sa + bswz(ar, 2 * ks + kh));
     }
     v2u w[4];  // the words of the block being staged, then of the next block
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
         }
         if (b < 7) {
           if (ni != i) afr[ks] = *reinterpret_cast<const v4i*>(sa + bswz(ar + ni * 32, 2 * ks + kh));
-          if (nj != j) bfr[ks] = *reinterpret_cast<const v4i*>(sb + bswz(br + nj * 128, 2 * ks + kh));
+          if (nj != j) bfr[ks] = *reinterpret_cast<const v4i*>(sb + bswz(brow(nj), 2 * ks + kh));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
