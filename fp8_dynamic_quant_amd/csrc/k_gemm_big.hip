@@ -49,8 +49,7 @@ constexpr int kRowsPerBankRow = 256 / kBKb;  // rows sharing one sweep of the 64
 constexpr int kRowsPerDma = 1024 / kBKb;   // rows one 64-lane x 16-byte DMA instruction covers
 constexpr int kDmaPerWave = kBT / 8 / kRowsPerDma;  // DMA instructions per operand per wave
 constexpr int kGroupRows = 4;              // tile rows per group in the tile order
-constexpr int kStgPitch = 80;              // epilogue staging: bytes per 64-byte row (bank spread)
-constexpr int kStgWave = 32 * kStgPitch;   // staging bytes per wave: one 32 x 32 block of bf16
+constexpr int kStgWave = 32 * 64;          // epilogue staging per wave: one 32 x 32 block of bf16
 static_assert(kBKb == 128 && kDmaPerWave == 4, "slice width: 4 K steps, 8 DMA instructions per wave");
 static_assert(kStages == 2 && kStages * kStageB <= 160 * 1024, "LDS ring: one slice in flight");
 static_assert(kStages * kStageB + 8 * kStgWave + 2 * 512 * 4 <= 160 * 1024, "ring, output staging and scales fit in LDS");
@@ -191,10 +190,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
   const int ar = wm * 128 + (lane & 31);
   auto brow = [&](int j) __attribute__((always_inline)) { return col0(j) + (lane & 31); };  // W row of block j
   const int kh = lane >> 5;
-  // this wave's output staging: one 32 x 32 block, 32 rows of 64 bytes at an 80-byte pitch
+  // This wave's output staging: one 32 x 32 block, row r (64 bytes) at 64 r, its 16-byte
+  // chunk c at position c ^ ((r / 4) % 4) and, for r >= 16, the two 8-byte halves of each
+  // chunk swapped.  Then the 32 lanes of a half-wave writing 8 bytes each (rows 0..31, one
+  // half of one chunk) cover the 64 banks once, and the 16 lanes of a quarter-wave reading
+  // 16 bytes each (four rows, four chunks) do too.
   int8_t* const stg = smem + kStages * kStageB + wv * kStgWave;
-  int8_t* const stg_wr = stg + (lane & 31) * kStgPitch + kh * 8;
-  const int8_t* const stg_rd = stg + (lane / 4) * kStgPitch + (lane % 4) * 16;
+  const int sr = lane & 31, sw = (sr >> 2) & 3;
+  int8_t* const stg_wr = stg + sr * 64 + 8 * (kh ^ (sr >> 4));
+  const int8_t* const stg_rd = stg + (lane / 4) * 64 + 16 * ((lane % 4) ^ ((lane >> 4) & 3));
   const uint32_t yoff = (uint32_t)((lane / 4) * p.ldy * 2 + (lane % 4) * 16);
   int m0, n0, nm0 = 0, nn0 = 0, om0 = 0, on0 = 0;
   tile_at(0, m0, n0);
@@ -240,24 +244,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm_i8_big(TileArgs p, BigTiles bt,
   // reads without a wait.
   auto stage_write = [&](const v2u (&w)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<v2u*>(stg_wr + q * 16) = w[q];
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<v2u*>(stg_wr + 16 * (q ^ sw)) = w[q];
   };
   auto stage_read = [&](v4i (&rows)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) rows[k] = *reinterpret_cast<const v4i*>(stg_rd + k * 16 * kStgPitch);
+    for (int k = 0; k < 2; ++k) rows[k] = *reinterpret_cast<const v4i*>(stg_rd + k * 16 * 64);
+    rows[1] = v4i{rows[1][2], rows[1][3], rows[1][0], rows[1][1]};  // rows 16..31: halves swapped back
   };
   auto stage_store = [&](int i, int j, const v4i (&rows)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int rr = wm * 128 + i * 32 + k * 16;  // first of the 16 rows of this store, in the tile
       const int cc = col0(j);                     // first of the 32 columns, in the tile
-      // Scalar tile base and offset, 32-bit lane offset (256 ldy < 2^30).  Nontemporal
-      // (streaming) when each XCD keeps a block of W resident in its L2 across many row blocks
-      // (the N-range tile order): the output then stays out of the L2's reuse set.  Otherwise
-      // the stores are cached, and the two halves of a line meet in the L2 before it is
-      // written back.
+      // Scalar tile base, 32-bit lane offset (256 ldy < 2^30).  Nontemporal (streaming) when
+      // each XCD keeps a block of W resident in its L2 across many row blocks (the N-range
+      // tile order): the output then stays out of the L2's reuse set.  Otherwise the stores
+      // are cached, and the two halves of a line meet in the L2 before it is written back.
+      // The whole offset is in the lane offset and soffset is the constant 0: the compiler
+      // then keeps a wait state between the 16-byte store and a VALU write of its data
+      // registers, which it leaves out when soffset is a register; without it the store sent
+      // some dwords of the registers' next values (seen with the register reused at once).
       __builtin_amdgcn_raw_buffer_store_b128(rows[k], raw_rsrc(reinterpret_cast<int8_t*>(p.y) + ((int64_t)om0 * p.ldy + on0) * 2),
-                                             (int)yoff, (int)((rr * p.ldy + cc) * 2), NT ? 2 : 0);
+                                             (int)(yoff + (uint32_t)((rr * p.ldy + cc) * 2)), 0, NT ? 2 : 0);
     }
   };
 
