@@ -119,7 +119,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
 // the DMA's target wait for all DMAs in flight (vmcnt(0) in the middle of the slice).  Here the
 // kernel orders them itself: each slice waits for its own DMA (vmcnt) and a barrier before
 // reading the stage, and nothing else reads a stage a DMA is filling.  The instruction has no
-// register result; M0 is written one instruction ahead of its use.
+// register result.  The compiler cannot see the hazards inside the statement, so it keeps its
+// own wait states: six between the statement's start and the load (a VALU write of an SGPR
+// the load reads, e.g. a readfirstlane just ahead, needs five; the M0 write needs one).
 __device__ __forceinline__ void dma_one(const int8_t* src, int64_t ld, int r0, int k0, int8_t* dst, int wv, int i,
                                         const uint32_t off[2]) {
   const int8_t* base = src + (int64_t)(r0 + wv * 32 + i * kRowsPerDma) * ld + k0;
@@ -127,7 +129,7 @@ __device__ __forceinline__ void dma_one(const int8_t* src, int64_t ld, int r0, i
   const uint32_t la = (uint32_t)(uintptr_t)(lds_ptr_b)(dst + (wv * kDmaPerWave + i) * 1024);
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(o), "s"(base), "s"(la)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(o), "s"(base), "s"(la)
                : "memory", "m0");
 #pragma clang diagnostic pop
 }
