@@ -224,14 +224,16 @@ def test_epilogue_is_the_documented_f32_sequence(M, K, N):
         assert np.array_equal(got, want), f"fused={fused}: {(got != want).sum()} outputs differ"
 
 
-@pytest.mark.parametrize("M,K,N", [(1000, 128, 16384), (1024, 256, 16400)])
+@pytest.mark.parametrize("M,K,N", [(1000, 128, 16384), (1024, 256, 16400), (2048, 128, 16384), (2600, 128, 4112)])
 def test_large_gemm_tile_orders_sampled_rows(M, K, N):
     """The M, N >= 256 GEMM in both tile orders: N-range (each XCD walks a range of W's columns,
-    nontemporal output; 1000 x 16384) and row groups (cached output; 1024 x 16400), each with
-    a last tile row or column shifted back to end at M or N, so some rows or columns are
-    computed by two tiles.  Sampled rows (every row the shifted tile shares) against the
-    oracle's accumulators and the documented f32 epilogue, and the production launch against
-    the one that also exports the accumulators."""
+    nontemporal output; 1000 x 16384, 2048 x 16384) and row groups (cached output; 1024 x
+    16400, 2600 x 4112), with a last tile row or column shifted back to end at M or N, so some
+    rows or columns are computed by two tiles, and with several tiles per workgroup (the
+    epilogue carried into the next tile's first slice) at one slice per tile (K = 128).
+    Sampled rows (every row the shifted tile shares) against the oracle's accumulators and
+    the documented f32 epilogue, and the production launch against the one that also exports
+    the accumulators."""
     x = syn.activations((101, M, K), M, K, outlier_frac=0.01, outlier_mul=20.0)
     w, sw = syn.int8_weights((102, N, K), N, K)
     xq, xs = wq.wq_dynamic_quant(bf16_dev(x))
