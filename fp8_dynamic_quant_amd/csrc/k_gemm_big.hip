@@ -5,10 +5,10 @@
 // MFMA units, not HBM, bound the run (e.g. M = 8192, K = 1024, N = 32768: 550 Gop, 587 MB).
 //
 // Shape of the kernel (MI355X):
-//  * one workgroup per CU, persistent: 512 threads = 8 waves in a 2 x 4 grid, each wave a
-//    128 x 64 block of the 256 x 256 tile as 4 x 2 v_mfma_i32_32x32x32_i8 tiles (128 int32
-//    accumulators per lane).  The 256 x 256 tile halves the L2 traffic per MAC of a 128 x 128
-//    tile; two waves per SIMD hide each other's LDS latency;
+//  * one workgroup per CU, persistent: 512 threads = 8 waves in a 2 x 4 grid, each wave 128
+//    rows by two 32-column blocks of the 256 x 256 tile as 4 x 2 v_mfma_i32_32x32x32_i8 tiles
+//    (128 int32 accumulators per lane).  The 256 x 256 tile halves the L2 traffic per MAC of
+//    a 128 x 128 tile; two waves per SIMD hide each other's LDS latency;
 //  * operands move global -> LDS with global_load_lds_dwordx4 in 128-byte K slices through
 //    two 64 KiB stages (A 256 x 128 and B 256 x 128 bytes, XOR-swizzled chunks): one slice
 //    loads while the other is multiplied.  The next slice's eight DMA instructions per wave
@@ -25,9 +25,10 @@
 //    consecutive output columns of one row.  Epilogue: bf16((f32(acc) * s_m) * sw_n), carried
 //    into the next tile's first K slice, which runs block by block: each 32 x 32 block's
 //    accumulators are converted during the previous block's MFMAs, staged through a private
-//    LDS area (four values per 8-byte write) and read back so that each nontemporal
-//    16-byte-per-lane store writes 16 rows of 64 bytes; the conversion, staging and stores
-//    run beside the MFMA pipe.  The last tile's epilogue runs on its own;
+//    LDS area (four values per 8-byte write) and read back so that each 16-byte-per-lane
+//    store writes 16 rows of 64 bytes; the conversion, staging and stores run beside the MFMA
+//    pipe.  The last tile's epilogue runs on its own.  Output stores are nontemporal in the
+//    N-range order and cached otherwise;
 //  * M, N >= 256; the last tile row and column are shifted back to end at M and N, so every
 //    DMA and store is inside the operands.
 // K must be a multiple of 128, N of 8.
