@@ -123,14 +123,21 @@ int quant_split(const wq_ctx* c, int64_t M, int64_t K) {
 // Shape of the one-launch fused kernel: nt columns and r rows per workgroup.  Every
 // workgroup quantises its r rows (VALU time ~ r) and streams nt K weight bytes (the row
 // tiles of one column slice share them through their XCD's L2).  The cost of a shape is
-// the rounds of workgroups per CU times the per-workgroup time 4 r + nt: measured at
-// K = 4096, N = 1024 on 256 CUs, one row of quantisation costs about as much as four
-// columns of weights, and for every M in 1..64 the fastest shape is the one this picks.
+// the rounds of workgroups per CU times the per-workgroup time row_cost r + max(nt,
+// col_floor).  With the quantisation (col_floor 16) a slice narrower than 16 columns costs
+// as much as 16: the kernel's MFMA tile is 16 columns wide, and a narrower slice runs a
+// partly used one.  Measured at K = 4096, N = 1024 on 256 CUs over every shape of r in
+// 1..16 and nt in 4..32, the pick is the fastest shape or within 0.1 us of it at M = 2, 4,
+// 7, 8, 16, 32, 64 for both weight layouts (row_cost 4 on plain weights, 6 on fragment-order
+// weights, which stream faster); a linear column cost had picked 2 x 8 at M = 4 (4.70 against
+// 4.34 us for 1 x 16) and, on fragment-order weights, 2 x 32 at M = 16 (5.29 against 4.85 us
+// for 4 x 16).
 // Ties go to the smaller r (a smaller kernel instance: less code, fewer registers); r is
 // at most the power of two at or above M.
-// row_cost: a row's cost in columns (4 with the quantisation; 10 with fragment-order
-// weights; the decode GEMM on given codes passes 1 above M = 16)
-void fused_shape(const wq_ctx* c, int64_t M, int64_t N, int* nt, int* r, int row_cost = 4) {
+// row_cost: a row's cost in columns (4 with the quantisation; 6 with fragment-order
+// weights; the decode GEMM on given codes passes 1 above M = 16); col_floor: 16 with the
+// quantisation, 0 (a linear column cost) for the decode GEMM on given codes
+void fused_shape(const wq_ctx* c, int64_t M, int64_t N, int* nt, int* r, int row_cost = 4, int col_floor = 16) {
   int64_t best = -1;
   for (int rr : {1, 2, 4, 8, 16}) {
     if (c->fused_r > 0 ? rr != c->fused_r : rr >= 2 * M) continue;
@@ -138,7 +145,7 @@ void fused_shape(const wq_ctx* c, int64_t M, int64_t N, int* nt, int* r, int row
       if (c->fused_nt > 0 && w != c->fused_nt) continue;
       const int64_t wgs = (N + w - 1) / w * ((M + rr - 1) / rr);
       const int64_t rounds = (wgs + c->num_cu - 1) / c->num_cu;
-      const int64_t cost = rounds * (row_cost * std::min<int64_t>(rr, M) + w);
+      const int64_t cost = rounds * (row_cost * std::min<int64_t>(rr, M) + std::max(w, col_floor));
       if (best < 0 || cost < best) {
         best = cost;
         *nt = w;
@@ -418,7 +425,7 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
     // codes with row tiles of up to 16 rows (at M = 128, N = 1024 the 128 x 128 tiles gave
     // only 8 workgroups: 41.6 us with the quant)
     int nt = 16, rr = 16;
-    fused_shape(c, M, N, &nt, &rr, 1);
+    fused_shape(c, M, N, &nt, &rr, 1, 0);
     hipError_t e = wq::launch_fused_decode(a, nt, rr, st, frag);
     if (c->log)
       std::fprintf(stderr, "[wq] quant_matmul int8 mid-M (decode kernel, given codes) M=%lld N=%lld K=%lld cols/wg=%d "
@@ -434,7 +441,7 @@ static int int8_matmul(wq_ctx* c, const wq_matmul_desc* d, hipStream_t st) {
       // costs about a column (both measured fastest at K = 4096, N = 1024).  Fragment-order
       // weights (any M <= 64) always take this kernel: it is the decode kernel that reads them
       int nt = 16, rr = 16;
-      fused_shape(c, M, N, &nt, &rr, M > 16 ? 1 : 4);
+      fused_shape(c, M, N, &nt, &rr, M > 16 ? 1 : 4, 0);
       hipError_t e = wq::launch_fused_decode(a, nt, rr, st, frag);
       if (c->log)
         std::fprintf(stderr, "[wq] quant_matmul int8 decode (fused kernel, given codes) M=%lld N=%lld K=%lld cols/wg=%d "
@@ -763,11 +770,9 @@ int wq_fused_quant_matmul_packed(wq_ctx* c, const void* x, int64_t M, int64_t K,
   a.xq_out = x_q_out;
   a.xs_out = x_scale_out;
   // fragment-order weights stream faster, so a row of quantisation weighs more against a
-  // column: about 10 columns (measured at K = 4096, N = 1024: M = 4 runs 1 x 16 in 4.48 us
-  // against 4.87 us for 2 x 8; every other M of 1..64 keeps the shape of row cost 4 or one
-  // within noise of it)
+  // column: about 6 columns (the shape model above)
   int nt = 16, rr = 16;
-  fused_shape(c, M, N, &nt, &rr, 10);
+  fused_shape(c, M, N, &nt, &rr, 6);
   hipError_t e = wq::launch_fused_decode(a, nt, rr, static_cast<hipStream_t>(stream), true);
   if (c->log)
     std::fprintf(stderr, "[wq] fused_quant_matmul_packed M=%lld N=%lld K=%lld cols/wg=%d rows/wg=%d\n",
