@@ -256,6 +256,26 @@ def test_large_gemm_tile_orders_sampled_rows(M, K, N):
     assert np.array_equal(got, want), f"{(got != want).sum()} outputs differ"
 
 
+@pytest.mark.parametrize("M,K,N", [(256, 128, 256), (511, 384, 272), (777, 640, 1040), (1300, 1152, 2064)])
+def test_large_gemm_odd_shapes(M, K, N):
+    """The M, N >= 256 GEMM at the smallest shape it takes and at shapes where M, N and the
+    number of K slices (1, 3, 5, 9) fit no power of two: every output against the oracle's
+    documented f32 epilogue, and the accumulator export against the oracle."""
+    x = syn.activations((103, M, K), M, K, outlier_frac=0.01, outlier_mul=20.0)
+    w, sw = syn.int8_weights((104, N, K), N, K)
+    xq, xs = wq.wq_dynamic_quant(bf16_dev(x))
+    acc = poison((M, N), torch.int32)
+    y_acc = wq.wq_quant_matmul(xq, xs, dev(w), dev(sw), acc_out=acc)
+    y = wq.wq_quant_matmul(xq, xs, dev(w), dev(sw))
+    torch.cuda.synchronize()
+    q, s = il.quant_int8_per_token(x)
+    accr = il.gemm_int8_int32(q, w)
+    assert np.array_equal(host(acc), accr)
+    want = _bf16_rne_bits((accr.astype(np.float32) * s[:, None]).astype(np.float32) * sw[None, :].astype(np.float32))
+    assert np.array_equal(host_bf16_bits(y), want)
+    assert torch.equal(y.view(torch.int16), y_acc.view(torch.int16))
+
+
 def test_wq_b_prefill_8192_sampled_rows():
     M = 8192
     x = syn.wq_b_x(M)
