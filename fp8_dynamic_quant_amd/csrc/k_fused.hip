@@ -22,10 +22,10 @@
 //    (CT = nt / 16 column tiles, or one partly used tile for nt < 16).
 //  * The per-row absmax is reduced inside the wave with DPP and across the 8 waves through
 //    LDS; each lane quantises its 8 values per row into the wave's private XOR-swizzled
-//    LDS tile (the MFMA A operand).  Only the fast path (an fma with RN(1/s), one
-//    near-tie check per 8 values) is inline; the rare chunks that fail it, and rows whose
-//    scale is zero or not normal, go through one rolled loop with the exact quant_i8, so
-//    the unrolled code stays small.
+//    LDS tile (the MFMA A operand) by the fast path (one fma per value with 1/s, whose bit
+//    pattern holds both the code and a near-tie flag); a row where some lane meets a
+//    near-tie, or whose scale is zero or not normal, is redone by the whole wave with the
+//    exact quant_i8 behind a uniform branch, from the chunk still in registers.
 //  * The 8 waves' int32 16 x 16 tiles are summed exactly in LDS and the epilogue writes
 //    bf16((f32(acc) * s_m) * sw_n).
 #include "wq_device.h"
@@ -71,9 +71,9 @@ __device__ __forceinline__ uint32_t bf16x8_absmax_bits(const uint4 u) {
   return max((uint32_t)e.x, (uint32_t)e.y);
 }
 
-// INT8 codes of 8 bf16 values by the fast path of quant_i8 (fma with inv = RN(1/s));
-// *ok is false when a value lies near a rounding tie (the codes are then not used)
-__device__ __forceinline__ uint2 quant8_bf16_fast(const uint4 u, float inv, bool* ok) {
+// INT8 codes of 8 bf16 values by the fast path of quant_i8 (one fma with inv ~ 1/s); *l is
+// 0 when a value lies near a rounding tie (the codes are then not used)
+__device__ __forceinline__ uint2 quant8_bf16_fast(const uint4 u, float inv, uint16_t* l) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
   float v[8];
   uint32_t b[8];
@@ -82,8 +82,8 @@ __device__ __forceinline__ uint2 quant8_bf16_fast(const uint4 u, float inv, bool
     v[2 * i] = __uint_as_float(w[i] << 16);
     v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
-  *ok = quant_fast<8>(v, inv, b);
-  return uint2{pack4_biased(b), pack4_biased(b + 4)};
+  *l = quant_fast_lmin<8>(v, inv, b);
+  return uint2{pack4_codes(b), pack4_codes(b + 4)};
 }
 
 // INT8 codes of 8 bf16 values by the exact quant_i8 (correctly rounded division)
@@ -215,50 +215,41 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
   }
 
   // ---- quantise this lane's 8 values of each row into the wave's tile ----------------------
-  // Straight-line per row: the fast codes are written whatever the check says, and a lane
-  // whose chunk fails it (a near-tie, or a scale that is zero or not normal) only sets the
-  // row's bit for the exact loop below, which overwrites them.  (Branching on the check per
-  // row cost ~35 scalar instructions and 8 branches per row.)  Rows past `rows` (the last
-  // tile) are quantised from their clamped copies into tile rows the MFMA never reads, and
-  // never marked.  The tile offset of chunk c of row r is r KW + ((c ^ (r % g)) << 4):
-  // the XOR with a per-row constant applies to this lane's fixed chunk offset.
+  // Per row, the fast codes (one fma per value, quant_fast_lmin); where some lane's chunk
+  // holds a near-tie, or the row's scale is zero, subnormal or infinite, the whole wave
+  // replaces them with the exact codes of that row at once, from the chunk still in its
+  // registers.  The branch is uniform (a ballot), so a row without a near-tie costs one
+  // compare and a few scalar instructions.  Only a few rows per call meet a near-tie, but
+  // their workgroups set the call's time: a marked-row loop after all rows either kept every
+  // row's chunk live through the whole quantisation (R = 16: 158 VGPRs against 101) or
+  // re-read it from L2 (a round trip per marked row; M = 64: 8.68 -> 9.49 us on plain
+  // weights).  Rows past `rows` (the last tile) are quantised from their clamped copies into
+  // tile rows the MFMA never reads, and never re-done.  The tile offset of chunk c of row r
+  // is r KW + ((c ^ (r % g)) << 4): the XOR with a per-row constant applies to this lane's
+  // fixed chunk offset.
   const bool export_q = p.xq_out != nullptr && slice == 0;
   const int chunks = KW >> 4;
   const int gmask = min(16, chunks & -chunks) - 1;
   const int lane_off = ((lane >> 1) << 4) + (lane & 1) * 8;
-  uint32_t bad = 0;  // rows whose chunk needs the exact path (bit r)
+  const uint32_t abnormal = (uint32_t)__builtin_amdgcn_ballot_w64(lane < R && !quant_scale_normal(s_l));
+  const uint64_t xmask = __builtin_amdgcn_ballot_w64(xlane);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if constexpr (kLateW) {  // this row's share of the weight fragments, outside any branch
 #pragma unroll
       for (int idx = r * kWLoads / R; idx < (r + 1) * kWLoads / R; ++idx) load_w(idx);
     }
-    const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_l), r));
     const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_l), r));
-    bool ok;
-    const uint2 q = quant8_bf16_fast(xr[r], inv, &ok);
-    const bool live = r < rows;  // uniform
-    if (!(ok && quant_scale_normal(s)) && live && xlane) bad |= 1u << r;
+    uint16_t l;
+    uint2 q = quant8_bf16_fast(xr[r], inv, &l);
+    const bool tie = (__builtin_amdgcn_ballot_w64(l == 0) & xmask) != 0;
+    if (r < rows && (tie || ((abnormal >> r) & 1u))) {  // uniform
+      const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_l), r));
+      q = quant8_bf16_exact(xr[r], s);
+    }
     if (xlane) {
       *reinterpret_cast<uint2*>(tile + r * KW + (lane_off ^ ((r & gmask) << 4))) = q;
-      if (export_q && live) *reinterpret_cast<uint2*>(p.xq_out + (int64_t)(row0 + r) * K + kbase + lane * 8) = q;
-    }
-  }
-  // the exact path, one affected row per iteration; each lane picks its row's 8 values out
-  // of its registers (re-reading them from L2 cost a memory round trip per iteration, and
-  // about a third of the workgroups meet a near-tie somewhere)
-  while (__any(bad != 0)) {
-    const int r = bad != 0 ? __builtin_ctz(bad) : 0;
-    const float s = __shfl(s_l, r, 64);
-    uint4 u = xr[0];
-#pragma unroll
-    for (int rr = 1; rr < R; ++rr)
-      if (r == rr) u = xr[rr];  // a per-lane select
-    if (bad != 0) {
-      const uint2 q = quant8_bf16_exact(u, s);
-      *reinterpret_cast<uint2*>(tile + fswz(r, lane >> 1, KW) + (lane & 1) * 8) = q;
-      if (export_q) *reinterpret_cast<uint2*>(p.xq_out + (int64_t)(row0 + r) * K + kbase + lane * 8) = q;
-      bad &= bad - 1;
+      if (export_q && r < rows) *reinterpret_cast<uint2*>(p.xq_out + (int64_t)(row0 + r) * K + kbase + lane * 8) = q;
     }
   }
   }  // quantisation

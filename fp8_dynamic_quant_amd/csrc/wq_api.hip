@@ -128,16 +128,17 @@ int quant_split(const wq_ctx* c, int64_t M, int64_t K) {
 // as much as 16: the kernel's MFMA tile is 16 columns wide, and a narrower slice runs a
 // partly used one.  Measured at K = 4096, N = 1024 on 256 CUs over every shape of r in
 // 1..16 and nt in 4..32, the pick is the fastest shape or within 0.1 us of it at M = 2, 4,
-// 7, 8, 16, 32, 64 for both weight layouts (row_cost 4 on plain weights, 6 on fragment-order
-// weights, which stream faster); a linear column cost had picked 2 x 8 at M = 4 (4.70 against
-// 4.34 us for 1 x 16) and, on fragment-order weights, 2 x 32 at M = 16 (5.29 against 4.85 us
-// for 4 x 16).
+// 7, 8, 16, 32, 64 for both weight layouts (row_cost 3 on plain weights, 6 on fragment-order
+// weights, which stream faster; with the one-fma quantisation, row_cost 4 on plain weights
+// picked 4 x 32 at M = 32, 7.23 us against 6.19 for 8 x 16); a linear column cost had picked
+// 2 x 8 at M = 4 (4.70 against 4.34 us for 1 x 16) and, on fragment-order weights, 2 x 32 at
+// M = 16 (5.29 against 4.85 us for 4 x 16).
 // Ties go to the smaller r (a smaller kernel instance: less code, fewer registers); r is
 // at most the power of two at or above M.
-// row_cost: a row's cost in columns (4 with the quantisation; 6 with fragment-order
-// weights; the decode GEMM on given codes passes 1 above M = 16); col_floor: 16 with the
-// quantisation, 0 (a linear column cost) for the decode GEMM on given codes
-void fused_shape(const wq_ctx* c, int64_t M, int64_t N, int* nt, int* r, int row_cost = 4, int col_floor = 16) {
+// row_cost: a row's cost in columns (3 with the quantisation; 6 with fragment-order
+// weights; the decode GEMM on given codes passes 1 above M = 16 and 4 below); col_floor: 16
+// with the quantisation, 0 (a linear column cost) for the decode GEMM on given codes
+void fused_shape(const wq_ctx* c, int64_t M, int64_t N, int* nt, int* r, int row_cost = 3, int col_floor = 16) {
   int64_t best = -1;
   for (int rr : {1, 2, 4, 8, 16}) {
     if (c->fused_r > 0 ? rr != c->fused_r : rr >= 2 * M) continue;

@@ -64,9 +64,9 @@ __device__ __forceinline__ float div127_bf16(float a) {
   return __builtin_fmaf(r, c, m);
 }
 
-// 1/s for a normal s with relative error below 2^-24 (1 + 2^-22): v_rcp_f32 (1 ulp) and one
-// Newton step.  The fast quant path needs only that bound (see quant_fast's proof, which
-// allows 2^-22.4); the exact path divides by s itself.
+// 1/s for a normal s with relative error below 2^-24 (1 + 2^-20): v_rcp_f32 (1 ulp) and one
+// Newton step.  The fast quant paths need 1/s within 2^-22.4 (quant_fast) and 2^-23.4
+// (quant_fast_lmin); the exact path divides by s itself.
 __device__ __forceinline__ float recip_refined(float s) {
   const float r0 = __builtin_amdgcn_rcpf(s);
   const float e = __builtin_fmaf(-s, r0, 1.0f);
@@ -126,6 +126,44 @@ __device__ __forceinline__ uint32_t pack4_biased(const uint32_t* u) {
   // of the first, 0x0c = zero
   const uint32_t lo = __builtin_amdgcn_perm(u[1], u[0], 0x0c0c0400u);  // u0.byte0, u1.byte0, 0, 0
   const uint32_t hi = __builtin_amdgcn_perm(u[3], u[2], 0x04000c0cu);  // 0, 0, u2.byte0, u3.byte0
+  return lo | hi;
+}
+
+// A second fast path of quant_i8, with one fma per value: for a normal finite scale
+// s = RN(a/127) of the row's absmax a, so |v/s| <= 127 (1 + 2^-24) for every value.  It needs
+// inv within relative 2^-23.4 of 1/s (RN(1/s) and recip_refined are within 2^-24 (1 + 2^-20)),
+// so that e = v * inv (the exact product, inside the fma) lies within 2^-17 of v/s.  The fma
+// gives b = RN(e + 384): in [256, 512) the unit is 2^-15, so b is 256 + M 2^-15 with M the low
+// 23 bits of b's pattern, and |M 2^-15 - (e + 128)| <= 2^-16.  Adding 2^14 - 128 * 2^15 to the
+// pattern and shifting it left by one leaves n = floor(M 2^-15 + 1/2) - 128 in bits 16..23
+// (two's complement) and 2 L in the low 16 bits, L = (M + 2^14) mod 2^15.  When L != 0,
+// M 2^-15 + 1/2 is at least 2^-15 from every integer, so v/s + 128 + 1/2 (within
+// 2^-16 + 2^-17 of it) is more than 2^-17 from one: v/s lies strictly between n - 1/2 and
+// n + 1/2 and more than half an ulp of either (at most 2^-18 below 128) inside, so RN(v/s)
+// does too and rounds to n, which is in [-127, 127]: n is quant_i8's code and the clamp is
+// moot.  Returns the minimum of the 2 L over the N values (0: a near-tie; the caller then
+// takes the exact path for them); u[i] receives the shifted patterns (pack4_codes packs
+// them).  Checked against exact rationals on the CPU for near-tie values at every bf16
+// absmax, with rcp results one ulp either side of RN(1/s).  Per value it costs an fma, an
+// add-and-shift and about one 16-bit minimum, against quant_fast's four: the fused decode
+// GEMM quantises in a VALU-bound phase.
+template <int N>
+__device__ __forceinline__ uint16_t quant_fast_lmin(const float* v, float inv, uint32_t* u) {
+  constexpr float kPlace = 384.0f;                // 1.5 * 2^8
+  constexpr uint32_t kAdj = 0x4000u - 0x400000u;  // + 2^14 (rounds), - 128 * 2^15 (recentres)
+#pragma unroll
+  for (int i = 0; i < N; ++i) u[i] = (__float_as_uint(__builtin_fmaf(v[i], inv, kPlace)) + kAdj) << 1;
+  uint16_t m = (uint16_t)u[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) m = __builtin_elementwise_min(m, (uint16_t)u[i]);
+  return m;
+}
+
+// four shifted patterns of quant_fast_lmin -> the four codes (byte 2 of each) packed little
+// endian, by v_perm_b32 as in pack4_biased
+__device__ __forceinline__ uint32_t pack4_codes(const uint32_t* u) {
+  const uint32_t lo = __builtin_amdgcn_perm(u[1], u[0], 0x0c0c0602u);  // u0.byte2, u1.byte2, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(u[3], u[2], 0x06020c0cu);  // 0, 0, u2.byte2, u3.byte2
   return lo | hi;
 }
 

@@ -166,6 +166,21 @@ def test_fused_ties_take_the_exact_path(R, NT):
         wq.set_fused_shape(DEV, 0, 0)
 
 
+@pytest.mark.parametrize("M,R,NT", [(5, 4, 16), (21, 16, 32), (3, 2, 16), (9, 8, 16)])
+def test_fused_ties_in_a_partial_row_tile(M, R, NT):
+    """The last row tile holds fewer than R rows and its missing rows are clamped copies of
+    a tie row: the live tie rows take the exact path, the copies are never stored."""
+    K, N = 4096, 1024
+    x = _tie_rows(M, K, 107)
+    x[M - 1] = x[M - 1 - ((M - 1) % 2)]  # the last row is a tie row
+    w, sw = syn.int8_weights((108, N, K), N, K)
+    wq.set_fused_shape(DEV, R, NT)
+    try:
+        _check_linear(x, w, sw, fused=True)
+    finally:
+        wq.set_fused_shape(DEV, 0, 0)
+
+
 @pytest.mark.parametrize("M,K,N", [(5, 4096, 1024), (64, 2048, 272), (3, 1040, 96), (80, 1024, 256)])
 def test_fused_strided_rows(M, K, N):
     # x rows ldx = K + 64 apart and y rows ldy = N + 8 apart (views into wider buffers), on
