@@ -158,7 +158,7 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
   v4i b[CT][kFMaxSteps];
   // weight fragment idx = ct * kFMaxSteps + j
   auto load_w = [&](int idx) {
-    const int ct = idx / kFMaxSteps, j = idx % kFMaxSteps;
+    const int ct = idx % CT, j = idx / CT;  // K-step-major: the order the MFMA loop takes them
     // B column cl of tile ct is output column ct * 16 + cl; columns past nt or N read a
     // column in range and are not stored
     const int c = CT == 1 ? (cl & (nt - 1)) : ct * 16 + cl;
@@ -180,13 +180,19 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
   // With several rows to quantise the weights are requested only once the rows have landed,
   // a few fragments per quantised row: issued up front they queued ahead of the rows at the
   // address unit (which takes ~64 bytes a cycle per CU) and held back the absmax and the
-  // quantisation, whose VALU work then covers their flight instead.
+  // quantisation, whose VALU work then covers their flight instead.  The first kEarly K
+  // steps of every column tile still go out with the rows where that measured faster
+  // (graph replays, cold weights): fragment order, R = 4 with two column tiles (the M = 32
+  // shape): 6.00 -> 5.59 us; plain weights, R = 4 with one tile (M = 16): 5.43 -> 5.21 us,
+  // and R = 8 with two (M = 64): 8.15 -> 8.00 us.  The other shapes measured slower with
+  // them (fragment order M = 16: 4.84 -> 4.95 us, M = 64: 7.52 -> 7.75 us).  Fragments go
+  // out K-step-major in the order the MFMA loop consumes them (M = 64: 7.59 -> 7.52 us).
   constexpr bool kLateW = !PREQ && R >= 4;  // at R = 2 the late weights were measured slower (5.08 -> 5.21 us)
   constexpr int kWLoads = CT * kFMaxSteps;
-  if constexpr (!kLateW) {
+  constexpr int kEarlySteps = PK ? ((R == 4 && CT == 2) ? 2 : 0) : (((R == 4 && CT == 1) || (R == 8 && CT == 2)) ? 2 : 0);
+  constexpr int kEarly = kLateW ? kEarlySteps * CT : kWLoads;
 #pragma unroll
-    for (int idx = 0; idx < kWLoads; ++idx) load_w(idx);
-  }
+  for (int idx = 0; idx < kEarly; ++idx) load_w(idx);
 
   if constexpr (PREQ) {
     // ---- the given codes into the wave's tile, the given scales into LDS ----------------
@@ -237,7 +243,8 @@ __global__ __launch_bounds__(512) void k_fused_decode(DecodeArgs p, int nt, int 
   for (int r = 0; r < R; ++r) {
     if constexpr (kLateW) {  // this row's share of the weight fragments, outside any branch
 #pragma unroll
-      for (int idx = r * kWLoads / R; idx < (r + 1) * kWLoads / R; ++idx) load_w(idx);
+      for (int idx = kEarly + r * (kWLoads - kEarly) / R; idx < kEarly + (r + 1) * (kWLoads - kEarly) / R; ++idx)
+        load_w(idx);
     }
     const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_l), r));
     uint16_t l;
